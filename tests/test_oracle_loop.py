@@ -1,0 +1,278 @@
+"""Pins of verification and of the whole speculative loop.
+
+* verify: brute-force enumeration against the set definition of the accepted
+  prefix, plus hand cases for stop ids, budget and commit rows;
+* loop: greedy speculative decoding must emit exactly the target's plain greedy
+  tokens (losslessness) with the oracle drafter and with perfect, adversarial
+  and random-prefix stub drafters, with the step counts each stub implies;
+* cache: after the loop the draft cache equals a from-scratch fuse+inject of a
+  full prefill's taps (commit positions are right);
+* block pass: one pass over the block equals per-row evaluation, is
+  non-causal, ignores dead cache slots and is batch independent.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from block_diffusion_drafter_target_amd import synth
+from oracle import ref
+
+
+# ---------------------------------------------------------------- verify
+
+def _m_by_definition(d, a):
+    """max { k in [0, B-1] : d_j == a_{j-1} for all 1 <= j <= k }."""
+    B = len(a)
+    best = 0
+    for k in range(B):
+        if all(d[j - 1] == a[j - 1] for j in range(1, k + 1)):
+            best = max(best, k)
+    return best
+
+
+def test_verify_bruteforce_b4_alphabet3():
+    B = 4
+    cases = 0
+    for d in itertools.product(range(3), repeat=B - 1):
+        for a in itertools.product(range(3), repeat=B):
+            r = ref.verify_accept([d], [a], [10])
+            m = int(r["accept_len"][0])
+            assert m == _m_by_definition(d, a)
+            assert 0 <= m <= B - 1
+            assert all(d[j - 1] == a[j - 1] for j in range(1, m + 1))
+            if m < B - 1:
+                assert d[m] != a[m]
+            assert r["anchor_out"][0] == a[m]
+            assert r["n_emit"][0] == m + 1
+            assert list(r["emitted"][0, :m + 1]) == list(a[:m + 1])
+            assert list(r["emitted"][0, :m + 1]) == list(d[:m]) + [a[m]]
+            assert r["new_ctx_len"][0] == 10 + m + 1
+            assert r["commit_rows"].tolist() == [[i, 0, 10 + i] for i in range(m + 1)]
+            cases += 1
+    assert cases == 27 * 81
+
+
+def test_verify_stop_budget_and_batch_commit_order():
+    B = 5
+    draft = np.array([[7, 8, 9, 1], [3, 3, 3, 3], [5, 6, 2, 2]])
+    target = np.array([[7, 8, 4, 0, 0], [3, 3, 3, 3, 9], [0, 6, 2, 2, 2]])
+    ctx = [100, 7, 0]
+    r = ref.verify_accept(draft, target, ctx, stop_ids=[8])
+    assert r["accept_len"].tolist() == [2, 4, 0]
+    # seq 0 emits 7, 8 then stops at the stop id 8
+    assert r["n_emit"].tolist() == [2, 5, 1]
+    assert r["emitted"][0].tolist() == [7, 8, -1, -1, -1]
+    assert r["done"].tolist() == [1, 0, 0]
+    assert r["commit_rows"].tolist() == [[0, 0, 100], [1, 0, 101], [2, 0, 102],
+                                         [5, 1, 7], [6, 1, 8], [7, 1, 9], [8, 1, 10], [9, 1, 11],
+                                         [10, 2, 0]]
+    # budget: 3 tokens left for seq 1, 0 for seq 2
+    r = ref.verify_accept(draft, target, ctx, budget=[10, 3, 0])
+    assert r["n_emit"].tolist() == [3, 3, 0]
+    assert r["budget"].tolist() == [7, 0, 0]
+    assert r["done"].tolist() == [0, 1, 1]
+
+
+def test_geometric_construction_is_recovered():
+    batch, B, V = 64, 16, 1000
+    g = np.random.default_rng(0)
+    draft = g.integers(0, V - 1, size=(batch, B - 1))
+    m = synth.geometric_accept(batch, B, 0.8, step=3)
+    assert m.max() <= B - 1 and m.min() >= 0
+    a = synth.synth_target_tokens(draft, m, V, step=3)
+    r = ref.verify_accept(draft, a, np.zeros(batch))
+    assert r["accept_len"].tolist() == m.tolist()
+
+
+def test_geometric_mean_acceptance():
+    m = synth.geometric_accept(200000, 16, 0.8, step=0)
+    expect = sum(0.8 ** k for k in range(1, 16))  # E[m] = sum_k P(m >= k)
+    assert abs(m.mean() - expect) < 0.02
+    assert abs(expect - 3.859) < 1e-3
+
+
+# ---------------------------------------------------------------- tiny loop
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = synth.CONFIGS["c1"]
+    W = synth.make_weights(cfg)
+    TW = synth.make_target_weights(cfg, W)
+    ocfg = ref.OracleConfig.from_any(cfg)
+    prompt = synth.make_prompt(cfg, cfg.ctx_len)
+    target = ref.TinyTarget(ocfg, TW, cfg.target_layers, cfg.tap_layers)
+    greedy = ref.greedy_generate(target, prompt, cfg.n_new + cfg.block)
+    return cfg, ocfg, W, TW, prompt, target, greedy
+
+
+def test_tiny_greedy_is_not_degenerate(tiny):
+    cfg, ocfg, W, TW, prompt, target, greedy = tiny
+    assert len(set(greedy)) > 8  # the random target does not emit one token forever
+
+
+def test_loop_lossless_with_oracle_drafter(tiny):
+    cfg, ocfg, W, TW, prompt, target, greedy = tiny
+    out, info = ref.spec_generate(ocfg, target, prompt, cfg.n_new, W=W)
+    assert out == greedy[:cfg.n_new]
+    # taps of the committed rows went into every layer at positions 0..L-1
+    L = info["ctx_len"]
+    target.reset()
+    # committed positions P..L-1 hold the first L-P generated (greedy) tokens
+    seq = list(prompt) + list(greedy[:L - len(prompt)])
+    _, taps = target.forward(seq)
+    fresh = ref.new_cache(ocfg, 1, info["cache"]["k"].shape[2])
+    ref.inject_kv(ocfg, W, ref.fuse_ctx(ocfg, W, taps), [(r, 0, r) for r in range(L)], fresh)
+    assert ref.rel_err(info["cache"]["k"][:, :, :L], fresh["k"][:, :, :L]) < 1e-9
+    assert ref.rel_err(info["cache"]["v"][:, :, :L], fresh["v"][:, :, :L]) < 1e-9
+
+
+def _perfect(greedy, P, B):
+    def propose(anchor, L, cache):
+        i = L - P + 1  # tokens already emitted
+        return greedy[i:i + B - 1]
+    return propose
+
+
+def _adversarial(greedy, P, B, V):
+    def propose(anchor, L, cache):
+        i = L - P + 1
+        nxt = greedy[i]
+        return [(nxt + 1) % (V - 1)] + [0] * (B - 2)
+    return propose
+
+
+def _random_prefix(greedy, P, B, V, seed=0):
+    g = np.random.default_rng(seed)
+
+    def propose(anchor, L, cache):
+        i = L - P + 1
+        k = int(g.integers(0, B))
+        d = list(greedy[i:i + B - 1])
+        if k < B - 1:
+            d[k] = (d[k] + 1) % (V - 1)
+        return d
+    return propose
+
+
+def test_loop_lossless_with_stub_drafters(tiny):
+    cfg, ocfg, W, TW, prompt, target, greedy = tiny
+    P, B, N, V = len(prompt), cfg.block, cfg.n_new, cfg.vocab
+    out, info = ref.spec_generate(ocfg, target, prompt, N, propose=_perfect(greedy, P, B))
+    assert out == greedy[:N]
+    assert len(info["m"]) == -(-(N - 1) // B)
+    assert all(m == B - 1 for m in info["m"])
+    out, info = ref.spec_generate(ocfg, target, prompt, N, propose=_adversarial(greedy, P, B, V))
+    assert out == greedy[:N]
+    assert len(info["m"]) == N - 1 and all(m == 0 for m in info["m"])
+    out, info = ref.spec_generate(ocfg, target, prompt, N, propose=_random_prefix(greedy, P, B, V))
+    assert out == greedy[:N]
+    assert 0 < np.mean(info["m"]) < B - 1
+
+
+def test_loop_stop_token(tiny):
+    cfg, ocfg, W, TW, prompt, target, greedy = tiny
+    stop = greedy[20]
+    first = greedy.index(stop)
+    out, _ = ref.spec_generate(ocfg, target, prompt, cfg.n_new, W=W, stop_ids=[stop])
+    assert out == greedy[:first + 1]
+
+
+# ---------------------------------------------------------------- block pass
+
+def _small():
+    cfg = ref.OracleConfig(hidden=48, n_layers=2, n_q_heads=6, n_kv_heads=2, head_dim=8,
+                           intermediate=64, vocab=50, n_tap=2, block=5, rope_theta=1e4, rms_eps=1e-6)
+    g = np.random.default_rng(21)
+    H, D, I, V = cfg.hidden, cfg.head_dim, cfg.intermediate, cfg.vocab
+    W = {"embed": g.standard_normal((V, H)), "lm_head": g.standard_normal((V, H)) * 0.2,
+         "w_fc": g.standard_normal((H, 2 * H)) * 0.2, "g_fc": 1 + 0.2 * g.standard_normal(H),
+         "g_final": 1 + 0.2 * g.standard_normal(H)}
+    for l in range(cfg.n_layers):
+        W[f"layers.{l}.w_qkv"] = g.standard_normal(((6 + 4) * D, H)) * 0.2
+        W[f"layers.{l}.w_o"] = g.standard_normal((H, 6 * D)) * 0.2
+        W[f"layers.{l}.w_gate"] = g.standard_normal((I, H)) * 0.2
+        W[f"layers.{l}.w_up"] = g.standard_normal((I, H)) * 0.2
+        W[f"layers.{l}.w_down"] = g.standard_normal((H, I)) * 0.2
+        for n, k in (("g_in", H), ("g_post", H), ("g_q", D), ("g_k", D)):
+            W[f"layers.{l}.{n}"] = 1 + 0.2 * g.standard_normal(k)
+    return cfg, W, g
+
+
+def _filled_cache(cfg, W, g, lens, max_ctx):
+    cache = ref.new_cache(cfg, len(lens), max_ctx, fill=np.nan)
+    for b, L in enumerate(lens):
+        taps = g.standard_normal((L, cfg.n_tap * cfg.hidden))
+        ref.inject_kv(cfg, W, ref.fuse_ctx(cfg, W, taps), [(r, b, r) for r in range(L)], cache)
+    return cache
+
+
+def test_block_pass_equals_per_row_evaluation():
+    cfg, W, g = _small()
+    L = 9
+    cache = _filled_cache(cfg, W, g, [L], 32)
+    x = g.standard_normal((cfg.block, cfg.hidden))
+    pos = L + np.arange(cfg.block)
+    full, k_blk, v_blk = ref.decoder_layer(cfg, W, 0, x, pos, cache["k"][0, 0, :L], cache["v"][0, 0, :L])
+    # row j alone, attending to the same keys: context + the whole block's K/V
+    Kall = np.concatenate([cache["k"][0, 0, :L], k_blk])
+    Vall = np.concatenate([cache["v"][0, 0, :L], v_blk])
+    Hq, D = cfg.n_q_heads, cfg.head_dim
+    for j in range(cfg.block):
+        u = ref.rms_norm(x[j:j + 1], W["layers.0.g_in"], cfg.rms_eps)
+        q = (u @ W["layers.0.w_qkv"][:Hq * D].T).reshape(1, Hq, D)
+        q = ref.rope(ref.rms_norm(q, W["layers.0.g_q"], cfg.rms_eps), pos[j:j + 1], cfg.rope_theta)
+        o = ref.attention(q, Kall, Vall).reshape(1, -1)
+        xr = x[j:j + 1] + o @ W["layers.0.w_o"].T
+        w = ref.rms_norm(xr, W["layers.0.g_post"], cfg.rms_eps)
+        xr = xr + (ref.silu(w @ W["layers.0.w_gate"].T) * (w @ W["layers.0.w_up"].T)) @ W["layers.0.w_down"].T
+        assert np.allclose(xr[0], full[j], atol=1e-12)
+
+
+def test_block_is_non_causal_and_target_is_causal():
+    cfg, W, g = _small()
+    L = 4
+    cache = _filled_cache(cfg, W, g, [L], 16)
+    x = g.standard_normal((cfg.block, cfg.hidden))
+    pos = L + np.arange(cfg.block)
+    a, _, _ = ref.decoder_layer(cfg, W, 0, x, pos, cache["k"][0, 0, :L], cache["v"][0, 0, :L])
+    x2 = x.copy()
+    x2[-1] += 1.0
+    b, _, _ = ref.decoder_layer(cfg, W, 0, x2, pos, cache["k"][0, 0, :L], cache["v"][0, 0, :L])
+    assert np.max(np.abs(a[1] - b[1])) > 1e-6  # the last row reaches row 1
+    allowed = np.arange(L + cfg.block)[None, :] <= pos[:, None]
+    a, _, _ = ref.decoder_layer(cfg, W, 0, x, pos, cache["k"][0, 0, :L], cache["v"][0, 0, :L], allowed)
+    b, _, _ = ref.decoder_layer(cfg, W, 0, x2, pos, cache["k"][0, 0, :L], cache["v"][0, 0, :L], allowed)
+    assert np.array_equal(a[:-1], b[:-1])
+
+
+def test_layer_position_shift_invariance():
+    cfg, W, g = _small()
+    L = 7
+    ctx = g.standard_normal((L, cfg.hidden))
+    x = g.standard_normal((cfg.block, cfg.hidden))
+    outs = []
+    for shift in (0, 13, 1000):
+        cp = shift + np.arange(L)
+        k, v = ref.project_kv(cfg, W, 0, ctx, cp)
+        y, _, _ = ref.decoder_layer(cfg, W, 0, x, shift + L + np.arange(cfg.block), k, v)
+        outs.append(y)
+    assert np.allclose(outs[1], outs[0], atol=1e-10)
+    assert np.allclose(outs[2], outs[0], atol=1e-10)
+
+
+def test_draft_block_ignores_dead_slots_and_is_batch_independent():
+    cfg, W, g = _small()
+    lens = [5, 0, 11]
+    cache = _filled_cache(cfg, W, g, lens, 24)  # slots >= L hold NaN
+    anchor = [3, 7, 49 - 1]
+    r = ref.draft_block(cfg, W, cache, lens, anchor)
+    assert np.all(np.isfinite(r["logits"]))
+    assert r["draft"].shape == (3, cfg.block - 1)
+    for b in range(3):
+        sub = {"k": cache["k"][:, b:b + 1], "v": cache["v"][:, b:b + 1]}
+        rb = ref.draft_block(cfg, W, sub, [lens[b]], [anchor[b]])
+        assert np.allclose(rb["logits"][0], r["logits"][b], atol=1e-12)
+        assert np.array_equal(rb["draft"][0], r["draft"][b])
+    # the tokens are the argmax of the logits of rows 1..B-1
+    assert np.array_equal(r["draft"], np.argmax(r["logits"], axis=-1))
