@@ -1,0 +1,642 @@
+// C ABI of the draft-step library: argument checks, launch plans and the
+// sequence of gfx950 kernels for each call. Every check that needs no GPU runs
+// before the first HIP call, so failures are reported without a device.
+#include <dflash.h>
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "internal.h"
+
+struct dflash_model {
+  dflash_config cfg;
+  dflash_weights w;
+  std::vector<dflash_layer_weights> layers;
+};
+
+namespace {
+
+using dfl::GemmParams;
+
+constexpr int kMaxBatch = 4096;
+constexpr int kRowChunk = 1024;  // rows per fuse / inject GEMM pass
+constexpr int kGemmRows = 64;    // rows per weight-streaming GEMM launch
+constexpr int kTargetWGs = 768;  // workgroups a GEMM launch aims for (3 per CU)
+
+inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct GemmPlan {
+  int mt, nf, splits, k_per_split;
+};
+
+// Tile shape and split-K for Y = A W^T with up to kGemmRows rows per launch.
+GemmPlan plan_gemm(int M, int N, int K, int nz, bool argmax) {
+  GemmPlan g;
+  const int rows = std::min(M, kGemmRows);
+  g.mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  g.nf = g.mt == 1 ? 4 : 2;
+  long long tiles = cdiv(N, 16 * g.nf) * nz;
+  if (g.nf == 4 && tiles < 2 * kTargetWGs / 3) {
+    g.nf = 2;
+    tiles = cdiv(N, 32) * nz;
+  }
+  const int kblocks = (int)cdiv(K, 128);
+  int s = 1;
+  if (!argmax) {
+    s = (int)std::max<long long>(1, cdiv(kTargetWGs, tiles));
+    s = std::min(s, std::max(1, kblocks / 4));  // at least one 128-k block per wave
+  }
+  const int per = (int)cdiv(kblocks, s);
+  g.splits = (int)cdiv(kblocks, per);
+  g.k_per_split = per * 128;
+  return g;
+}
+
+// Partial buffer (floats) that run_gemm needs for M rows.
+size_t gemm_partial_floats(int M, int N, int K, int nz) {
+  const GemmPlan g = plan_gemm(M, N, K, nz, false);
+  return (size_t)nz * g.splits * M * N;
+}
+
+struct GemmCall {
+  const uint16_t* A = nullptr;
+  long long lda = 0;
+  const int32_t* a_idx = nullptr;
+  int a_idx_stride = 0, a_idx_max = 0;
+  const uint16_t* W0[dfl::kMaxZ] = {};
+  const uint16_t* W1[dfl::kMaxZ] = {};
+  long long ldw = 0;
+  int n_split = 0;
+  int M = 0, N = 0, K = 0, nz = 1;
+  float* P = nullptr;                 // partial mode
+  unsigned long long* keys = nullptr; // argmax mode
+  float* dbg = nullptr;
+  long long ld_dbg = 0;
+};
+
+// Runs the weight-streaming GEMM over all M rows (kGemmRows per launch).
+// Partial output P[z][s][M][N]; returns the split count through *splits.
+hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
+  const bool argmax = c.keys != nullptr;
+  const GemmPlan g = plan_gemm(c.M, c.N, c.K, c.nz, argmax);
+  if (splits) *splits = g.splits;
+  for (int m0 = 0; m0 < c.M; m0 += kGemmRows) {
+    GemmParams p;
+    std::memset(&p, 0, sizeof(p));
+    const int rows = std::min(kGemmRows, c.M - m0);
+    const GemmPlan gl = plan_gemm(rows, c.N, c.K, c.nz, argmax);
+    // every chunk keeps the split layout of the full call
+    p.A = c.a_idx ? c.A : c.A + (long long)m0 * c.lda;
+    p.lda = c.lda;
+    p.a_idx = c.a_idx ? c.a_idx + (long long)m0 * c.a_idx_stride : nullptr;
+    p.a_idx_stride = c.a_idx_stride;
+    p.a_idx_max = c.a_idx_max;
+    for (int z = 0; z < c.nz; ++z) {
+      p.W0[z] = c.W0[z];
+      p.W1[z] = c.W1[z] ? c.W1[z] : c.W0[z];
+    }
+    p.ldw = c.ldw;
+    p.n_split = c.W1[0] ? c.n_split : c.N;
+    p.M = rows;
+    p.N = c.N;
+    p.K = c.K;
+    p.splits = g.splits;
+    p.k_per_split = g.k_per_split;
+    if (argmax) {
+      p.keys = c.keys + m0;
+      p.dbg = c.dbg ? c.dbg + (long long)m0 * c.ld_dbg : nullptr;
+      p.ld_dbg = c.ld_dbg;
+    } else {
+      p.P = c.P + (long long)m0 * c.N;
+      p.p_s_stride = (long long)c.M * c.N;
+      p.p_z_stride = (long long)g.splits * c.M * c.N;
+    }
+    hipError_t e = dfl::launch_gemm_stream(p, gl.mt, gl.nf, argmax ? dfl::kGemmArgmax : dfl::kGemmPartial,
+                                           c.nz, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+struct AttnPlan {
+  int chunk, n_chunks, gb_pad;
+};
+
+AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx) {
+  AttnPlan a;
+  const int G = c.n_q_heads / c.n_kv_heads;
+  a.gb_pad = (int)cdiv(G * c.block, 16) * 16;
+  const long long units = (long long)batch * c.n_kv_heads;
+  long long chunk = cdiv(units * max_ctx, 1024);
+  chunk = cdiv(chunk, 64) * 64;
+  chunk = std::max<long long>(64, std::min<long long>(chunk, 8192));
+  a.chunk = (int)chunk;
+  a.n_chunks = (int)cdiv(max_ctx, chunk);
+  return a;
+}
+
+// Workspace of dflash_draft_block (bytes, 256-aligned pieces).
+struct DraftWs {
+  size_t x, u, q, ao, s, ulm, keys, pm, pl, po, P, total;
+};
+
+DraftWs draft_ws(const dflash_config& c, int batch, int max_ctx) {
+  DraftWs w;
+  const long long Mb = (long long)batch * c.block, Ml = (long long)batch * (c.block - 1);
+  const int H = c.hidden, qw = c.n_q_heads * c.head_dim;
+  const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const AttnPlan a = plan_attn(c, batch, max_ctx);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  w.x = take(Mb * H * 4);
+  w.u = take(Mb * H * 2);
+  w.q = take(Mb * qw * 2);
+  w.ao = take(Mb * qw * 2);
+  w.s = take(Mb * c.intermediate * 2);
+  w.ulm = take(Ml * H * 2);
+  w.keys = take(Ml * 8);
+  const long long att_rows = (long long)batch * c.n_kv_heads * a.n_chunks * a.gb_pad;
+  w.pm = take(att_rows * 4);
+  w.pl = take(att_rows * 4);
+  w.po = take(att_rows * c.head_dim * 4);
+  size_t pf = 0;
+  pf = std::max(pf, gemm_partial_floats((int)Mb, qkvw, H, 1));
+  pf = std::max(pf, gemm_partial_floats((int)Mb, H, qw, 1));
+  pf = std::max(pf, gemm_partial_floats((int)Mb, 2 * c.intermediate, H, 1));
+  pf = std::max(pf, gemm_partial_floats((int)Mb, H, c.intermediate, 1));
+  w.P = take(pf * 4);
+  w.total = off;
+  return w;
+}
+
+size_t fuse_ws(const dflash_config& c, int rows) {
+  const int r = std::min(rows, kRowChunk);
+  return align256(gemm_partial_floats(r, c.hidden, c.n_tap * c.hidden, 1) * 4);
+}
+
+size_t inject_ws(const dflash_config& c, int rows) {
+  const int r = std::min(rows, kRowChunk);
+  return align256(gemm_partial_floats(r, 2 * c.n_kv_heads * c.head_dim, c.hidden, c.n_layers) * 4);
+}
+
+dflash_status hip_status(hipError_t e) { return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+dflash_status check_kv(const dflash_model* m, const dflash_kv* kv) {
+  if (!kv || !kv->k || !kv->v || !kv->ctx_len || !kv->status) return DFLASH_ERR_NULL;
+  if (kv->batch < 1 || kv->batch > kMaxBatch) return DFLASH_ERR_SHAPE;
+  if (kv->max_ctx < m->cfg.block) return DFLASH_ERR_SHAPE;
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_string(dflash_status s) {
+  switch (s) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_ERR_NULL: return "null pointer";
+    case DFLASH_ERR_SHAPE: return "bad shape";
+    case DFLASH_ERR_UNSUPPORTED: return "unsupported shape";
+    case DFLASH_ERR_WORKSPACE: return "workspace too small";
+    case DFLASH_ERR_CAPACITY: return "cache capacity exceeded";
+    case DFLASH_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights* w,
+                                  dflash_model** out) {
+  if (!cfg || !w || !out) return DFLASH_ERR_NULL;
+  *out = nullptr;
+  const dflash_config& c = *cfg;
+  if (c.hidden <= 0 || c.n_layers <= 0 || c.n_q_heads <= 0 || c.n_kv_heads <= 0 ||
+      c.head_dim <= 0 || c.intermediate <= 0 || c.vocab <= 1 || c.n_tap <= 0 || c.block <= 0)
+    return DFLASH_ERR_SHAPE;
+  if (c.mask_id < 0 || c.mask_id >= c.vocab) return DFLASH_ERR_SHAPE;
+  if (c.n_q_heads % c.n_kv_heads != 0) return DFLASH_ERR_SHAPE;
+  if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f)) return DFLASH_ERR_SHAPE;
+  if (c.block < 2 || c.block > 16) return DFLASH_ERR_UNSUPPORTED;
+  if (c.n_layers > dfl::kMaxLayers) return DFLASH_ERR_UNSUPPORTED;
+  if (c.head_dim != 64 && c.head_dim != 128) return DFLASH_ERR_UNSUPPORTED;
+  if (c.hidden % 64 || c.intermediate % 64 || (c.n_q_heads * c.head_dim) % 64 ||
+      ((long long)c.n_tap * c.hidden) % 64 || c.vocab % 16)
+    return DFLASH_ERR_UNSUPPORTED;
+  if ((c.n_q_heads / c.n_kv_heads) * c.block > 256) return DFLASH_ERR_UNSUPPORTED;
+  if (!w->embed || !w->lm_head || !w->w_fc || !w->g_fc || !w->g_final || !w->layers || !w->rope)
+    return DFLASH_ERR_NULL;
+  if (w->rope_max_pos < 1) return DFLASH_ERR_SHAPE;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const dflash_layer_weights& L = w->layers[l];
+    if (!L.g_in || !L.w_qkv || !L.g_q || !L.g_k || !L.w_o || !L.g_post || !L.w_gate || !L.w_up ||
+        !L.w_down)
+      return DFLASH_ERR_NULL;
+  }
+  dflash_model* m = new (std::nothrow) dflash_model;
+  if (!m) return DFLASH_ERR_SHAPE;
+  m->cfg = c;
+  m->w = *w;
+  m->layers.assign(w->layers, w->layers + c.n_layers);
+  m->w.layers = m->layers.data();
+  *out = m;
+  return DFLASH_OK;
+}
+
+void dflash_model_destroy(dflash_model* m) { delete m; }
+
+dflash_status dflash_rope_table(float* out, int32_t max_pos, int32_t head_dim, float theta) {
+  if (!out) return DFLASH_ERR_NULL;
+  if (max_pos < 1 || head_dim < 2 || head_dim % 2 || !(theta > 0.f)) return DFLASH_ERR_SHAPE;
+  const int half = head_dim / 2;
+  std::vector<double> freq(half);
+  for (int i = 0; i < half; ++i) freq[i] = std::pow((double)theta, -2.0 * i / head_dim);
+  for (long long p = 0; p < max_pos; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double a = (double)p * freq[i];
+      out[(p * half + i) * 2] = (float)std::cos(a);
+      out[(p * half + i) * 2 + 1] = (float)std::sin(a);
+    }
+  return DFLASH_OK;
+}
+
+size_t dflash_workspace_bytes(const dflash_model* m, int32_t max_batch, int32_t max_ctx,
+                              int32_t max_rows) {
+  if (!m || max_batch < 1 || max_ctx < 1 || max_rows < 0) return 0;
+  size_t n = draft_ws(m->cfg, max_batch, max_ctx).total;
+  n = std::max(n, fuse_ws(m->cfg, std::max(1, max_rows)));
+  n = std::max(n, inject_ws(m->cfg, std::max(1, max_rows)));
+  return n;
+}
+
+dflash_status dflash_fuse_ctx(const dflash_model* m, const void* taps, int32_t n_rows, void* ctx,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (!m) return DFLASH_ERR_NULL;
+  if (n_rows < 0) return DFLASH_ERR_SHAPE;
+  if (n_rows == 0) return DFLASH_OK;
+  if (!taps || !ctx || !ws) return DFLASH_ERR_NULL;
+  const dflash_config& c = m->cfg;
+  if (ws_bytes < fuse_ws(c, n_rows)) return DFLASH_ERR_WORKSPACE;
+  const hipStream_t st = as_stream(stream);
+  const int H = c.hidden, K = c.n_tap * c.hidden;
+  float* P = static_cast<float*>(ws);
+  for (int r0 = 0; r0 < n_rows; r0 += kRowChunk) {
+    const int rows = std::min(kRowChunk, n_rows - r0);
+    GemmCall g;
+    g.A = static_cast<const uint16_t*>(taps) + (long long)r0 * K;
+    g.lda = K;
+    g.W0[0] = static_cast<const uint16_t*>(m->w.w_fc);
+    g.ldw = K;
+    g.M = rows;
+    g.N = H;
+    g.K = K;
+    g.P = P;
+    int splits = 1;
+    hipError_t e = run_gemm(g, st, &splits);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+    dfl::RowNormParams rn;
+    std::memset(&rn, 0, sizeof(rn));
+    rn.P = P;
+    rn.p_s_stride = (long long)rows * H;
+    rn.splits = splits;
+    rn.gain = static_cast<const uint16_t*>(m->w.g_fc);
+    rn.eps = c.rms_eps;
+    rn.rows = rows;
+    rn.n = H;
+    rn.out = static_cast<uint16_t*>(ctx) + (long long)r0 * H;
+    e = dfl::launch_row_norm(rn, st);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_inject_kv(const dflash_model* m, const void* ctx, int32_t n_ctx_rows,
+                               const int32_t* commit_rows, const int32_t* n_commit,
+                               int32_t max_commit, dflash_kv* kv, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (!m) return DFLASH_ERR_NULL;
+  if (max_commit < 0 || n_ctx_rows < 0) return DFLASH_ERR_SHAPE;
+  if (max_commit == 0) return DFLASH_OK;
+  if (!ctx || !commit_rows || !n_commit || !ws) return DFLASH_ERR_NULL;
+  if (n_ctx_rows == 0) return DFLASH_ERR_SHAPE;
+  dflash_status ks = check_kv(m, kv);
+  if (ks != DFLASH_OK) return ks;
+  const dflash_config& c = m->cfg;
+  if (ws_bytes < inject_ws(c, max_commit)) return DFLASH_ERR_WORKSPACE;
+  const hipStream_t st = as_stream(stream);
+  const int H = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int N = 2 * Hkv * D;
+  float* P = static_cast<float*>(ws);
+  for (int c0 = 0; c0 < max_commit; c0 += kRowChunk) {
+    const int rows = std::min(kRowChunk, max_commit - c0);
+    GemmCall g;
+    g.A = static_cast<const uint16_t*>(ctx);
+    g.lda = H;
+    g.a_idx = commit_rows + 3ll * c0;
+    g.a_idx_stride = 3;
+    g.a_idx_max = n_ctx_rows;
+    g.nz = c.n_layers;
+    for (int l = 0; l < c.n_layers; ++l)  // k rows then v rows of each layer's W_qkv
+      g.W0[l] = static_cast<const uint16_t*>(m->layers[l].w_qkv) + (long long)Hq * D * H;
+    g.ldw = H;
+    g.M = rows;
+    g.N = N;
+    g.K = H;
+    g.P = P;
+    int splits = 1;
+    hipError_t e = run_gemm(g, st, &splits);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+    dfl::InjectPostParams ip;
+    std::memset(&ip, 0, sizeof(ip));
+    ip.P = P;
+    ip.p_s_stride = (long long)rows * N;
+    ip.p_z_stride = (long long)splits * rows * N;
+    ip.splits = splits;
+    for (int l = 0; l < c.n_layers; ++l) ip.gk[l] = static_cast<const uint16_t*>(m->layers[l].g_k);
+    ip.rope = m->w.rope;
+    ip.rope_max = m->w.rope_max_pos;
+    ip.commit_rows = commit_rows;
+    ip.n_commit = n_commit;
+    ip.max_commit = max_commit;
+    ip.n_ctx_rows = n_ctx_rows;
+    ip.c0 = c0;
+    ip.c1 = c0 + rows;
+    ip.n_layers = c.n_layers;
+    ip.batch = kv->batch;
+    ip.Hkv = Hkv;
+    ip.D = D;
+    ip.max_ctx = kv->max_ctx;
+    ip.eps = c.rms_eps;
+    ip.kc = static_cast<uint16_t*>(kv->k);
+    ip.vc = static_cast<uint16_t*>(kv->v);
+    ip.ctx_len = kv->ctx_len;
+    ip.status = kv->status;
+    e = dfl::launch_inject_post(ip, st);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
+                                 int32_t* draft, float* dbg_logits, float* dbg_hidden, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!m || !anchor || !draft || !ws) return DFLASH_ERR_NULL;
+  dflash_status ks = check_kv(m, kv);
+  if (ks != DFLASH_OK) return ks;
+  const dflash_config& c = m->cfg;
+  const int batch = kv->batch, B = c.block, H = c.hidden, D = c.head_dim;
+  const int Hq = c.n_q_heads, Hkv = c.n_kv_heads, I = c.intermediate, NL = c.n_layers;
+  const int Mb = batch * B, Ml = batch * (B - 1);
+  const int qw = Hq * D, qkvw = (Hq + 2 * Hkv) * D;
+  const DraftWs w = draft_ws(c, batch, kv->max_ctx);
+  if (ws_bytes < w.total) return DFLASH_ERR_WORKSPACE;
+  const AttnPlan ap = plan_attn(c, batch, kv->max_ctx);
+  const hipStream_t st = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  float* x = reinterpret_cast<float*>(base + w.x);
+  uint16_t* u = reinterpret_cast<uint16_t*>(base + w.u);
+  uint16_t* q = reinterpret_cast<uint16_t*>(base + w.q);
+  uint16_t* ao = reinterpret_cast<uint16_t*>(base + w.ao);
+  uint16_t* sb = reinterpret_cast<uint16_t*>(base + w.s);
+  uint16_t* ulm = reinterpret_cast<uint16_t*>(base + w.ulm);
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(base + w.keys);
+  float* pm = reinterpret_cast<float*>(base + w.pm);
+  float* pl = reinterpret_cast<float*>(base + w.pl);
+  float* po = reinterpret_cast<float*>(base + w.po);
+  float* P = reinterpret_cast<float*>(base + w.P);
+  const long long layer_kv = (long long)batch * Hkv * kv->max_ctx * D;
+  const long long hid = (long long)Mb * H;
+  hipError_t e;
+
+  dfl::EmbedParams ep;
+  std::memset(&ep, 0, sizeof(ep));
+  ep.anchor = anchor;
+  ep.embed = static_cast<const uint16_t*>(m->w.embed);
+  ep.gain = static_cast<const uint16_t*>(m->layers[0].g_in);
+  ep.ctx_len = kv->ctx_len;
+  ep.status = kv->status;
+  ep.batch = batch;
+  ep.B = B;
+  ep.H = H;
+  ep.V = c.vocab;
+  ep.mask_id = c.mask_id;
+  ep.max_ctx = kv->max_ctx;
+  ep.rope_max = m->w.rope_max_pos;
+  ep.eps = c.rms_eps;
+  ep.x = x;
+  ep.u = u;
+  ep.dbg = dbg_hidden;
+  if ((e = dfl::launch_embed(ep, st)) != hipSuccess) return DFLASH_ERR_HIP;
+
+  for (int l = 0; l < NL; ++l) {
+    const dflash_layer_weights& L = m->layers[l];
+    int splits = 1;
+    // q, k, v
+    GemmCall g;
+    g.A = u;
+    g.lda = H;
+    g.W0[0] = static_cast<const uint16_t*>(L.w_qkv);
+    g.ldw = H;
+    g.M = Mb;
+    g.N = qkvw;
+    g.K = H;
+    g.P = P;
+    if ((e = run_gemm(g, st, &splits)) != hipSuccess) return DFLASH_ERR_HIP;
+    dfl::QkvPostParams qp;
+    std::memset(&qp, 0, sizeof(qp));
+    qp.P = P;
+    qp.p_s_stride = (long long)Mb * qkvw;
+    qp.splits = splits;
+    qp.gq = static_cast<const uint16_t*>(L.g_q);
+    qp.gk = static_cast<const uint16_t*>(L.g_k);
+    qp.rope = m->w.rope;
+    qp.ctx_len = kv->ctx_len;
+    qp.status = kv->status;
+    qp.batch = batch;
+    qp.B = B;
+    qp.Hq = Hq;
+    qp.Hkv = Hkv;
+    qp.D = D;
+    qp.max_ctx = kv->max_ctx;
+    qp.eps = c.rms_eps;
+    qp.q = q;
+    qp.kc = static_cast<uint16_t*>(kv->k) + l * layer_kv;
+    qp.vc = static_cast<uint16_t*>(kv->v) + l * layer_kv;
+    if ((e = dfl::launch_qkv_post(qp, st)) != hipSuccess) return DFLASH_ERR_HIP;
+    // attention over [context ; block]
+    dfl::AttnParams at;
+    std::memset(&at, 0, sizeof(at));
+    at.q = q;
+    at.k = qp.kc;
+    at.v = qp.vc;
+    at.ctx_len = kv->ctx_len;
+    at.status = kv->status;
+    at.batch = batch;
+    at.Hq = Hq;
+    at.Hkv = Hkv;
+    at.B = B;
+    at.max_ctx = kv->max_ctx;
+    at.chunk = ap.chunk;
+    at.n_chunks = ap.n_chunks;
+    at.gb_pad = ap.gb_pad;
+    at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+    at.pm = pm;
+    at.pl = pl;
+    at.po = po;
+    if ((e = dfl::launch_attention(at, D, st)) != hipSuccess) return DFLASH_ERR_HIP;
+    dfl::MergeParams mp;
+    std::memset(&mp, 0, sizeof(mp));
+    mp.pm = pm;
+    mp.pl = pl;
+    mp.po = po;
+    mp.ctx_len = kv->ctx_len;
+    mp.status = kv->status;
+    mp.batch = batch;
+    mp.Hq = Hq;
+    mp.Hkv = Hkv;
+    mp.B = B;
+    mp.D = D;
+    mp.chunk = ap.chunk;
+    mp.n_chunks = ap.n_chunks;
+    mp.gb_pad = ap.gb_pad;
+    mp.out = ao;
+    if ((e = dfl::launch_attn_merge(mp, st)) != hipSuccess) return DFLASH_ERR_HIP;
+    // o projection, residual, post-attention norm
+    GemmCall go;
+    go.A = ao;
+    go.lda = qw;
+    go.W0[0] = static_cast<const uint16_t*>(L.w_o);
+    go.ldw = qw;
+    go.M = Mb;
+    go.N = H;
+    go.K = qw;
+    go.P = P;
+    if ((e = run_gemm(go, st, &splits)) != hipSuccess) return DFLASH_ERR_HIP;
+    dfl::RowNormParams rn;
+    std::memset(&rn, 0, sizeof(rn));
+    rn.x = x;
+    rn.P = P;
+    rn.p_s_stride = (long long)Mb * H;
+    rn.splits = splits;
+    rn.gain = static_cast<const uint16_t*>(L.g_post);
+    rn.eps = c.rms_eps;
+    rn.rows = Mb;
+    rn.n = H;
+    rn.out = u;
+    if ((e = dfl::launch_row_norm(rn, st)) != hipSuccess) return DFLASH_ERR_HIP;
+    // gate and up in one pass, then SwiGLU
+    GemmCall gg;
+    gg.A = u;
+    gg.lda = H;
+    gg.W0[0] = static_cast<const uint16_t*>(L.w_gate);
+    gg.W1[0] = static_cast<const uint16_t*>(L.w_up);
+    gg.n_split = I;
+    gg.ldw = H;
+    gg.M = Mb;
+    gg.N = 2 * I;
+    gg.K = H;
+    gg.P = P;
+    if ((e = run_gemm(gg, st, &splits)) != hipSuccess) return DFLASH_ERR_HIP;
+    dfl::SwigluParams sp;
+    sp.P = P;
+    sp.p_s_stride = (long long)Mb * 2 * I;
+    sp.splits = splits;
+    sp.rows = Mb;
+    sp.I = I;
+    sp.out = sb;
+    if ((e = dfl::launch_swiglu(sp, st)) != hipSuccess) return DFLASH_ERR_HIP;
+    // down projection, residual, next norm (or the final norm)
+    GemmCall gd;
+    gd.A = sb;
+    gd.lda = I;
+    gd.W0[0] = static_cast<const uint16_t*>(L.w_down);
+    gd.ldw = I;
+    gd.M = Mb;
+    gd.N = H;
+    gd.K = I;
+    gd.P = P;
+    if ((e = run_gemm(gd, st, &splits)) != hipSuccess) return DFLASH_ERR_HIP;
+    std::memset(&rn, 0, sizeof(rn));
+    rn.x = x;
+    rn.P = P;
+    rn.p_s_stride = (long long)Mb * H;
+    rn.splits = splits;
+    rn.eps = c.rms_eps;
+    rn.rows = Mb;
+    rn.n = H;
+    rn.dbg = dbg_hidden ? dbg_hidden + (long long)(l + 1) * hid : nullptr;
+    if (l + 1 < NL) {
+      rn.gain = static_cast<const uint16_t*>(m->layers[l + 1].g_in);
+      rn.out = u;
+    } else {
+      rn.gain = static_cast<const uint16_t*>(m->w.g_final);
+      rn.out = ulm;
+      rn.final_mode = 1;
+      rn.B = B;
+      rn.keys = keys;
+    }
+    if ((e = dfl::launch_row_norm(rn, st)) != hipSuccess) return DFLASH_ERR_HIP;
+  }
+
+  // LM head with the argmax fused; logits only for the debug buffer
+  GemmCall gl;
+  gl.A = ulm;
+  gl.lda = H;
+  gl.W0[0] = static_cast<const uint16_t*>(m->w.lm_head);
+  gl.ldw = H;
+  gl.M = Ml;
+  gl.N = c.vocab;
+  gl.K = H;
+  gl.keys = keys;
+  gl.dbg = dbg_logits;
+  gl.ld_dbg = c.vocab;
+  if ((e = run_gemm(gl, st, nullptr)) != hipSuccess) return DFLASH_ERR_HIP;
+  return hip_status(dfl::launch_unpack_draft(keys, kv->status, batch, B, draft, st));
+}
+
+dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,
+                                   const int32_t* draft, const int32_t* target_argmax,
+                                   const int32_t* stop_ids, int32_t n_stop, int32_t* budget,
+                                   int32_t* accept_len, int32_t* anchor_out, int32_t* emitted,
+                                   int32_t* n_emit, int32_t* done, int32_t* commit_rows,
+                                   int32_t* n_commit, void* stream) {
+  if (!m) return DFLASH_ERR_NULL;
+  dflash_status ks = check_kv(m, kv);
+  if (ks != DFLASH_OK) return ks;
+  if (!draft || !target_argmax || !accept_len || !anchor_out || !emitted || !n_emit || !done ||
+      !commit_rows || !n_commit)
+    return DFLASH_ERR_NULL;
+  if (n_stop < 0) return DFLASH_ERR_SHAPE;
+  if (n_stop > 0 && !stop_ids) return DFLASH_ERR_NULL;
+  dfl::VerifyParams p;
+  p.draft = draft;
+  p.target = target_argmax;
+  p.stop_ids = stop_ids;
+  p.n_stop = n_stop;
+  p.budget = budget;
+  p.ctx_len = kv->ctx_len;
+  p.status = kv->status;
+  p.batch = kv->batch;
+  p.B = m->cfg.block;
+  p.accept_len = accept_len;
+  p.anchor_out = anchor_out;
+  p.emitted = emitted;
+  p.n_emit = n_emit;
+  p.done = done;
+  p.commit_rows = commit_rows;
+  p.n_commit = n_commit;
+  return hip_status(dfl::launch_verify(p, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,295 @@
+// Block attention of the draft step on gfx950.
+//
+// For sequence b and kv head g, the G = Hq/Hkv query heads times B block rows
+// (G*B query rows, padded to 16) attend with no mask over the cache slots
+// [0, L_b + B): the injected context followed by the block's own K/V. Every
+// key costs 4*D bytes of K+V and 4*D*G*B flops, so at G*B = 64..128 the kernel
+// is bound by streaming K/V from HBM; MFMA keeps the arithmetic far below that
+// bound.
+//
+// Decomposition: workgroup (4 waves) = (b, g, key chunk of p.chunk keys);
+// chunks past L_b + B exit at once. The chunk is walked in 64-key slices
+// staged through LDS (K row-major with a 16-byte XOR swizzle, V transposed),
+// the next slice's global loads issued before the current slice's math.
+// Wave w owns query tiles w, w+4, ... (16 query rows each).
+//   S^T = K Q^T    A = K slice rows (LDS), B = Q^T (registers for the chunk)
+//   O^T += V^T P^T A = V^T (LDS, transposed), B = P^T straight from the S^T
+//                  accumulators, so each lane keeps one query's softmax state
+// Online softmax in base 2 (scale * log2 e folded in); row max and row sum
+// combine the four lanes that share a query with two xor shuffles. Each
+// workgroup writes (max, sum, unnormalised O) for its chunk; the merge kernel
+// combines chunks with the log-sum-exp rule.
+#include "common.h"
+#include "internal.h"
+
+namespace dfl {
+
+namespace {
+
+constexpr int kSlice = 64;           // keys per LDS slice
+constexpr int kVtStride = kSlice + 4;  // bf16 per transposed V row (8-byte pad)
+
+template <int D>
+struct Slice {
+  static constexpr int DC = D / 8;  // 16-byte chunks per key row
+  static constexpr int KL = kSlice * DC / 256;
+  static constexpr int VL = (kSlice / 2) * DC / 256;
+};
+
+// Global -> registers: the K and V rows of keys [k0, k0 + 64), clamped to the
+// last valid key (clamped rows are masked out of the softmax).
+template <int D>
+__device__ __forceinline__ void load_slice(u32x4 (&kreg)[Slice<D>::KL], u32x4 (&va)[Slice<D>::VL],
+                                           u32x4 (&vb)[Slice<D>::VL], const bf16_t* kc,
+                                           const bf16_t* vc, int k0, int k_end) {
+  constexpr int DC = Slice<D>::DC;
+#pragma unroll
+  for (int t = 0; t < Slice<D>::KL; ++t) {
+    const int e = threadIdx.x + t * 256;
+    const int key = e / DC, ch = e % DC;
+    const int kidx = min(k0 + key, k_end - 1);
+    kreg[t] = *reinterpret_cast<const u32x4*>(kc + (long long)kidx * D + ch * 8);
+  }
+#pragma unroll
+  for (int t = 0; t < Slice<D>::VL; ++t) {
+    const int e = threadIdx.x + t * 256;
+    const int kp = e / DC, ch = e % DC;
+    const int k0i = min(k0 + 2 * kp, k_end - 1), k1i = min(k0 + 2 * kp + 1, k_end - 1);
+    va[t] = *reinterpret_cast<const u32x4*>(vc + (long long)k0i * D + ch * 8);
+    vb[t] = *reinterpret_cast<const u32x4*>(vc + (long long)k1i * D + ch * 8);
+  }
+}
+
+__device__ __forceinline__ void store_vpair(bf16_t* vt, int d, int kp, uint32_t a, uint32_t b) {
+  // a holds keys 2kp's elements (d, d+1), b the same of key 2kp+1
+  *reinterpret_cast<uint32_t*>(vt + d * kVtStride + 2 * kp) = (a & 0xFFFFu) | (b << 16);
+  *reinterpret_cast<uint32_t*>(vt + (d + 1) * kVtStride + 2 * kp) = (a >> 16) | (b & 0xFFFF0000u);
+}
+
+// Registers -> LDS: K row-major with the 16-byte chunk index XOR (key & 7);
+// V transposed to [d][key] so that a lane reads 4 keys of one d in 8 bytes.
+template <int D>
+__device__ __forceinline__ void store_slice(u32x4* ks, bf16_t* vt, const u32x4 (&kreg)[Slice<D>::KL],
+                                            const u32x4 (&va)[Slice<D>::VL],
+                                            const u32x4 (&vb)[Slice<D>::VL]) {
+  constexpr int DC = Slice<D>::DC;
+#pragma unroll
+  for (int t = 0; t < Slice<D>::KL; ++t) {
+    const int e = threadIdx.x + t * 256;
+    const int key = e / DC, ch = e % DC;
+    ks[key * DC + (ch ^ (key & 7))] = kreg[t];
+  }
+#pragma unroll
+  for (int t = 0; t < Slice<D>::VL; ++t) {
+    const int e = threadIdx.x + t * 256;
+    const int kp = e / DC, ch = e % DC;
+    store_vpair(vt, ch * 8 + 0, kp, va[t].x, vb[t].x);
+    store_vpair(vt, ch * 8 + 2, kp, va[t].y, vb[t].y);
+    store_vpair(vt, ch * 8 + 4, kp, va[t].z, vb[t].z);
+    store_vpair(vt, ch * 8 + 6, kp, va[t].w, vb[t].w);
+  }
+}
+
+template <int D, int QPW>
+__global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
+  constexpr int DC = Slice<D>::DC;
+  constexpr int KL = Slice<D>::KL;
+  constexpr int VL = Slice<D>::VL;
+  static_assert(KL >= 1 && VL >= 1, "slice too small");
+  __shared__ __align__(16) u32x4 ks[kSlice * DC];
+  __shared__ __align__(16) bf16_t vt[D * kVtStride];
+
+  const int b = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
+  if (p.status[b] != 0) return;
+  const int Lk = p.ctx_len[b] + p.B;
+  const int k_start = c * p.chunk;
+  if (k_start >= Lk) return;
+  const int k_end = min(Lk, k_start + p.chunk);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, gq = lane >> 4;
+  const int G = p.Hq / p.Hkv;
+  const int GB = G * p.B;
+  const int QT = p.gb_pad / 16;
+
+  // queries of this wave, as MFMA B operands (column = query, k = d)
+  u32x4 qreg[QPW][D / 32];
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int qt = wave + 4 * i;
+    int rr = qt * 16 + r;
+    rr = rr < GB ? rr : GB - 1;
+    const int hl = rr / p.B, j = rr % p.B;
+    const bf16_t* qrow = p.q + ((long long)(b * p.B + j) * p.Hq + g * G + hl) * D + gq * 8;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds)
+      qreg[i][ds] = qt < QT ? *reinterpret_cast<const u32x4*>(qrow + ds * 32) : u32x4{0, 0, 0, 0};
+  }
+
+  float mrun[QPW], lrun[QPW];
+  f32x4_t o[QPW][D / 16];
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    mrun[i] = -__builtin_inff();
+    lrun[i] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[i][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const long long head_off = ((long long)b * p.Hkv + g) * p.max_ctx * D;
+  const bf16_t* kc = p.k + head_off;
+  const bf16_t* vc = p.v + head_off;
+
+  u32x4 kreg[KL], va[VL], vb[VL];
+
+  load_slice<D>(kreg, va, vb, kc, vc, k_start, k_end);
+  for (int k0 = k_start; k0 < k_end; k0 += kSlice) {
+    store_slice<D>(ks, vt, kreg, va, vb);
+    __syncthreads();
+    // prefetch the next slice (past the end it re-reads the last key: valid
+    // memory, never used)
+    load_slice<D>(kreg, va, vb, kc, vc, k0 + kSlice, k_end);
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int qt = wave + 4 * i;
+      if (qt >= QT) continue;
+      f32x4_t sacc[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        sacc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int key = kt * 16 + r;
+#pragma unroll
+        for (int ds = 0; ds < D / 32; ++ds) {
+          const u32x4 a = ks[key * DC + ((ds * 4 + gq) ^ (key & 7))];
+          sacc[kt] = mfma16x16x32(a, qreg[i][ds], sacc[kt]);
+        }
+      }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + kt * 16 + 4 * gq + e;
+          const float sv = key < k_end ? sacc[kt][e] * p.scale_log2 : -__builtin_inff();
+          sacc[kt][e] = sv;
+          mx = fmaxf(mx, sv);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrun[i], mx);
+      const float alpha = exp2f(mrun[i] - mnew);
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pv = exp2f(sacc[kt][e] - mnew);
+          sacc[kt][e] = pv;
+          rs += pv;
+        }
+      rs += __shfl_xor(rs, 16);
+      rs += __shfl_xor(rs, 32);
+      lrun[i] = lrun[i] * alpha + rs;
+      mrun[i] = mnew;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[i][dt] *= alpha;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 pb;
+        pb.x = pack_bf2(sacc[2 * h][0], sacc[2 * h][1]);
+        pb.y = pack_bf2(sacc[2 * h][2], sacc[2 * h][3]);
+        pb.z = pack_bf2(sacc[2 * h + 1][0], sacc[2 * h + 1][1]);
+        pb.w = pack_bf2(sacc[2 * h + 1][2], sacc[2 * h + 1][3]);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const bf16_t* row = vt + (dt * 16 + r) * kVtStride + 32 * h + 4 * gq;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
+          const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
+          o[i][dt] = mfma16x16x32(a, pb, o[i][dt]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  const long long base = (((long long)b * p.Hkv + g) * p.n_chunks + c) * p.gb_pad;
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int qt = wave + 4 * i;
+    if (qt >= QT) continue;
+    const int rr = qt * 16 + r;
+    if (gq == 0) {
+      p.pm[base + rr] = mrun[i];
+      p.pl[base + rr] = lrun[i];
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      *reinterpret_cast<f32x4_t*>(p.po + (base + rr) * D + dt * 16 + 4 * gq) = o[i][dt];
+  }
+}
+
+// o[m][h] = sum_c exp2(m_c - M) O_c / sum_c exp2(m_c - M) l_c over the chunks
+// that hold keys of the sequence. One wave per (row, head).
+__global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = blockIdx.y;
+  const int h = blockIdx.x * 4 + wave;
+  if (h >= p.Hq) return;
+  const int b = m / p.B, j = m % p.B;
+  bf16_t* out = p.out + ((long long)m * p.Hq + h) * p.D;
+  if (p.status[b] != 0) {
+    for (int d = lane; d < p.D; d += 64) out[d] = 0;
+    return;
+  }
+  const int G = p.Hq / p.Hkv;
+  const int g = h / G, rr = (h % G) * p.B + j;
+  const int Lk = p.ctx_len[b] + p.B;
+  int nch = (Lk + p.chunk - 1) / p.chunk;
+  nch = nch < p.n_chunks ? nch : p.n_chunks;
+  const long long base = ((long long)b * p.Hkv + g) * p.n_chunks;
+  float M = -__builtin_inff();
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, p.pm[(base + c) * p.gb_pad + rr]);
+  float l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const long long idx = (base + c) * p.gb_pad + rr;
+    const float w = exp2f(p.pm[idx] - M);
+    l += w * p.pl[idx];
+    const float* po = p.po + idx * p.D;
+    o0 += w * po[lane];
+    if (p.D > 64) o1 += w * po[lane + 64];
+  }
+  const float inv = 1.0f / l;
+  out[lane] = f2bf(o0 * inv);
+  if (p.D > 64) out[lane + 64] = f2bf(o1 * inv);
+}
+
+template <int D>
+hipError_t launch_d(const AttnParams& p, hipStream_t st) {
+  dim3 grid(p.n_chunks, p.Hkv, p.batch);
+  const int qt = p.gb_pad / 16;
+  if (qt <= 4)
+    hipLaunchKernelGGL((attn_kernel<D, 1>), grid, dim3(256), 0, st, p);
+  else if (qt <= 8)
+    hipLaunchKernelGGL((attn_kernel<D, 2>), grid, dim3(256), 0, st, p);
+  else if (qt <= 16)
+    hipLaunchKernelGGL((attn_kernel<D, 4>), grid, dim3(256), 0, st, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnParams& p, int D, hipStream_t st) {
+  if (D == 128) return launch_d<128>(p, st);
+  if (D == 64) return launch_d<64>(p, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_merge(const MergeParams& p, hipStream_t st) {
+  hipLaunchKernelGGL(merge_kernel, dim3((p.Hq + 3) / 4, p.batch * p.B), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace dfl

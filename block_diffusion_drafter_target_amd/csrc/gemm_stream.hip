@@ -1,0 +1,182 @@
+// Weight-streaming bf16 GEMM for few activation rows (M <= 64), gfx950.
+//
+// Y[m][n] = sum_k A[m][k] * W[n][k]. With M <= 64 the product is bound by
+// reading W once from HBM (2 flop per weight byte per row of A), so the kernel
+// is built around the weight stream:
+//   * a workgroup (4 waves) owns 16*NF weight rows and all 16*MT rows of A;
+//   * each wave takes every fourth 128-wide k block of the split's k range
+//     and loads its W rows straight into MFMA operand registers with 16-byte
+//     loads (64 contiguous bytes per row per instruction), one block ahead of
+//     the MFMAs (register double buffering);
+//   * A is tiny and re-read from L1/L2 by the four waves;
+//   * the four waves' partial tiles are summed through LDS;
+//   * the grid's y dimension splits K (fp32 partials P[z][s][m][n], summed by
+//     the consumer kernel), z batches independent weight matrices;
+//   * argmax mode (one split) reduces each row's logits to a packed
+//     (value, index) key and merges it with a 64-bit atomic max, so logits are
+//     never written unless a debug buffer is given.
+// MFMA: W rows are the A operand (16 rows x 32 k), activations the B operand,
+// so a lane's four results are four consecutive n of one row m.
+#include "common.h"
+#include "internal.h"
+
+namespace dfl {
+
+namespace {
+
+constexpr int kKB = 128;  // k per block = four 32-wide MFMA steps
+
+template <int MT, int NF, int MODE>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
+  __shared__ f32x4_t red[4][NF * MT][kWave];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int z = blockIdx.z;
+  const int s = blockIdx.y;
+  const int n0 = blockIdx.x * 16 * NF;
+  const int kbeg = s * p.k_per_split;
+  const int kend = min(p.K, kbeg + p.k_per_split);
+
+  const bf16_t* wrow[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int n = min(n0 + 16 * f + r, p.N - 1);
+    const bf16_t* base = (n < p.n_split) ? p.W0[z] + (long long)n * p.ldw
+                                         : p.W1[z] + (long long)(n - p.n_split) * p.ldw;
+    wrow[f] = base + g * 8;
+  }
+  const bf16_t* arow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = min(16 * t + r, p.M - 1);
+    int row = m;
+    if (p.a_idx) {  // gathered rows (commit rows of the KV injection)
+      row = p.a_idx[(long long)m * p.a_idx_stride];
+      row = row < 0 ? 0 : (row >= p.a_idx_max ? p.a_idx_max - 1 : row);
+    }
+    arow[t] = p.A + (long long)row * p.lda + g * 8;
+  }
+
+  f32x4_t acc[NF][MT];
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 wa[NF][4], xa[MT][4], wb[NF][4], xb[MT][4];
+
+  auto load = [&](u32x4(&w)[NF][4], u32x4(&x)[MT][4], int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kk = k + 32 * u;
+      if (kk < kend) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) w[f][u] = *reinterpret_cast<const u32x4*>(wrow[f] + kk);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) x[t][u] = *reinterpret_cast<const u32x4*>(arow[t] + kk);
+      } else {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) w[f][u] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < MT; ++t) x[t][u] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto compute = [&](const u32x4(&w)[NF][4], const u32x4(&x)[MT][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[f][t] = mfma16x16x32(w[f][u], x[t][u], acc[f][t]);
+  };
+
+  // k blocks of this wave: kbeg + (wave + 4*i) * 128 while < kend
+  int k = kbeg + wave * kKB;
+  if (k < kend) {
+    load(wa, xa, k);
+    while (true) {
+      const int k1 = k + 4 * kKB;
+      if (k1 < kend) load(wb, xb, k1);
+      compute(wa, xa);
+      if (k1 >= kend) break;
+      const int k2 = k1 + 4 * kKB;
+      if (k2 < kend) load(wa, xa, k2);
+      compute(wb, xb);
+      if (k2 >= kend) break;
+      k = k2;
+    }
+  }
+
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[wave][f * MT + t][lane] = acc[f][t];
+  __syncthreads();
+
+  // each wave finishes the fragments idx = wave, wave + 4, ...
+  for (int idx = wave; idx < NF * MT; idx += 4) {
+    const int f = idx / MT, t = idx % MT;
+    f32x4_t v = red[0][idx][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += red[w][idx][lane];
+    const int m = 16 * t + r;
+    const int nb = n0 + 16 * f + 4 * g;  // four consecutive n
+    if (MODE == kGemmPartial) {
+      if (m < p.M && nb < p.N) {
+        float* dst = p.P + (long long)z * p.p_z_stride + (long long)s * p.p_s_stride +
+                     (long long)m * p.N + nb;
+        *reinterpret_cast<f32x4_t*>(dst) = v;
+      }
+    } else {
+      if (p.dbg != nullptr && m < p.M && nb < p.N)
+        *reinterpret_cast<f32x4_t*>(p.dbg + (long long)m * p.ld_dbg + nb) = v;
+      float bv = -__builtin_inff();
+      int bn = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (nb + i < p.N && v[i] > bv) {
+          bv = v[i];
+          bn = nb + i;
+        }
+      }
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int on = __shfl_xor(bn, o);
+        if (ov > bv || (ov == bv && on < bn)) {
+          bv = ov;
+          bn = on;
+        }
+      }
+      if (g == 0 && m < p.M && bn != 0x7FFFFFFF) atomicMax(p.keys + m, argmax_key(bv, bn));
+    }
+  }
+}
+
+template <int MT, int NF>
+hipError_t launch_mt_nf(const GemmParams& p, int mode, int nz, hipStream_t st) {
+  dim3 grid((p.N + 16 * NF - 1) / (16 * NF), p.splits, nz);
+  if (mode == kGemmArgmax)
+    hipLaunchKernelGGL((gemm_stream_kernel<MT, NF, kGemmArgmax>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((gemm_stream_kernel<MT, NF, kGemmPartial>), grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_stream(const GemmParams& p, int mt, int nf, int mode, int nz,
+                              hipStream_t st) {
+  // (MT, NF) pairs that fit the register file without spills
+  if (mt == 1 && nf == 4) return launch_mt_nf<1, 4>(p, mode, nz, st);
+  if (mt == 1 && nf == 2) return launch_mt_nf<1, 2>(p, mode, nz, st);
+  if (mt == 2 && nf == 2) return launch_mt_nf<2, 2>(p, mode, nz, st);
+  if (mt == 4 && nf == 2) return launch_mt_nf<4, 2>(p, mode, nz, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dfl

@@ -1,0 +1,181 @@
+// Host-visible launch parameters and launchers of the gfx950 kernels. Used by
+// the C ABI implementation (api.cpp); not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dfl {
+
+constexpr int kMaxZ = 16;       // weight matrices batched in one GEMM launch
+constexpr int kMaxLayers = 16;  // draft layers supported
+
+// Y = A * W^T, bf16 in, fp32 accumulate. Rows n < n_split of the logical W
+// come from W0[z] (row n), rows n >= n_split from W1[z] (row n - n_split).
+struct GemmParams {
+  const uint16_t* A;  // [M, K] activations, row stride lda
+  long long lda;
+  // optional row gather: GEMM row m reads A row a_idx[m * a_idx_stride],
+  // clamped to [0, a_idx_max)
+  const int32_t* a_idx;
+  int a_idx_stride, a_idx_max;
+  const uint16_t* W0[kMaxZ];
+  const uint16_t* W1[kMaxZ];
+  long long ldw;
+  int n_split;
+  int M, N, K;
+  int k_per_split;  // k range of one split (multiple of 128)
+  int splits;
+  // partial-sum output: P[z][s][m][n], fp32
+  float* P;
+  long long p_z_stride, p_s_stride;
+  // argmax output (splits == 1): keys[m] = max over n of argmax_key(y[m][n], n)
+  unsigned long long* keys;
+  float* dbg;  // optional logits [M, ld_dbg]
+  long long ld_dbg;
+};
+
+enum GemmMode { kGemmPartial = 0, kGemmArgmax = 1 };
+
+hipError_t launch_gemm_stream(const GemmParams& p, int mt, int nf, int mode, int nz,
+                              hipStream_t st);
+
+struct AttnParams {
+  const uint16_t* q;  // [batch*B, Hq, D]
+  const uint16_t* k;  // layer base: [batch][Hkv][max_ctx][D]
+  const uint16_t* v;
+  const int32_t* ctx_len;
+  const int32_t* status;
+  int batch, Hq, Hkv, B, max_ctx;
+  int chunk;   // keys per workgroup (multiple of 64)
+  int n_chunks;
+  int gb_pad;  // query rows per (b, g), padded to 16
+  float scale_log2;
+  float* pm;   // [batch][Hkv][n_chunks][gb_pad]
+  float* pl;
+  float* po;   // [batch][Hkv][n_chunks][gb_pad][D]
+};
+
+hipError_t launch_attention(const AttnParams& p, int D, hipStream_t st);
+
+struct MergeParams {
+  const float* pm;
+  const float* pl;
+  const float* po;
+  const int32_t* ctx_len;
+  const int32_t* status;
+  int batch, Hq, Hkv, B, D, chunk, n_chunks, gb_pad;
+  uint16_t* out;  // [batch*B, Hq*D]
+};
+
+hipError_t launch_attn_merge(const MergeParams& p, hipStream_t st);
+
+// Row-wise RMSNorm with optional residual add of split partials.
+//   x[m] (fp32, [rows, n]) += sum_s P[s][m] when residual; else y = sum_s P[s][m]
+//   out[m] = bf16(rmsnorm(x or y) * gain)
+// Final mode (lm_rows): rows j >= 1 of each block go to out[b*(B-1)+j-1] and
+// their argmax keys are cleared; row j == 0 writes nothing.
+struct RowNormParams {
+  float* x;            // residual stream or NULL
+  const float* P;      // partials [splits][rows][n] or NULL
+  long long p_s_stride;
+  int splits;
+  const uint16_t* gain;
+  float eps;
+  int rows, n;
+  uint16_t* out;       // bf16 [rows, n] (or [batch*(B-1), n] in final mode)
+  float* dbg;          // optional fp32 copy of x after the add, [rows, n]
+  int final_mode, B;
+  unsigned long long* keys;
+};
+
+hipError_t launch_row_norm(const RowNormParams& p, hipStream_t st);
+
+struct EmbedParams {
+  const int32_t* anchor;
+  const uint16_t* embed;
+  const uint16_t* gain;
+  int32_t* ctx_len;
+  int32_t* status;
+  int batch, B, H, V, mask_id, max_ctx, rope_max;
+  float eps;
+  float* x;        // [batch*B, H]
+  uint16_t* u;     // [batch*B, H]
+  float* dbg;      // optional [batch*B, H]
+};
+
+hipError_t launch_embed(const EmbedParams& p, hipStream_t st);
+
+struct QkvPostParams {
+  const float* P;  // [splits][rows][(Hq+2Hkv)*D]
+  long long p_s_stride;
+  int splits;
+  const uint16_t* gq;
+  const uint16_t* gk;
+  const float* rope;  // [max_pos][D/2][2]
+  const int32_t* ctx_len;
+  const int32_t* status;
+  int batch, B, Hq, Hkv, D, max_ctx;
+  float eps;
+  uint16_t* q;        // [rows, Hq, D]
+  uint16_t* kc;       // layer base [batch][Hkv][max_ctx][D]
+  uint16_t* vc;
+};
+
+hipError_t launch_qkv_post(const QkvPostParams& p, hipStream_t st);
+
+struct SwigluParams {
+  const float* P;  // [splits][rows][2I]: gate at n < I, up at n >= I
+  long long p_s_stride;
+  int splits, rows, I;
+  uint16_t* out;   // [rows, I]
+};
+
+hipError_t launch_swiglu(const SwigluParams& p, hipStream_t st);
+
+struct InjectPostParams {
+  const float* P;  // [layer][split][c1 - c0][2*Hkv*D], row = commit index - c0
+  long long p_z_stride, p_s_stride;
+  int splits;
+  const uint16_t* gk[kMaxLayers];
+  const float* rope;
+  int rope_max;
+  const int32_t* commit_rows;
+  const int32_t* n_commit;
+  int max_commit, n_ctx_rows;
+  int c0, c1;  // commit indices handled by this launch
+  int n_layers, batch, Hkv, D, max_ctx;
+  float eps;
+  uint16_t* kc;  // [NL][batch][Hkv][max_ctx][D]
+  uint16_t* vc;
+  int32_t* ctx_len;
+  int32_t* status;
+};
+
+hipError_t launch_inject_post(const InjectPostParams& p, hipStream_t st);
+
+hipError_t launch_unpack_draft(const unsigned long long* keys, const int32_t* status, int batch,
+                               int B, int32_t* draft, hipStream_t st);
+
+struct VerifyParams {
+  const int32_t* draft;
+  const int32_t* target;
+  const int32_t* stop_ids;
+  int n_stop;
+  int32_t* budget;
+  const int32_t* ctx_len;
+  const int32_t* status;
+  int batch, B;
+  int32_t* accept_len;
+  int32_t* anchor_out;
+  int32_t* emitted;
+  int32_t* n_emit;
+  int32_t* done;
+  int32_t* commit_rows;
+  int32_t* n_commit;
+};
+
+hipError_t launch_verify(const VerifyParams& p, hipStream_t st);
+
+}  // namespace dfl

@@ -1,0 +1,116 @@
+// Greedy verification of a drafted block (gfx950), integer only.
+//
+// One workgroup. Wave w takes sequences w, w+4, ...; lane j compares
+// d_{j+1} with a_j, and a ballot of the mismatches gives the accepted prefix
+// length m (the first mismatch index, or B-1). Stop ids and the token budget
+// cut the emitted tokens a_0..a_m. The commit counts m+1 are scanned across the
+// batch in LDS to lay out the commit rows of all sequences back to back.
+#include "common.h"
+#include "internal.h"
+
+namespace dfl {
+
+namespace {
+
+constexpr int kMaxBatch = 4096;
+
+__global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
+  __shared__ int cnt[kMaxBatch];
+  __shared__ short macc[kMaxBatch];
+  __shared__ int part[256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int B = p.B;
+
+  for (int b = wave; b < p.batch; b += 4) {
+    const bool bad = p.status[b] != 0;
+    const int j = lane;
+    const int a = j < B ? p.target[b * B + j] : 0;
+    const int d = j < B - 1 ? p.draft[b * (B - 1) + j] : 0;
+    const unsigned long long mism = __ballot(j < B - 1 && d != a);
+    const int m = bad ? 0 : (mism ? min(__ffsll((long long)mism) - 1, B - 1) : B - 1);
+    bool is_stop = false;
+    if (j <= m) {
+      for (int s = 0; s < p.n_stop; ++s) is_stop |= (a == p.stop_ids[s]);
+    }
+    const unsigned long long stops = __ballot(is_stop);
+    int n = m + 1;
+    int done = 0;
+    if (stops) {
+      n = __ffsll((long long)stops);  // through the first stop id
+      done = 1;
+    }
+    if (p.budget) {
+      int left = p.budget[b];
+      left = left < 0 ? 0 : left;
+      if (n >= left) {
+        n = left;
+        done = 1;
+      }
+      if (lane == 0 && !bad) p.budget[b] = left - n;
+    }
+    if (bad) {
+      n = 0;
+      done = 1;
+    }
+    const int am = __shfl(a, m);
+    if (j < B) p.emitted[b * B + j] = j < n ? a : -1;
+    if (lane == 0) {
+      p.accept_len[b] = m;
+      p.anchor_out[b] = am;
+      p.n_emit[b] = n;
+      p.done[b] = done;
+      cnt[b] = bad ? 0 : m + 1;
+      macc[b] = (short)m;
+    }
+  }
+  __syncthreads();
+
+  // exclusive scan of cnt[0..batch): each thread sums a contiguous range,
+  // thread 0 scans the 256 range sums, then each range is rewritten.
+  const int per = (p.batch + 255) / 256;
+  const int lo = min(p.batch, threadIdx.x * per), hi = min(p.batch, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += cnt[i];
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int v = part[t];
+      part[t] = run;
+      run += v;
+    }
+    *p.n_commit = run;
+  }
+  __syncthreads();
+  int run = part[threadIdx.x];
+  for (int i = lo; i < hi; ++i) {
+    const int v = cnt[i];
+    cnt[i] = run;
+    run += v;
+  }
+  __syncthreads();
+
+  for (int b = wave; b < p.batch; b += 4) {
+    const int m = macc[b];
+    if (p.status[b] != 0) continue;
+    const int off = cnt[b];
+    const int L = p.ctx_len[b];
+    if (lane <= m) {
+      int32_t* row = p.commit_rows + 3 * (off + lane);
+      row[0] = b * B + lane;
+      row[1] = b;
+      row[2] = L + lane;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_verify(const VerifyParams& p, hipStream_t st) {
+  if (p.batch > kMaxBatch) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(verify_kernel, dim3(1), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace dfl

@@ -1,0 +1,202 @@
+"""Device-resident drafter over the C ABI, and the greedy speculative loop.
+
+``Drafter`` owns torch device buffers (weights, draft KV cache, workspace,
+per-step outputs) and a model handle; each method marshals pointers to one
+C entry point. ``spec_generate`` drives the greedy loop for one sequence with a
+caller-supplied target, following the pages' ``spec_generate`` call shape
+(input ids, a token budget, temperature 0, a target, stop ids) [P4
+"Ejecutando DFlash"].
+
+Pages: [P4] DFlash news article, 7minutos.es, 2026-06-26.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Protocol, Sequence
+
+import numpy as np
+
+from . import binding as bd
+from .synth import DraftConfig, f32_to_bf16
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device_bf16(a: np.ndarray, device):
+    """bf16 bits (uint16) or fp32 on the bf16 grid -> torch bf16 tensor on device."""
+    torch = _torch()
+    if a.dtype != np.uint16:
+        a = f32_to_bf16(a)
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    return t.to(device)
+
+
+class Drafter:
+    """A drafter, its draft KV cache for ``batch`` sequences of up to ``max_ctx``
+    slots, and the workspace for fuse/inject calls of up to ``max_rows`` rows."""
+
+    def __init__(self, cfg: DraftConfig, weights: dict, batch: int, max_ctx: int,
+                 max_rows: int | None = None, device="cuda", rope_max: int | None = None):
+        torch = _torch()
+        bd.load()
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.batch = batch
+        self.max_ctx = max_ctx
+        B = cfg.block
+        self.max_rows = max_rows if max_rows is not None else batch * B
+        self.rope_max = rope_max or max_ctx
+        # weights (device bf16); torch tensors are kept so the pointers stay valid
+        self.w = {}
+        for name, arr in weights.items():
+            t = arr if hasattr(arr, "data_ptr") else to_device_bf16(np.asarray(arr), self.device)
+            self.w[name] = t
+        rope = np.empty(self.rope_max * (cfg.head_dim // 2) * 2, np.float32)
+        bd.dflash_rope_table(rope.ctypes.data_as(C.c_void_p), self.rope_max, cfg.head_dim, cfg.rope_theta)
+        self.rope = torch.from_numpy(rope).to(self.device)
+        c = bd.dflash_config(hidden=cfg.hidden, n_layers=cfg.n_layers, n_q_heads=cfg.n_q_heads,
+                             n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim,
+                             intermediate=cfg.intermediate, vocab=cfg.vocab, n_tap=cfg.n_tap,
+                             block=B, mask_id=cfg.mask_id, rope_theta=cfg.rope_theta,
+                             rms_eps=cfg.rms_eps)
+        layers = (bd.dflash_layer_weights * cfg.n_layers)()
+        for l in range(cfg.n_layers):
+            for f in ("g_in", "w_qkv", "g_q", "g_k", "w_o", "g_post", "w_gate", "w_up", "w_down"):
+                setattr(layers[l], f, self.w[f"layers.{l}.{f}"].data_ptr())
+        wst = bd.dflash_weights(embed=self.w["embed"].data_ptr(), lm_head=self.w["lm_head"].data_ptr(),
+                                w_fc=self.w["w_fc"].data_ptr(), g_fc=self.w["g_fc"].data_ptr(),
+                                g_final=self.w["g_final"].data_ptr(), layers=layers,
+                                rope=self.rope.data_ptr(), rope_max_pos=self.rope_max)
+        self._c_cfg, self._c_layers, self._c_w = c, layers, wst
+        self.model = bd.dflash_model_create(c, wst)
+        # draft KV cache
+        NL, Hkv, D = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+        dev = self.device
+        self.k = torch.zeros((NL, batch, Hkv, max_ctx, D), dtype=torch.bfloat16, device=dev)
+        self.v = torch.zeros((NL, batch, Hkv, max_ctx, D), dtype=torch.bfloat16, device=dev)
+        self.ctx_len = torch.zeros(batch, dtype=torch.int32, device=dev)
+        self.status = torch.zeros(batch, dtype=torch.int32, device=dev)
+        self.kv = bd.dflash_kv(k=self.k.data_ptr(), v=self.v.data_ptr(), batch=batch, max_ctx=max_ctx,
+                               ctx_len=self.ctx_len.data_ptr(), status=self.status.data_ptr())
+        self.ws_bytes = bd.dflash_workspace_bytes(self.model, batch, max_ctx, self.max_rows)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        # per-step buffers
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.anchor = torch.zeros(batch, **i32)
+        self.draft = torch.zeros((batch, B - 1), **i32)
+        self.accept_len = torch.zeros(batch, **i32)
+        self.anchor_out = torch.zeros(batch, **i32)
+        self.emitted = torch.zeros((batch, B), **i32)
+        self.n_emit = torch.zeros(batch, **i32)
+        self.done = torch.zeros(batch, **i32)
+        self.commit_rows = torch.zeros((batch * B, 3), **i32)
+        self.n_commit = torch.zeros(1, **i32)
+        self.ctx = torch.zeros((self.max_rows, cfg.hidden), dtype=torch.bfloat16, device=dev)
+
+    def __del__(self):
+        m = getattr(self, "model", None)
+        if m:
+            bd.dflash_model_destroy(m)
+            self.model = None
+
+    @staticmethod
+    def stream():
+        return _torch().cuda.current_stream().cuda_stream
+
+    # -- entry points --------------------------------------------------------
+    def fuse_ctx(self, taps, n_rows: int | None = None, ctx=None):
+        n = taps.shape[0] if n_rows is None else n_rows
+        out = self.ctx if ctx is None else ctx
+        bd.dflash_fuse_ctx(self.model, bd.ptr(taps), n, bd.ptr(out), bd.ptr(self.ws), self.ws_bytes,
+                           self.stream())
+        return out
+
+    def inject_kv(self, ctx, n_ctx_rows: int, commit_rows, n_commit, max_commit: int):
+        bd.dflash_inject_kv(self.model, bd.ptr(ctx), n_ctx_rows, bd.ptr(commit_rows), bd.ptr(n_commit),
+                            max_commit, self.kv, bd.ptr(self.ws), self.ws_bytes, self.stream())
+
+    def draft_block(self, anchor=None, dbg_logits=None, dbg_hidden=None):
+        a = self.anchor if anchor is None else anchor
+        bd.dflash_draft_block(self.model, self.kv, bd.ptr(a), bd.ptr(self.draft), bd.ptr(dbg_logits),
+                              bd.ptr(dbg_hidden), bd.ptr(self.ws), self.ws_bytes, self.stream())
+        return self.draft
+
+    def verify_accept(self, target_argmax, stop_ids=None, budget=None, draft=None):
+        d = self.draft if draft is None else draft
+        n_stop = 0 if stop_ids is None else int(stop_ids.numel())
+        bd.dflash_verify_accept(self.model, self.kv, bd.ptr(d), bd.ptr(target_argmax), bd.ptr(stop_ids),
+                                n_stop, bd.ptr(budget), bd.ptr(self.accept_len), bd.ptr(self.anchor_out),
+                                bd.ptr(self.emitted), bd.ptr(self.n_emit), bd.ptr(self.done),
+                                bd.ptr(self.commit_rows), bd.ptr(self.n_commit), self.stream())
+
+    # -- helpers -------------------------------------------------------------
+    def ingest(self, b: int, taps, start: int = 0):
+        """Fuse and inject context rows of sequence b at positions start.. ."""
+        torch = _torch()
+        n = taps.shape[0]
+        ctx = torch.empty((n, self.cfg.hidden), dtype=torch.bfloat16, device=self.device)
+        if n > self.max_rows:
+            raise ValueError("ingest rows exceed max_rows of the workspace")
+        self.fuse_ctx(taps, n, ctx)
+        rows = torch.stack([torch.arange(n, dtype=torch.int32), torch.full((n,), b, dtype=torch.int32),
+                            start + torch.arange(n, dtype=torch.int32)], dim=1).to(self.device)
+        cnt = torch.tensor([n], dtype=torch.int32, device=self.device)
+        self.inject_kv(ctx, n, rows, cnt, n)
+
+
+class Target(Protocol):
+    """What the loop needs from the target model (batch 1)."""
+
+    def reset(self) -> None: ...
+
+    def forward(self, tokens: Sequence[int]) -> tuple[np.ndarray, np.ndarray]:
+        """Append tokens; return (greedy argmax per row, taps [n, n_tap*H])."""
+
+    def truncate(self, length: int) -> None: ...
+
+
+def spec_generate(drafter: Drafter, target: Target, prompt: Sequence[int], max_new_tokens: int,
+                  stop_token_ids: Sequence[int] = (), temperature: float = 0.0):
+    """Greedy speculative decoding of one sequence with the device drafter.
+
+    Returns (tokens, accepted lengths per step)."""
+    if temperature != 0.0:
+        raise NotImplementedError("only greedy (temperature 0) verification is implemented")
+    if drafter.batch != 1:
+        raise ValueError("spec_generate drives one sequence")
+    torch = _torch()
+    dev = drafter.device
+    B = drafter.cfg.block
+    target.reset()
+    drafter.ctx_len.zero_()
+    a, taps = target.forward(list(prompt))
+    anchor = int(a[-1])
+    out = [anchor]
+    P = len(prompt)
+    drafter.ingest(0, to_device_bf16(np.asarray(taps, np.float32), dev))
+    stops = torch.tensor(list(stop_token_ids), dtype=torch.int32, device=dev) if stop_token_ids else None
+    budget = torch.tensor([max_new_tokens - 1], dtype=torch.int32, device=dev)
+    L = P
+    ms = []
+    stop_set = set(int(s) for s in stop_token_ids)
+    while len(out) < max_new_tokens and out[-1] not in stop_set:
+        drafter.anchor.fill_(anchor)
+        d = drafter.draft_block().cpu().numpy()[0]
+        at, taps = target.forward([anchor] + [int(t) for t in d])
+        tgt = torch.from_numpy(np.asarray(at, np.int32).reshape(1, B)).to(dev)
+        drafter.verify_accept(tgt, stops, budget)
+        m = int(drafter.accept_len.item())
+        target.truncate(L + m + 1)
+        ctx = drafter.fuse_ctx(to_device_bf16(np.asarray(taps, np.float32), dev), B)
+        drafter.inject_kv(ctx, B, drafter.commit_rows, drafter.n_commit, B)
+        n = int(drafter.n_emit.item())
+        out += [int(t) for t in drafter.emitted[0, :n].cpu().numpy()]
+        ms.append(m)
+        anchor = int(drafter.anchor_out.item())
+        L += m + 1
+        if int(drafter.done.item()):
+            break
+    return out[:max_new_tokens], ms

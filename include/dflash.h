@@ -1,0 +1,212 @@
+/*
+ * dflash.h — C ABI of the MI355X (gfx950) library for one DFlash-style draft
+ * step: fuse target taps into a context feature, inject it into every draft
+ * layer's KV cache, denoise a masked block in one forward pass, and accept the
+ * longest verified prefix with KV commit / rollback.
+ *
+ * Sources (prose only; none gives equations):
+ *   [P1] "DFlash: slik kan spekulativ dekoding gi opptil 6x raskere
+ *        AI-inferens", jansverre.net/?p=12023
+ *   [P2] DFlash news article, news.bpdata.com (address slug
+ *        "dflash-block-diffuzios-spekulativ-dekodolassal-akar-15")
+ *   [P3] "DFlash Crea Blocchi Interi di Token Contemporaneamente, Aumentando
+ *        Fino a 15x la Velocità su NVIDIA Blackwell", theaistack.guide
+ *   [P4] DFlash news article, 7minutos.es, 2026-06-26
+ *
+ * Conventions for every call
+ *   - bf16 tensors are 16-bit brain-float bit patterns, row-major, densely
+ *     packed unless a leading dimension is given. Matrices are [out, in].
+ *   - "device" pointers are GPU memory owned by the caller (for example torch
+ *     tensors); "host" pointers are CPU memory. The library never allocates,
+ *     frees or retains device memory, and never synchronises the stream.
+ *   - stream is a hipStream_t passed as void*; NULL means the null stream.
+ *     Work is enqueued asynchronously on it; all calls that share a dflash_kv
+ *     must use one stream (or be ordered by the caller).
+ *   - Argument checks that need no GPU run first and return an error before
+ *     any HIP call. Errors of kernel launch return DFLASH_ERR_HIP. Conditions
+ *     only visible on the device (a context that would overflow the cache) are
+ *     reported per sequence in dflash_kv.status, and that sequence is skipped.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dflash_status {
+  DFLASH_OK = 0,
+  DFLASH_ERR_NULL = -1,        /* a required pointer is NULL */
+  DFLASH_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  DFLASH_ERR_UNSUPPORTED = -3, /* a shape the kernels do not implement */
+  DFLASH_ERR_WORKSPACE = -4,   /* workspace too small */
+  DFLASH_ERR_CAPACITY = -5,    /* per-sequence: positions beyond max_ctx or the RoPE table */
+  DFLASH_ERR_HIP = -6          /* a HIP launch failed */
+} dflash_status;
+
+/* Drafter shape. Requirements checked at create: hidden, intermediate,
+ * n_q_heads*head_dim and n_tap*hidden multiples of 64; head_dim 64 or 128;
+ * n_q_heads a multiple of n_kv_heads; 2 <= block <= 16; 1 <= n_layers <= 16;
+ * 0 <= mask_id < vocab. */
+typedef struct dflash_config {
+  int32_t hidden;       /* H */
+  int32_t n_layers;     /* NL */
+  int32_t n_q_heads;    /* Hq */
+  int32_t n_kv_heads;   /* Hkv */
+  int32_t head_dim;     /* D */
+  int32_t intermediate; /* I (SwiGLU) */
+  int32_t vocab;        /* V */
+  int32_t n_tap;        /* number of tapped target layers */
+  int32_t block;        /* B: block rows per sequence (anchor + B-1 masks) */
+  int32_t mask_id;      /* token id that fills block rows 1..B-1 */
+  float rope_theta;
+  float rms_eps;
+} dflash_config;
+
+/* One draft layer; all device bf16.
+ *   g_in [H], g_post [H], g_q [D], g_k [D]     RMSNorm gains
+ *   w_qkv [(Hq+2Hkv)*D, H]  rows: q heads, then k heads, then v heads
+ *   w_o   [H, Hq*D]
+ *   w_gate, w_up [I, H]
+ *   w_down [H, I] */
+typedef struct dflash_layer_weights {
+  const void* g_in;
+  const void* w_qkv;
+  const void* g_q;
+  const void* g_k;
+  const void* w_o;
+  const void* g_post;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+} dflash_layer_weights;
+
+/* Whole drafter; device pointers unless noted.
+ *   embed, lm_head [V, H] bf16 (the target's, shared)
+ *   w_fc [H, n_tap*H] bf16, columns tap-major; g_fc [H], g_final [H] bf16
+ *   layers: HOST array of n_layers entries (copied at create)
+ *   rope: device fp32 [rope_max_pos, D/2, 2] = (cos, sin) of pos*theta^(-2i/D),
+ *         as written by dflash_rope_table. */
+typedef struct dflash_weights {
+  const void* embed;
+  const void* lm_head;
+  const void* w_fc;
+  const void* g_fc;
+  const void* g_final;
+  const dflash_layer_weights* layers;
+  const float* rope;
+  int32_t rope_max_pos;
+} dflash_weights;
+
+/* Draft KV cache of a batch of sequences; device memory.
+ *   k, v   bf16 [NL][batch][Hkv][max_ctx][D]
+ *   ctx_len int32 [batch]: committed context length L_b. Only inject_kv
+ *          advances it, so block slots written speculatively by draft_block
+ *          are dead until a commit overwrites them (rollback by construction).
+ *   status  int32 [batch]: 0, or DFLASH_ERR_CAPACITY set by the device. */
+typedef struct dflash_kv {
+  void* k;
+  void* v;
+  int32_t batch;
+  int32_t max_ctx;
+  int32_t* ctx_len;
+  int32_t* status;
+} dflash_kv;
+
+typedef struct dflash_model dflash_model;
+
+/* Check the shape, copy the layer table, and keep the (borrowed) weight
+ * pointers; they must outlive the model. Host only: no HIP call. */
+dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights* w,
+                                  dflash_model** out);
+void dflash_model_destroy(dflash_model* m);
+
+/* Host helper: cos/sin table for RoPE, computed in double and rounded to
+ * float. out: host float[max_pos * head_dim/2 * 2]. */
+dflash_status dflash_rope_table(float* out, int32_t max_pos, int32_t head_dim, float theta);
+
+/* Workspace (device scratch, caller-allocated) needed by calls that handle up
+ * to max_batch sequences, a cache of max_ctx slots and up to max_rows context
+ * rows per fuse/inject call. */
+size_t dflash_workspace_bytes(const dflash_model* m, int32_t max_batch, int32_t max_ctx,
+                              int32_t max_rows);
+
+/* S1 — context-feature fusion. [P3 "L'idea chiave: Il target sa meglio";
+ * P4 "La idea de que 'el objetivo sabe más'"]: the hidden states of several
+ * target layers are merged into one compact context feature.
+ *   taps  device bf16 [n_rows, n_tap*H], taps of one row layer-major
+ *   ctx   device bf16 [n_rows, H] out: RMSNorm(W_fc taps_r; g_fc)
+ * n_rows >= 0 (0 is a no-op). */
+dflash_status dflash_fuse_ctx(const dflash_model* m, const void* taps, int32_t n_rows, void* ctx,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* S2 — KV injection. [P3 "L'idea chiave: Il target sa meglio"; P4 "La idea
+ * de que 'el objetivo sabe más'"; P1 "Hva gjør DFlash annerledes enn vanlig
+ * spekulativ dekoding?"]: the context feature enters the key and value
+ * projections of every draft layer and stays in the draft KV cache.
+ * For every layer l and commit row i < *n_commit (device count):
+ *   (src, seq, pos) = commit_rows[i]
+ *   K^l[seq][g][pos] = RoPE(RMSNorm_head(W_k^l ctx[src]; g_k^l), pos)
+ *   V^l[seq][g][pos] = W_v^l ctx[src]
+ *   ctx_len[seq] = max(ctx_len[seq], pos + 1)
+ *   ctx          device bf16 [n_ctx_rows, H]
+ *   commit_rows  device int32 [max_commit, 3]
+ *   n_commit     device int32 [1], clamped to [0, max_commit]
+ * A row with src, seq or pos out of range is skipped; out-of-range pos also
+ * sets status[seq] = DFLASH_ERR_CAPACITY. */
+dflash_status dflash_inject_kv(const dflash_model* m, const void* ctx, int32_t n_ctx_rows,
+                               const int32_t* commit_rows, const int32_t* n_commit,
+                               int32_t max_commit, dflash_kv* kv, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* S3–S10 — one denoising pass over the masked block. [P1 "Hva gjør DFlash
+ * annerledes enn vanlig spekulativ dekoding?"; P3 "Come funziona il drafting a
+ * blocchi"; P2 "Hogyan működik a DFlash spekulatív dekódolás?"]
+ * Row j of sequence b sits at position L_b + j and holds anchor[b] (j = 0) or
+ * mask_id (j >= 1). Each layer appends the block's K/V at slots
+ * [L_b, L_b + B) and attends, unmasked, over slots [0, L_b + B).
+ *   anchor     device int32 [batch]
+ *   draft      device int32 [batch, B-1] out: argmax of rows 1..B-1,
+ *              lowest index on ties
+ *   dbg_logits device fp32 [batch*(B-1), V] or NULL
+ *   dbg_hidden device fp32 [NL+1, batch*B, H] or NULL: residual stream after
+ *              the embedding and after each layer
+ * status[b] is set to DFLASH_ERR_CAPACITY when L_b + B exceeds max_ctx or the
+ * RoPE table; that sequence's draft is then filled with -1. */
+dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
+                                 int32_t* draft, float* dbg_logits, float* dbg_hidden, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* S11 — greedy acceptance of the longest valid prefix. [P2 introduction: the
+ * target checks the block in parallel and keeps the longest valid prefix;
+ * P4 "Ejecutando DFlash" for stop tokens and the token budget]
+ *   draft          device int32 [batch, B-1]  d_1..d_{B-1}
+ *   target_argmax  device int32 [batch, B]    a_0..a_{B-1}
+ *   stop_ids       device int32 [n_stop] (may be NULL if n_stop == 0)
+ *   budget         device int32 [batch] in/out remaining tokens, or NULL
+ * Outputs (device int32):
+ *   accept_len [batch]  m_b = max k <= B-1 with d_j == a_{j-1} for all j <= k
+ *   anchor_out [batch]  a_m
+ *   emitted [batch, B]  a_0..a_m cut after the first stop id and to budget,
+ *                       -1 padded; n_emit [batch]; done [batch] (0/1)
+ *   commit_rows [batch*B, 3], n_commit [1]: (b*B + i, b, L_b + i) for
+ *                       i = 0..m_b, sequences in order
+ * ctx_len is read, never written (inject_kv commits). A sequence whose status
+ * is nonzero emits and commits nothing and is reported done. */
+dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,
+                                   const int32_t* draft, const int32_t* target_argmax,
+                                   const int32_t* stop_ids, int32_t n_stop, int32_t* budget,
+                                   int32_t* accept_len, int32_t* anchor_out, int32_t* emitted,
+                                   int32_t* n_emit, int32_t* done, int32_t* commit_rows,
+                                   int32_t* n_commit, void* stream);
+
+const char* dflash_status_string(dflash_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

@@ -1,0 +1,80 @@
+"""Shared pieces of the GPU parity tests: seeded cases, oracle conversion,
+tolerance checks. The oracle side always receives the exact bf16 (or fp32)
+values that the device path receives, widened to fp64."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from block_diffusion_drafter_target_amd import synth
+from oracle import ref
+
+# max |gpu - ref| / max |ref| for bf16 hidden states and logits
+TOL = 2e-2
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def as_f64(a: np.ndarray) -> np.ndarray:
+    return synth.bf16_to_f64(a) if a.dtype == np.uint16 else np.asarray(a, np.float64)
+
+
+def oracle_weights(W: dict) -> dict:
+    return {k: as_f64(v) for k, v in W.items()}
+
+
+def to_np_bf16(t) -> np.ndarray:
+    """torch bf16 tensor -> fp64 numpy (exact)."""
+    import torch
+    u = t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+    return synth.bf16_to_f64(u)
+
+
+def check_rel(got, want, tol=TOL, what=""):
+    e = ref.rel_err(got, want)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    assert e <= tol, f"{what}: rel err {e:.3e} > {tol}"
+    return e
+
+
+def check_tokens(gpu_tok, gpu_logits, ref_logits, what=""):
+    """Tokens: the device argmax equals the argmax of its own fp32 logits (same
+    precision, bit exact); against the fp64 reference a different token is
+    allowed only inside the tie band z*_ref - z*_gpu <= 2 max|z_gpu - z_ref|.
+    Returns the number of rows decided inside the band."""
+    gpu_tok = np.asarray(gpu_tok).reshape(-1)
+    gl = np.asarray(gpu_logits, np.float64).reshape(len(gpu_tok), -1)
+    rl = np.asarray(ref_logits, np.float64).reshape(len(gpu_tok), -1)
+    assert np.array_equal(gpu_tok, np.argmax(gl, axis=1)), f"{what}: token is not the argmax of its logits"
+    rt = np.argmax(rl, axis=1)
+    band = 0
+    for i in np.nonzero(gpu_tok != rt)[0]:
+        err = np.max(np.abs(gl[i] - rl[i]))
+        gap = rl[i, rt[i]] - rl[i, gpu_tok[i]]
+        assert gap <= 2 * err, f"{what}: row {i} token {gpu_tok[i]} vs {rt[i]}, gap {gap:.3e} > 2*{err:.3e}"
+        band += 1
+    return band
+
+
+# small shapes that exercise every kernel branch (see the parity tests)
+SHAPES = {
+    # GQA G=4, D=128, B=16, 80 block rows (two GEMM row chunks), ragged and
+    # empty contexts, vocab not a multiple of 64
+    "gqa-d128": synth.DraftConfig(name="gqa-d128", hidden=512, n_layers=2, n_q_heads=8, n_kv_heads=2,
+                                  head_dim=128, intermediate=1024, vocab=4144, n_tap=3, block=16,
+                                  batch=5, ctx_len=0),
+    # G=8, D=64 (two query tiles per wave), k = 320 and 1600 (partial k blocks)
+    "g8-d64": synth.DraftConfig(name="g8-d64", hidden=320, n_layers=3, n_q_heads=16, n_kv_heads=2,
+                                head_dim=64, intermediate=640, vocab=1008, n_tap=5, block=16,
+                                batch=2, ctx_len=0),
+    # block 12 (three query tiles, one idle wave), MHA-free G=4
+    "b12": synth.DraftConfig(name="b12", hidden=256, n_layers=2, n_q_heads=8, n_kv_heads=2,
+                             head_dim=64, intermediate=512, vocab=512, n_tap=2, block=12,
+                             batch=3, ctx_len=0),
+}
+
+CTX = {"gqa-d128": [1, 300, 777, 0, 64], "g8-d64": [500, 33], "b12": [129, 0, 64]}

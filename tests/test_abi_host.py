@@ -1,0 +1,151 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+that include/dflash.h declares, and rejects bad arguments before any HIP call."""
+import ctypes as C
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_diffusion_drafter_target_amd import binding as bd
+from block_diffusion_drafter_target_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_step_calls():
+    names = declared_functions()
+    for n in ("dflash_fuse_ctx", "dflash_inject_kv", "dflash_draft_block", "dflash_verify_accept"):
+        assert n in names
+    assert set(names) == set(bd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bd.load()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def _cfg(**kw):
+    c = synth.CONFIGS["c2"]
+    d = dict(hidden=c.hidden, n_layers=c.n_layers, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads,
+             head_dim=c.head_dim, intermediate=c.intermediate, vocab=c.vocab, n_tap=c.n_tap,
+             block=c.block, mask_id=c.mask_id, rope_theta=c.rope_theta, rms_eps=c.rms_eps)
+    d.update(kw)
+    return bd.dflash_config(**d)
+
+
+def _fake_weights(n_layers):
+    # non-null dummy addresses: create never dereferences them
+    layers = (bd.dflash_layer_weights * n_layers)()
+    for l in range(n_layers):
+        for f in ("g_in", "w_qkv", "g_q", "g_k", "w_o", "g_post", "w_gate", "w_up", "w_down"):
+            setattr(layers[l], f, 0x1000)
+    w = bd.dflash_weights(embed=0x1000, lm_head=0x1000, w_fc=0x1000, g_fc=0x1000, g_final=0x1000,
+                          layers=layers, rope=0x1000, rope_max_pos=4096)
+    return w, layers
+
+
+def _create(cfg, w):
+    h = C.c_void_p()
+    rc = bd.load().dflash_model_create(C.byref(cfg), C.byref(w), C.byref(h))
+    return rc, h.value
+
+
+def test_model_create_validation():
+    w, keep = _fake_weights(5)
+    rc, h = _create(_cfg(), w)
+    assert rc == bd.DFLASH_OK and h
+    bd.dflash_model_destroy(h)
+    bad = {
+        "head_dim": (96, bd.DFLASH_ERR_UNSUPPORTED),
+        "block": (17, bd.DFLASH_ERR_UNSUPPORTED),
+        "n_kv_heads": (7, bd.DFLASH_ERR_SHAPE),
+        "hidden": (4000, bd.DFLASH_ERR_UNSUPPORTED),
+        "mask_id": (151936, bd.DFLASH_ERR_SHAPE),
+        "vocab": (151937, bd.DFLASH_ERR_UNSUPPORTED),
+        "n_layers": (17, bd.DFLASH_ERR_UNSUPPORTED),
+        "rms_eps": (0.0, bd.DFLASH_ERR_SHAPE),
+    }
+    for field, (val, code) in bad.items():
+        rc, h = _create(_cfg(**{field: val}), w)
+        assert rc == code, field
+        assert not h
+    w.w_fc = None
+    assert _create(_cfg(), w)[0] == bd.DFLASH_ERR_NULL
+    w, keep = _fake_weights(5)
+    keep[3].w_down = None
+    assert _create(_cfg(), w)[0] == bd.DFLASH_ERR_NULL
+
+
+def test_calls_reject_bad_arguments_without_a_gpu():
+    lib = bd.load()
+    w, keep = _fake_weights(5)
+    rc, h = _create(_cfg(), w)
+    assert rc == 0
+    try:
+        ws_need = bd.dflash_workspace_bytes(h, 1, 2048, 16)
+        assert ws_need > 0
+        assert bd.dflash_workspace_bytes(h, 8, 2048, 16) > ws_need
+        kv = bd.dflash_kv(k=0x1000, v=0x1000, batch=1, max_ctx=2048, ctx_len=0x1000, status=0x1000)
+        # workspace too small
+        assert lib.dflash_draft_block(h, C.byref(kv), 0x1000, 0x1000, None, None, 0x1000,
+                                      ws_need - 1, None) == bd.DFLASH_ERR_WORKSPACE
+        # null pointers
+        assert lib.dflash_draft_block(h, C.byref(kv), None, 0x1000, None, None, 0x1000,
+                                      ws_need, None) == bd.DFLASH_ERR_NULL
+        assert lib.dflash_draft_block(None, C.byref(kv), 0x1000, 0x1000, None, None, 0x1000,
+                                      ws_need, None) == bd.DFLASH_ERR_NULL
+        # cache smaller than one block, batch out of range
+        small = bd.dflash_kv(k=0x1000, v=0x1000, batch=1, max_ctx=8, ctx_len=0x1000, status=0x1000)
+        assert lib.dflash_draft_block(h, C.byref(small), 0x1000, 0x1000, None, None, 0x1000,
+                                      ws_need, None) == bd.DFLASH_ERR_SHAPE
+        big = bd.dflash_kv(k=0x1000, v=0x1000, batch=5000, max_ctx=2048, ctx_len=0x1000, status=0x1000)
+        assert lib.dflash_draft_block(h, C.byref(big), 0x1000, 0x1000, None, None, 0x1000,
+                                      1 << 40, None) == bd.DFLASH_ERR_SHAPE
+        # fuse: zero rows is a no-op, negative rows a shape error, tiny workspace rejected
+        assert lib.dflash_fuse_ctx(h, None, 0, None, None, 0, None) == bd.DFLASH_OK
+        assert lib.dflash_fuse_ctx(h, 0x1000, -1, 0x1000, 0x1000, 1 << 30, None) == bd.DFLASH_ERR_SHAPE
+        assert lib.dflash_fuse_ctx(h, 0x1000, 16, 0x1000, 0x1000, 16, None) == bd.DFLASH_ERR_WORKSPACE
+        # inject: nothing to commit is a no-op; missing count pointer rejected
+        assert lib.dflash_inject_kv(h, 0x1000, 16, 0x1000, 0x1000, 0, C.byref(kv), 0x1000, 1 << 30,
+                                    None) == bd.DFLASH_OK
+        assert lib.dflash_inject_kv(h, 0x1000, 16, 0x1000, None, 16, C.byref(kv), 0x1000, 1 << 30,
+                                    None) == bd.DFLASH_ERR_NULL
+        assert lib.dflash_inject_kv(h, 0x1000, 16, 0x1000, 0x1000, 16, C.byref(kv), 0x1000, 16,
+                                    None) == bd.DFLASH_ERR_WORKSPACE
+        # verify: negative stop count, stop ids missing
+        args = [0x1000] * 2
+        outs = [0x1000] * 7
+        assert lib.dflash_verify_accept(h, C.byref(kv), *args, None, -1, None, *outs, None) == bd.DFLASH_ERR_SHAPE
+        assert lib.dflash_verify_accept(h, C.byref(kv), *args, None, 2, None, *outs, None) == bd.DFLASH_ERR_NULL
+        assert lib.dflash_verify_accept(h, C.byref(kv), None, 0x1000, None, 0, None, *outs,
+                                        None) == bd.DFLASH_ERR_NULL
+    finally:
+        bd.dflash_model_destroy(h)
+
+
+def test_rope_table_values():
+    max_pos, D, theta = 300, 64, 1e6
+    out = np.empty(max_pos * D // 2 * 2, np.float32)
+    bd.dflash_rope_table(out.ctypes.data_as(C.c_void_p), max_pos, D, theta)
+    out = out.reshape(max_pos, D // 2, 2)
+    for p in (0, 1, 17, 299):
+        for i in (0, 1, 5, 31):
+            ang = p * theta ** (-2.0 * i / D)
+            assert out[p, i, 0] == np.float32(math.cos(ang))
+            assert out[p, i, 1] == np.float32(math.sin(ang))
+    assert bd.load().dflash_rope_table(None, 4, 64, 1e6) == bd.DFLASH_ERR_NULL
+    assert bd.load().dflash_rope_table(out.ctypes.data_as(C.c_void_p), 4, 63, 1e6) == bd.DFLASH_ERR_SHAPE
+
+
+def test_status_strings():
+    assert bd.status_string(0) == "ok"
+    assert "workspace" in bd.status_string(bd.DFLASH_ERR_WORKSPACE)
