@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of one DFlash-style draft step on one MI355X (gfx950).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+
+One step = fuse_ctx + inject_kv of the rows committed by the previous step,
+draft_block (5-layer Qwen3-8B-shaped drafter, block 16, context 1024 at the
+start) and verify_accept against a synthetic target argmax whose accepted
+prefix lengths follow a geometric law with p = 0.8, truncated at B-1. The
+target tokens depend on the step's own drafts, so they are built in an untimed
+first pass over the same steps; the state is then reset and the steps replayed
+(bit-identically) with the recorded targets, so the timed region holds only
+library calls. Inputs are seeded synthetic tensors resident in HBM.
+
+Prints one JSON line: drafted tokens/s (batch*(B-1) per step), the step
+latency, the roofline of the dominant kernel (the LM-head GEMM with fused
+argmax: it streams the whole [V, H] head once per step) and, on rank 0, the
+fp64 oracle timed on the host cores for the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "draft-step latency (µs) + drafted tokens/s, 5-layer drafter, block 16; %roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def synth_target(torch, draft, m, rnd, vocab):
+    """Target argmax rows [batch, B] whose accepted prefix with draft is m."""
+    batch, bm1 = draft.shape
+    j = torch.arange(bm1 + 1, device=draft.device)[None, :]
+    d_ext = torch.nn.functional.pad(draft, (0, 1))
+    t = torch.where(j < m[:, None], d_ext, rnd)
+    return torch.where((j == m[:, None]) & (m[:, None] < bm1), (d_ext + 1) % (vocab - 1), t)
+
+
+def cpu_baseline(cfg, W, L, repeats: int):
+    """The fp64 oracle's draft step on the host cores (median of repeats)."""
+    from threadpoolctl import threadpool_info
+
+    from block_diffusion_drafter_target_amd import synth
+    from oracle import ref
+    ocfg = ref.OracleConfig.from_any(cfg)
+    t0 = time.time()
+    WO = {k: synth.bf16_to_f64(v) for k, v in W.items()}
+    prep = time.time() - t0
+    B, batch = cfg.block, cfg.batch
+    g = np.random.default_rng(0)
+    cache = ref.new_cache(ocfg, batch, L + B)
+    cache["k"][:, :, :L] = g.standard_normal(cache["k"][:, :, :L].shape)
+    cache["v"][:, :, :L] = g.standard_normal(cache["v"][:, :, :L].shape)
+    taps = synth.bf16_to_f64(synth.make_taps(cfg, batch * B, tid=999))
+    anchor = synth.make_anchors(cfg)
+    times = []
+    for _ in range(repeats):
+        t = time.perf_counter()
+        ctx = ref.fuse_ctx(ocfg, WO, taps)
+        ref.inject_kv(ocfg, WO, ctx, [(b * B + i, b, L - B + i) for b in range(batch) for i in range(B)], cache)
+        r = ref.draft_block(ocfg, WO, cache, [L] * batch, anchor)
+        tgt = np.concatenate([r["draft"], np.zeros((batch, 1), np.int64)], axis=1)
+        ref.verify_accept(r["draft"], tgt, [L] * batch)
+        times.append(time.perf_counter() - t)
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = int(blas[0]["num_threads"]) if blas else (os.cpu_count() or 1)
+    t_step = float(np.median(times))
+    return {"value": batch * (B - 1) / t_step, "unit": "drafted tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"one full draft step (fuse+inject of {batch * B} rows, {cfg.n_layers} layers at "
+                       f"context {L}, full LM head, verify) in fp64 numpy, median of {repeats}; "
+                       f"step {t_step * 1e3:.0f} ms; weight upcast to fp64 ({prep:.1f} s) not timed"),
+            "ms_per_step": t_step * 1e3}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from block_diffusion_drafter_target_amd import Drafter, synth
+    from block_diffusion_drafter_target_amd import binding as bd
+
+    cfg = synth.CONFIGS[args.config]
+    B, V, H, batch = cfg.block, cfg.vocab, cfg.hidden, cfg.batch
+    lens = synth.make_ctx_lens(cfg)
+    n_break = min(args.steps, 20)  # steps of the per-phase breakdown pass
+    n_steps = 1 + args.warmup + args.steps + n_break
+    max_ctx = int(lens.max()) + (n_steps + 2) * B + 64
+    t0 = time.time()
+    W = synth.make_weights(cfg)
+    log(f"weights generated in {time.time() - t0:.1f} s")
+    dev = torch.device("cuda")
+    dr = Drafter(cfg, W, batch=batch, max_ctx=max_ctx, max_rows=max(int(lens.max()), batch * B), device=dev)
+
+    # context ingest (fuse + inject of the whole prompt), timed on its own
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ingest_ms = 0.0
+    for b in range(batch):
+        taps = torch.from_numpy(synth.make_taps(cfg, int(lens[b]), tid=b).view(np.int16)).view(torch.bfloat16).to(dev)
+        ev0.record()
+        dr.ingest(b, taps)
+        ev1.record()
+        torch.cuda.synchronize()
+        ingest_ms += ev0.elapsed_time(ev1)
+        del taps
+    assert dr.ctx_len.cpu().numpy().tolist() == lens.tolist()
+
+    # per-step synthetic inputs, resident before timing
+    taps_step = torch.from_numpy(synth.make_taps(cfg, batch * B, tid=999).view(np.int16)).view(torch.bfloat16).to(dev)
+    m_all = torch.from_numpy(np.stack([synth.geometric_accept(batch, B, 0.8, step=i) for i in range(n_steps)])).to(dev)
+    g = np.random.default_rng(synth.SEED_TARGET)
+    rnd_all = torch.from_numpy(g.integers(0, V - 1, size=(n_steps, batch, B)).astype(np.int32)).to(dev)
+    dr.anchor.copy_(torch.from_numpy(synth.make_anchors(cfg)))
+
+    # bootstrap: one draft + verify so that the first step has committed rows
+    dr.draft_block(anchor=dr.anchor)
+    dr.verify_accept(synth_target(torch, dr.draft, m_all[0], rnd_all[0], V))
+    saved = {k: getattr(dr, k).clone() for k in ("ctx_len", "anchor_out", "commit_rows", "n_commit")}
+
+    def step(tgt):
+        dr.fuse_ctx(taps_step, batch * B, dr.ctx)
+        dr.inject_kv(dr.ctx, batch * B, dr.commit_rows, dr.n_commit, batch * B)
+        dr.draft_block(anchor=dr.anchor_out)
+        dr.verify_accept(tgt)
+
+    # pass 1 (untimed): the target tokens of every step
+    targets = [None]
+    for i in range(1, n_steps):
+        dr.fuse_ctx(taps_step, batch * B, dr.ctx)
+        dr.inject_kv(dr.ctx, batch * B, dr.commit_rows, dr.n_commit, batch * B)
+        dr.draft_block(anchor=dr.anchor_out)
+        targets.append(synth_target(torch, dr.draft, m_all[i], rnd_all[i], V).clone())
+        dr.verify_accept(targets[i])
+    torch.cuda.synchronize()
+    for k, v in saved.items():
+        getattr(dr, k).copy_(v)
+
+    # pass 2: warmup, timed steps, per-phase breakdown steps
+    for i in range(args.warmup):
+        step(targets[1 + i])
+    torch.cuda.synchronize()
+    assert int(dr.status.abs().max()) == 0, "a sequence ran out of cache"
+    bd.dflash_profile_enable(["lm_head"])
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(targets[1 + args.warmup + i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    lm_ms, lm_n = bd.dflash_profile_read("lm_head")
+    bd.dflash_profile_enable([])
+    ctx_after = dr.ctx_len.cpu().numpy()
+    assert int(dr.status.abs().max()) == 0
+    # the replay accepted exactly the recorded prefix lengths
+    assert dr.accept_len.cpu().numpy().tolist() == m_all[args.warmup + args.steps].cpu().numpy().tolist()
+
+    bd.dflash_profile_enable(list(bd.PHASES))
+    for i in range(n_break):
+        step(targets[1 + args.warmup + args.steps + i])
+    torch.cuda.synchronize()
+    phases = {}
+    for name in bd.PHASES:
+        t, n = bd.dflash_profile_read(name)
+        if n:
+            phases[name] = {"us_per_step": round(1e3 * t / n_break, 2), "launches_per_step": n / n_break,
+                            "us_per_launch": round(1e3 * t / n, 2)}
+    bd.dflash_profile_enable([])
+
+    # roofline of the dominant kernel: the LM head streams V*H bf16 weights
+    Ml = batch * (B - 1)
+    lm_bytes = V * H * 2 + Ml * H * 2 + Ml * 8
+    lm_us = 1e3 * lm_ms / max(1, lm_n)
+    achieved = lm_bytes / (lm_us * 1e-6) / 1e9
+    roofline = {"kernel": "gemm_stream_kernel<1,4,argmax> (LM head + fused argmax)", "bound": "hbm",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": lm_bytes, "us_per_launch": round(lm_us, 2)}
+    # whole-step weight streaming, for context
+    layer_bytes = 2 * H * (cfg.qkv_width + cfg.q_width + 2 * cfg.intermediate) + 2 * cfg.intermediate * H
+    step_weight_bytes = cfg.n_layers * layer_bytes + V * H * 2 + H * cfg.tap_width * 2 + \
+        cfg.n_layers * 2 * cfg.kv_width * H * 2
+    drafted = batch * (B - 1)
+    out = {
+        "metric": METRIC,
+        "value": round(drafted / (ms * 1e-3), 1),
+        "unit": "drafted tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "latency_us": round(ms * 1e3, 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": (f"{cfg.name} drafter: H {H}, {cfg.n_q_heads}/{cfg.n_kv_heads} heads of "
+                                f"{cfg.head_dim}, I {cfg.intermediate}, V {V}, {cfg.n_tap} taps; batch {batch}, "
+                                f"block {B}, context {int(lens.min())}..{int(lens.max())} at start "
+                                f"(ends at {int(ctx_after.max())}); geometric acceptance p=0.8"),
+                   "batch": batch, "block": B, "context": int(lens.max()), "layers": cfg.n_layers},
+        "roofline": roofline,
+        "step_weight_bytes": step_weight_bytes,
+        "step_weight_stream_frac": round(step_weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "ingest_ms": round(ingest_ms, 3),
+        "phases": phases,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host ...")
+        out["cpu_baseline"] = cpu_baseline(cfg, W, int(lens.max()), args.cpu_repeats)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

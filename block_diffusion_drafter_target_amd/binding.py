@@ -22,7 +22,11 @@ DFLASH_ERR_HIP = -6
 
 EXPORTED = ("dflash_model_create", "dflash_model_destroy", "dflash_rope_table",
             "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_inject_kv",
-            "dflash_draft_block", "dflash_verify_accept", "dflash_status_string")
+            "dflash_draft_block", "dflash_verify_accept", "dflash_status_string",
+            "dflash_profile_enable", "dflash_profile_read", "dflash_pack_matrix")
+
+PHASES = {"lm_head": 0, "attention": 1, "qkv": 2, "o": 3, "gate_up": 4, "down": 5, "fuse": 6,
+          "inject": 7, "verify": 8}
 
 
 class dflash_config(C.Structure):
@@ -78,6 +82,12 @@ def load() -> C.CDLL:
     lib.dflash_draft_block.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp, vp, sz, vp]
     lib.dflash_verify_accept.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, i32, vp, vp, vp, vp,
                                          vp, vp, vp, vp, vp]
+    lib.dflash_pack_matrix.argtypes = [vp, vp, i32, i32, vp]
+    lib.dflash_pack_matrix.restype = i32
+    lib.dflash_profile_enable.argtypes = [C.c_uint32]
+    lib.dflash_profile_enable.restype = i32
+    lib.dflash_profile_read.argtypes = [i32, C.POINTER(C.c_double), C.POINTER(C.c_int32)]
+    lib.dflash_profile_read.restype = i32
     lib.dflash_status_string.argtypes = [i32]
     lib.dflash_status_string.restype = C.c_char_p
     for fn in ("dflash_model_create", "dflash_rope_table", "dflash_fuse_ctx", "dflash_inject_kv",
@@ -146,3 +156,23 @@ def dflash_verify_accept(model, kv, draft, target_argmax, stop_ids, n_stop, budg
     _check("dflash_verify_accept", load().dflash_verify_accept(
         model, C.byref(kv), draft, target_argmax, stop_ids, n_stop, budget, accept_len, anchor_out,
         emitted, n_emit, done, commit_rows, n_commit, stream))
+
+
+def dflash_pack_matrix(src, dst, rows: int, cols: int, stream) -> None:
+    _check("dflash_pack_matrix", load().dflash_pack_matrix(src, dst, rows, cols, stream))
+
+
+def dflash_profile_enable(phases=()) -> None:
+    """Time the named phases (an empty list switches timing off)."""
+    mask = 0
+    for p in phases:
+        mask |= 1 << (PHASES[p] if isinstance(p, str) else int(p))
+    _check("dflash_profile_enable", load().dflash_profile_enable(mask))
+
+
+def dflash_profile_read(phase) -> tuple[float, int]:
+    """(summed ms, launches) of one phase (name or id) since profiling was enabled."""
+    pid = PHASES[phase] if isinstance(phase, str) else int(phase)
+    t, n = C.c_double(), C.c_int32()
+    _check("dflash_profile_read", load().dflash_profile_read(pid, C.byref(t), C.byref(n)))
+    return t.value, n.value

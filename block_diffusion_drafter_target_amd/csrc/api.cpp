@@ -23,10 +23,41 @@ namespace {
 
 using dfl::GemmParams;
 
+// ---------------------------------------------------------------------------
+// optional per-phase event timing (benchmarks)
+namespace prof {
+struct Rec {
+  int phase;
+  hipEvent_t a, b;
+};
+uint32_t mask = 0;
+std::vector<Rec> recs;  // events are created once and reused
+size_t used = 0;
+
+struct Scope {
+  Rec* r = nullptr;
+  hipStream_t st;
+  Scope(int phase, hipStream_t s) : st(s) {
+    if (!(mask >> phase & 1u)) return;
+    if (used == recs.size()) {
+      Rec n{phase, nullptr, nullptr};
+      if (hipEventCreate(&n.a) != hipSuccess || hipEventCreate(&n.b) != hipSuccess) return;
+      recs.push_back(n);
+    }
+    r = &recs[used++];
+    r->phase = phase;
+    if (hipEventRecord(r->a, st) != hipSuccess) r = nullptr;
+  }
+  ~Scope() {
+    if (r) (void)hipEventRecord(r->b, st);
+  }
+};
+}  // namespace prof
+
 constexpr int kMaxBatch = 4096;
 constexpr int kRowChunk = 1024;  // rows per fuse / inject GEMM pass
 constexpr int kGemmRows = 64;    // rows per weight-streaming GEMM launch
-constexpr int kTargetWGs = 768;  // workgroups a GEMM launch aims for (3 per CU)
+constexpr int kTargetWGs = 384;  // workgroups a split-K GEMM launch aims for
 
 inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -36,19 +67,19 @@ struct GemmPlan {
 };
 
 // Tile shape and split-K for Y = A W^T with up to kGemmRows rows per launch.
-GemmPlan plan_gemm(int M, int N, int K, int nz, bool argmax) {
+// NF = 4 weight fragments per workgroup when one activation tile suffices
+// (the widest tile the register file holds without spills), else 2. Split-K
+// only in partial mode, to bring the grid to about kTargetWGs workgroups.
+GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
   GemmPlan g;
   const int rows = std::min(M, kGemmRows);
   g.mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   g.nf = g.mt == 1 ? 4 : 2;
-  long long tiles = cdiv(N, 16 * g.nf) * nz;
-  if (g.nf == 4 && tiles < 2 * kTargetWGs / 3) {
-    g.nf = 2;
-    tiles = cdiv(N, 32) * nz;
-  }
+  const int out_frags = mode == dfl::kGemmSwiglu ? g.nf / 2 : g.nf;
+  const long long tiles = cdiv(N, 16 * out_frags) * nz;
   const int kblocks = (int)cdiv(K, 128);
   int s = 1;
-  if (!argmax) {
+  if (mode == dfl::kGemmPartial) {
     s = (int)std::max<long long>(1, cdiv(kTargetWGs, tiles));
     s = std::min(s, std::max(1, kblocks / 4));  // at least one 128-k block per wave
   }
@@ -60,7 +91,7 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, bool argmax) {
 
 // Partial buffer (floats) that run_gemm needs for M rows.
 size_t gemm_partial_floats(int M, int N, int K, int nz) {
-  const GemmPlan g = plan_gemm(M, N, K, nz, false);
+  const GemmPlan g = plan_gemm(M, N, K, nz, dfl::kGemmPartial);
   return (size_t)nz * g.splits * M * N;
 }
 
@@ -74,23 +105,25 @@ struct GemmCall {
   long long ldw = 0;
   int n_split = 0;
   int M = 0, N = 0, K = 0, nz = 1;
+  int mode = dfl::kGemmPartial;
   float* P = nullptr;                 // partial mode
   unsigned long long* keys = nullptr; // argmax mode
   float* dbg = nullptr;
   long long ld_dbg = 0;
+  uint16_t* out = nullptr;            // swiglu mode
+  long long ld_out = 0;
 };
 
 // Runs the weight-streaming GEMM over all M rows (kGemmRows per launch).
 // Partial output P[z][s][M][N]; returns the split count through *splits.
 hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
-  const bool argmax = c.keys != nullptr;
-  const GemmPlan g = plan_gemm(c.M, c.N, c.K, c.nz, argmax);
+  const GemmPlan g = plan_gemm(c.M, c.N, c.K, c.nz, c.mode);
   if (splits) *splits = g.splits;
   for (int m0 = 0; m0 < c.M; m0 += kGemmRows) {
     GemmParams p;
     std::memset(&p, 0, sizeof(p));
     const int rows = std::min(kGemmRows, c.M - m0);
-    const GemmPlan gl = plan_gemm(rows, c.N, c.K, c.nz, argmax);
+    const GemmPlan gl = plan_gemm(rows, c.N, c.K, c.nz, c.mode);
     // every chunk keeps the split layout of the full call
     p.A = c.a_idx ? c.A : c.A + (long long)m0 * c.lda;
     p.lda = c.lda;
@@ -102,42 +135,44 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
       p.W1[z] = c.W1[z] ? c.W1[z] : c.W0[z];
     }
     p.ldw = c.ldw;
-    p.n_split = c.W1[0] ? c.n_split : c.N;
+    p.n_split = (c.W1[0] && c.mode != dfl::kGemmSwiglu) ? c.n_split : c.N;
     p.M = rows;
     p.N = c.N;
     p.K = c.K;
     p.splits = g.splits;
     p.k_per_split = g.k_per_split;
-    if (argmax) {
+    if (c.mode == dfl::kGemmArgmax) {
       p.keys = c.keys + m0;
       p.dbg = c.dbg ? c.dbg + (long long)m0 * c.ld_dbg : nullptr;
       p.ld_dbg = c.ld_dbg;
+    } else if (c.mode == dfl::kGemmSwiglu) {
+      p.out = c.out + (long long)m0 * c.ld_out;
+      p.ld_out = c.ld_out;
     } else {
       p.P = c.P + (long long)m0 * c.N;
       p.p_s_stride = (long long)c.M * c.N;
       p.p_z_stride = (long long)g.splits * c.M * c.N;
     }
-    hipError_t e = dfl::launch_gemm_stream(p, gl.mt, gl.nf, argmax ? dfl::kGemmArgmax : dfl::kGemmPartial,
-                                           c.nz, st);
+    hipError_t e = dfl::launch_gemm_stream(p, gl.mt, gl.nf, c.mode, c.nz, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 struct AttnPlan {
-  int chunk, n_chunks, gb_pad;
+  int n_chunks, gb_pad;
 };
 
+// Key chunks per (sequence, kv head): enough workgroups for the chip
+// (about 512) without chunks shorter than one 64-key slice of the cache.
 AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx) {
   AttnPlan a;
   const int G = c.n_q_heads / c.n_kv_heads;
   a.gb_pad = (int)cdiv(G * c.block, 16) * 16;
   const long long units = (long long)batch * c.n_kv_heads;
-  long long chunk = cdiv(units * max_ctx, 1024);
-  chunk = cdiv(chunk, 64) * 64;
-  chunk = std::max<long long>(64, std::min<long long>(chunk, 8192));
-  a.chunk = (int)chunk;
-  a.n_chunks = (int)cdiv(max_ctx, chunk);
+  long long n = cdiv(512, units);
+  n = std::min<long long>(n, cdiv(max_ctx, 64));
+  a.n_chunks = (int)std::max<long long>(1, std::min<long long>(n, 64));
   return a;
 }
 
@@ -172,7 +207,6 @@ DraftWs draft_ws(const dflash_config& c, int batch, int max_ctx) {
   size_t pf = 0;
   pf = std::max(pf, gemm_partial_floats((int)Mb, qkvw, H, 1));
   pf = std::max(pf, gemm_partial_floats((int)Mb, H, qw, 1));
-  pf = std::max(pf, gemm_partial_floats((int)Mb, 2 * c.intermediate, H, 1));
   pf = std::max(pf, gemm_partial_floats((int)Mb, H, c.intermediate, 1));
   w.P = take(pf * 4);
   w.total = off;
@@ -235,6 +269,7 @@ dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights
       ((long long)c.n_tap * c.hidden) % 64 || c.vocab % 16)
     return DFLASH_ERR_UNSUPPORTED;
   if ((c.n_q_heads / c.n_kv_heads) * c.block > 256) return DFLASH_ERR_UNSUPPORTED;
+  if (c.hidden > 8192) return DFLASH_ERR_UNSUPPORTED;  // row kernels hold a row in registers
   if (!w->embed || !w->lm_head || !w->w_fc || !w->g_fc || !w->g_final || !w->layers || !w->rope)
     return DFLASH_ERR_NULL;
   if (w->rope_max_pos < 1) return DFLASH_ERR_SHAPE;
@@ -303,7 +338,11 @@ dflash_status dflash_fuse_ctx(const dflash_model* m, const void* taps, int32_t n
     g.K = K;
     g.P = P;
     int splits = 1;
-    hipError_t e = run_gemm(g, st, &splits);
+    hipError_t e;
+    {
+      prof::Scope ps(DFLASH_PHASE_FUSE, st);
+      e = run_gemm(g, st, &splits);
+    }
     if (e != hipSuccess) return DFLASH_ERR_HIP;
     dfl::RowNormParams rn;
     std::memset(&rn, 0, sizeof(rn));
@@ -347,15 +386,19 @@ dflash_status dflash_inject_kv(const dflash_model* m, const void* ctx, int32_t n
     g.a_idx_stride = 3;
     g.a_idx_max = n_ctx_rows;
     g.nz = c.n_layers;
-    for (int l = 0; l < c.n_layers; ++l)  // k rows then v rows of each layer's W_qkv
-      g.W0[l] = static_cast<const uint16_t*>(m->layers[l].w_qkv) + (long long)Hq * D * H;
+    for (int l = 0; l < c.n_layers; ++l)  // k rows then v rows of each layer's (packed) W_qkv
+      g.W0[l] = static_cast<const uint16_t*>(m->layers[l].w_qkv) + (long long)(Hq * D / 16) * (H / 32) * 512;
     g.ldw = H;
     g.M = rows;
     g.N = N;
     g.K = H;
     g.P = P;
     int splits = 1;
-    hipError_t e = run_gemm(g, st, &splits);
+    hipError_t e;
+    {
+      prof::Scope ps(DFLASH_PHASE_INJECT, st);
+      e = run_gemm(g, st, &splits);
+    }
     if (e != hipSuccess) return DFLASH_ERR_HIP;
     dfl::InjectPostParams ip;
     std::memset(&ip, 0, sizeof(ip));
@@ -452,7 +495,11 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     g.N = qkvw;
     g.K = H;
     g.P = P;
-    if ((e = run_gemm(g, st, &splits)) != hipSuccess) return DFLASH_ERR_HIP;
+    {
+      prof::Scope ps(DFLASH_PHASE_QKV, st);
+      e = run_gemm(g, st, &splits);
+    }
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
     dfl::QkvPostParams qp;
     std::memset(&qp, 0, sizeof(qp));
     qp.P = P;
@@ -487,14 +534,17 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     at.Hkv = Hkv;
     at.B = B;
     at.max_ctx = kv->max_ctx;
-    at.chunk = ap.chunk;
     at.n_chunks = ap.n_chunks;
     at.gb_pad = ap.gb_pad;
     at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     at.pm = pm;
     at.pl = pl;
     at.po = po;
-    if ((e = dfl::launch_attention(at, D, st)) != hipSuccess) return DFLASH_ERR_HIP;
+    {
+      prof::Scope ps(DFLASH_PHASE_ATTENTION, st);
+      e = dfl::launch_attention(at, D, st);
+    }
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
     dfl::MergeParams mp;
     std::memset(&mp, 0, sizeof(mp));
     mp.pm = pm;
@@ -507,7 +557,6 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     mp.Hkv = Hkv;
     mp.B = B;
     mp.D = D;
-    mp.chunk = ap.chunk;
     mp.n_chunks = ap.n_chunks;
     mp.gb_pad = ap.gb_pad;
     mp.out = ao;
@@ -522,7 +571,11 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     go.N = H;
     go.K = qw;
     go.P = P;
-    if ((e = run_gemm(go, st, &splits)) != hipSuccess) return DFLASH_ERR_HIP;
+    {
+      prof::Scope ps(DFLASH_PHASE_O, st);
+      e = run_gemm(go, st, &splits);
+    }
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
     dfl::RowNormParams rn;
     std::memset(&rn, 0, sizeof(rn));
     rn.x = x;
@@ -535,27 +588,24 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     rn.n = H;
     rn.out = u;
     if ((e = dfl::launch_row_norm(rn, st)) != hipSuccess) return DFLASH_ERR_HIP;
-    // gate and up in one pass, then SwiGLU
+    // gate and up in one pass with SwiGLU in the epilogue
     GemmCall gg;
     gg.A = u;
     gg.lda = H;
     gg.W0[0] = static_cast<const uint16_t*>(L.w_gate);
     gg.W1[0] = static_cast<const uint16_t*>(L.w_up);
-    gg.n_split = I;
     gg.ldw = H;
     gg.M = Mb;
-    gg.N = 2 * I;
+    gg.N = I;
     gg.K = H;
-    gg.P = P;
-    if ((e = run_gemm(gg, st, &splits)) != hipSuccess) return DFLASH_ERR_HIP;
-    dfl::SwigluParams sp;
-    sp.P = P;
-    sp.p_s_stride = (long long)Mb * 2 * I;
-    sp.splits = splits;
-    sp.rows = Mb;
-    sp.I = I;
-    sp.out = sb;
-    if ((e = dfl::launch_swiglu(sp, st)) != hipSuccess) return DFLASH_ERR_HIP;
+    gg.mode = dfl::kGemmSwiglu;
+    gg.out = sb;
+    gg.ld_out = I;
+    {
+      prof::Scope ps(DFLASH_PHASE_GATE_UP, st);
+      e = run_gemm(gg, st, nullptr);
+    }
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
     // down projection, residual, next norm (or the final norm)
     GemmCall gd;
     gd.A = sb;
@@ -566,7 +616,11 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     gd.N = H;
     gd.K = I;
     gd.P = P;
-    if ((e = run_gemm(gd, st, &splits)) != hipSuccess) return DFLASH_ERR_HIP;
+    {
+      prof::Scope ps(DFLASH_PHASE_DOWN, st);
+      e = run_gemm(gd, st, &splits);
+    }
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
     std::memset(&rn, 0, sizeof(rn));
     rn.x = x;
     rn.P = P;
@@ -598,10 +652,15 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
   gl.M = Ml;
   gl.N = c.vocab;
   gl.K = H;
+  gl.mode = dfl::kGemmArgmax;
   gl.keys = keys;
   gl.dbg = dbg_logits;
   gl.ld_dbg = c.vocab;
-  if ((e = run_gemm(gl, st, nullptr)) != hipSuccess) return DFLASH_ERR_HIP;
+  {
+    prof::Scope ps(DFLASH_PHASE_LM_HEAD, st);
+    e = run_gemm(gl, st, nullptr);
+  }
+  if (e != hipSuccess) return DFLASH_ERR_HIP;
   return hip_status(dfl::launch_unpack_draft(keys, kv->status, batch, B, draft, st));
 }
 
@@ -636,7 +695,41 @@ dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,
   p.done = done;
   p.commit_rows = commit_rows;
   p.n_commit = n_commit;
+  prof::Scope ps(DFLASH_PHASE_VERIFY, as_stream(stream));
   return hip_status(dfl::launch_verify(p, as_stream(stream)));
+}
+
+dflash_status dflash_pack_matrix(const void* src, void* dst, int32_t rows, int32_t cols, void* stream) {
+  if (!src || !dst) return DFLASH_ERR_NULL;
+  if (rows <= 0 || cols <= 0 || rows % 16 || cols % 32) return DFLASH_ERR_SHAPE;
+  if (src == dst) return DFLASH_ERR_SHAPE;
+  return hip_status(dfl::launch_pack(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), rows,
+                                     cols, as_stream(stream)));
+}
+
+dflash_status dflash_profile_enable(uint32_t phase_mask) {
+  prof::mask = phase_mask;
+  if (phase_mask) prof::used = 0;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_profile_read(int32_t phase, double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return DFLASH_ERR_NULL;
+  if (phase < 0 || phase >= DFLASH_N_PHASES) return DFLASH_ERR_SHAPE;
+  double t = 0.0;
+  int n = 0;
+  for (size_t i = 0; i < prof::used; ++i) {
+    const prof::Rec& r = prof::recs[i];
+    if (r.phase != phase) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return DFLASH_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return DFLASH_ERR_HIP;
+    t += ms;
+    ++n;
+  }
+  *total_ms = t;
+  *launches = n;
+  return DFLASH_OK;
 }
 
 }  // extern "C"

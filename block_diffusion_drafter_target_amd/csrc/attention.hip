@@ -7,8 +7,10 @@
 // is bound by streaming K/V from HBM; MFMA keeps the arithmetic far below that
 // bound.
 //
-// Decomposition: workgroup (4 waves) = (b, g, key chunk of p.chunk keys);
-// chunks past L_b + B exit at once. The chunk is walked in 64-key slices
+// Decomposition: workgroup (4 waves) = (b, g, key chunk). Each sequence's
+// L_b + B keys are split into at most n_chunks chunks of a multiple of 64 keys,
+// sized on the device from ctx_len, so the work follows the real context
+// rather than the cache capacity; chunks past the end exit at once. The chunk is walked in 64-key slices
 // staged through LDS (K row-major with a 16-byte XOR swizzle, V transposed),
 // the next slice's global loads issued before the current slice's math.
 // Wave w owns query tiles w, w+4, ... (16 query rows each).
@@ -28,6 +30,12 @@ namespace {
 
 constexpr int kSlice = 64;           // keys per LDS slice
 constexpr int kVtStride = kSlice + 4;  // bf16 per transposed V row (8-byte pad)
+
+// Keys per chunk of a sequence with Lk keys split n_chunks ways.
+__device__ __forceinline__ int chunk_len(int Lk, int n_chunks) {
+  const int c = (Lk + n_chunks - 1) / n_chunks;
+  return max(kSlice, (c + kSlice - 1) / kSlice * kSlice);
+}
 
 template <int D>
 struct Slice {
@@ -102,9 +110,10 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
   const int b = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
   if (p.status[b] != 0) return;
   const int Lk = p.ctx_len[b] + p.B;
-  const int k_start = c * p.chunk;
+  const int chunk = chunk_len(Lk, p.n_chunks);
+  const int k_start = c * chunk;
   if (k_start >= Lk) return;
-  const int k_end = min(Lk, k_start + p.chunk);
+  const int k_end = min(Lk, k_start + chunk);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, gq = lane >> 4;
@@ -230,7 +239,9 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
 }
 
 // o[m][h] = sum_c exp2(m_c - M) O_c / sum_c exp2(m_c - M) l_c over the chunks
-// that hold keys of the sequence. One wave per (row, head).
+// that hold keys of the sequence. One wave per (row, head); lane c holds
+// chunk c's statistics, and the D outputs accumulate over chunks with the
+// loads of eight chunks issued together.
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = blockIdx.y;
@@ -245,19 +256,31 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const int G = p.Hq / p.Hkv;
   const int g = h / G, rr = (h % G) * p.B + j;
   const int Lk = p.ctx_len[b] + p.B;
-  int nch = (Lk + p.chunk - 1) / p.chunk;
-  nch = nch < p.n_chunks ? nch : p.n_chunks;
+  const int nch = min(p.n_chunks, (Lk + chunk_len(Lk, p.n_chunks) - 1) / chunk_len(Lk, p.n_chunks));
   const long long base = ((long long)b * p.Hkv + g) * p.n_chunks;
-  float M = -__builtin_inff();
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, p.pm[(base + c) * p.gb_pad + rr]);
-  float l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const long long idx = (base + c) * p.gb_pad + rr;
-    const float w = exp2f(p.pm[idx] - M);
-    l += w * p.pl[idx];
-    const float* po = p.po + idx * p.D;
-    o0 += w * po[lane];
-    if (p.D > 64) o1 += w * po[lane + 64];
+  const float mc = lane < nch ? p.pm[(base + lane) * p.gb_pad + rr] : -__builtin_inff();
+  const float lc = lane < nch ? p.pl[(base + lane) * p.gb_pad + rr] : 0.f;
+  const float M = wave_max(mc);
+  const float w = lane < nch ? exp2f(mc - M) : 0.f;
+  const float l = wave_sum(w * lc);
+  float o0 = 0.f, o1 = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += 8) {
+    float a[8], bb[8], wc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int c = c0 + t;
+      wc[t] = __shfl(w, c < 64 ? c : 63);
+      const float* po = p.po + ((base + (c < nch ? c : 0)) * p.gb_pad + rr) * p.D;
+      a[t] = c < nch ? po[lane] : 0.f;
+      bb[t] = (c < nch && p.D > 64) ? po[lane + 64] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (c0 + t < nch) {
+        o0 += wc[t] * a[t];
+        o1 += wc[t] * bb[t];
+      }
+    }
   }
   const float inv = 1.0f / l;
   out[lane] = f2bf(o0 * inv);
@@ -282,12 +305,14 @@ hipError_t launch_d(const AttnParams& p, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, int D, hipStream_t st) {
+  if (p.n_chunks < 1 || p.n_chunks > 64) return hipErrorInvalidValue;
   if (D == 128) return launch_d<128>(p, st);
   if (D == 64) return launch_d<64>(p, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t st) {
+  if (p.n_chunks < 1 || p.n_chunks > 64) return hipErrorInvalidValue;
   hipLaunchKernelGGL(merge_kernel, dim3((p.Hq + 3) / 4, p.batch * p.B), dim3(256), 0, st, p);
   return hipGetLastError();
 }

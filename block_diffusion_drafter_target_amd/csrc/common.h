@@ -45,6 +45,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
 // Sum over a 256-thread workgroup; every thread gets the result.
 __device__ __forceinline__ float block_sum_256(float v, float* smem4) {
   v = wave_sum(v);

@@ -3,20 +3,24 @@
 // Y[m][n] = sum_k A[m][k] * W[n][k]. With M <= 64 the product is bound by
 // reading W once from HBM (2 flop per weight byte per row of A), so the kernel
 // is built around the weight stream:
+//   * W is in the packed fragment layout (pack.hip): every 16-row x 32-k MFMA
+//     operand is one contiguous 1 KB block, lane l's 16 bytes at offset 16*l,
+//     and a 16-row group's blocks follow each other along k. One wave load of
+//     an operand is one fully used 1 KB line, and a wave walking k reads
+//     contiguous memory;
 //   * a workgroup (4 waves) owns 16*NF weight rows and all 16*MT rows of A;
-//   * each wave takes every fourth 128-wide k block of the split's k range
-//     and loads its W rows straight into MFMA operand registers with 16-byte
-//     loads (64 contiguous bytes per row per instruction), one block ahead of
-//     the MFMAs (register double buffering);
-//   * A is tiny and re-read from L1/L2 by the four waves;
-//   * the four waves' partial tiles are summed through LDS;
-//   * the grid's y dimension splits K (fp32 partials P[z][s][m][n], summed by
-//     the consumer kernel), z batches independent weight matrices;
+//     wave w takes every fourth 128-wide k block of the split's k range;
+//     the four partial tiles are summed through LDS;
+//   * A (activations, row-major) is tiny and re-read from L1/L2;
+//   * grid y splits K (fp32 partials P[z][s][m][n], summed by the consumer),
+//     grid z batches independent weight matrices;
 //   * argmax mode (one split) reduces each row's logits to a packed
-//     (value, index) key and merges it with a 64-bit atomic max, so logits are
-//     never written unless a debug buffer is given.
-// MFMA: W rows are the A operand (16 rows x 32 k), activations the B operand,
-// so a lane's four results are four consecutive n of one row m.
+//     (value, index) key merged with a 64-bit atomic max: logits are never
+//     written unless a debug buffer is given;
+//   * swiglu mode (one split) pairs gate rows (W0) and up rows (W1) of the same
+//     output columns inside the workgroup and writes bf16 silu(g) * u.
+// MFMA: W rows are the A operand, activations the B operand, so a lane's four
+// results are four consecutive n of one row m.
 #include "common.h"
 #include "internal.h"
 
@@ -36,17 +40,27 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
   const int g = lane >> 4;
   const int z = blockIdx.z;
   const int s = blockIdx.y;
-  const int n0 = blockIdx.x * 16 * NF;
+  constexpr int kOutFrags = MODE == kGemmSwiglu ? NF / 2 : NF;  // output fragments
+  const int n0 = blockIdx.x * 16 * kOutFrags;
   const int kbeg = s * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
+  const long long frag_row = (long long)(p.K / 32) * 512;  // elements per 16-row group
 
   const bf16_t* wrow[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const int n = min(n0 + 16 * f + r, p.N - 1);
-    const bf16_t* base = (n < p.n_split) ? p.W0[z] + (long long)n * p.ldw
-                                         : p.W1[z] + (long long)(n - p.n_split) * p.ldw;
-    wrow[f] = base + g * 8;
+    const bf16_t* base;
+    int grp;
+    if (MODE == kGemmSwiglu) {
+      const int fo = f < NF / 2 ? f : f - NF / 2;
+      grp = min(n0 + 16 * fo, p.N - 16) >> 4;
+      base = f < NF / 2 ? p.W0[z] : p.W1[z];
+    } else {
+      const int n = min(n0 + 16 * f, p.N - 16);
+      base = n < p.n_split ? p.W0[z] : p.W1[z];
+      grp = (n < p.n_split ? n : n - p.n_split) >> 4;
+    }
+    wrow[f] = base + grp * frag_row + lane * 8;
   }
   const bf16_t* arow[MT];
 #pragma unroll
@@ -68,30 +82,32 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 
   u32x4 wa[NF][4], xa[MT][4], wb[NF][4], xb[MT][4];
 
+  // Loads are unconditional (clamped to the row's last k chunk) so the
+  // compiler can overlap them with the MFMAs; k chunks past the split's end
+  // are zeroed on the activation side with a uniform mask.
+  const int klast = p.K - 32;
   auto load = [&](u32x4(&w)[NF][4], u32x4(&x)[MT][4], int k) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int kk = k + 32 * u;
-      if (kk < kend) {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) w[f][u] = *reinterpret_cast<const u32x4*>(wrow[f] + kk);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) x[t][u] = *reinterpret_cast<const u32x4*>(arow[t] + kk);
-      } else {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) w[f][u] = u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int t = 0; t < MT; ++t) x[t][u] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto compute = [&](const u32x4(&w)[NF][4], const u32x4(&x)[MT][4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
+      const int kk = min(k + 32 * u, klast);
 #pragma unroll
       for (int f = 0; f < NF; ++f)
+        w[f][u] = *reinterpret_cast<const u32x4*>(wrow[f] + (long long)(kk >> 5) * 512);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[f][t] = mfma16x16x32(w[f][u], x[t][u], acc[f][t]);
+      for (int t = 0; t < MT; ++t) x[t][u] = *reinterpret_cast<const u32x4*>(arow[t] + kk);
+    }
+  };
+  auto compute = [&](const u32x4(&w)[NF][4], const u32x4(&x)[MT][4], int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t keep = (k + 32 * u < kend) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const u32x4 xv = x[t][u] & keep;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[f][t] = mfma16x16x32(w[f][u], xv, acc[f][t]);
+      }
+    }
   };
 
   // k blocks of this wave: kbeg + (wave + 4*i) * 128 while < kend
@@ -100,13 +116,15 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
     load(wa, xa, k);
     while (true) {
       const int k1 = k + 4 * kKB;
-      if (k1 < kend) load(wb, xb, k1);
-      compute(wa, xa);
-      if (k1 >= kend) break;
+      const bool more1 = k1 < kend;
+      load(wb, xb, more1 ? k1 : k);  // past the end: re-read a valid block, unused
+      compute(wa, xa, k);
+      if (!more1) break;
       const int k2 = k1 + 4 * kKB;
-      if (k2 < kend) load(wa, xa, k2);
-      compute(wb, xb);
-      if (k2 >= kend) break;
+      const bool more2 = k2 < kend;
+      load(wa, xa, more2 ? k2 : k1);
+      compute(wb, xb, k1);
+      if (!more2) break;
       k = k2;
     }
   }
@@ -117,8 +135,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
     for (int t = 0; t < MT; ++t) red[wave][f * MT + t][lane] = acc[f][t];
   __syncthreads();
 
-  // each wave finishes the fragments idx = wave, wave + 4, ...
-  for (int idx = wave; idx < NF * MT; idx += 4) {
+  // each wave finishes the output fragments idx = wave, wave + 4, ...
+  for (int idx = wave; idx < kOutFrags * MT; idx += 4) {
     const int f = idx / MT, t = idx % MT;
     f32x4_t v = red[0][idx][lane];
 #pragma unroll
@@ -130,6 +148,18 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
         float* dst = p.P + (long long)z * p.p_z_stride + (long long)s * p.p_s_stride +
                      (long long)m * p.N + nb;
         *reinterpret_cast<f32x4_t*>(dst) = v;
+      }
+    } else if (MODE == kGemmSwiglu) {
+      const int iu = (f + NF / 2) * MT + t;
+      f32x4_t up = red[0][iu][lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) up += red[w][iu][lane];
+      if (m < p.M && nb < p.N) {
+        float sv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[i] = v[i] / (1.0f + __expf(-v[i])) * up[i];
+        const u32x2 o = u32x2{pack_bf2(sv[0], sv[1]), pack_bf2(sv[2], sv[3])};
+        *reinterpret_cast<u32x2*>(p.out + (long long)m * p.ld_out + nb) = o;
       }
     } else {
       if (p.dbg != nullptr && m < p.M && nb < p.N)
@@ -159,9 +189,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const GemmParams p) {
 
 template <int MT, int NF>
 hipError_t launch_mt_nf(const GemmParams& p, int mode, int nz, hipStream_t st) {
-  dim3 grid((p.N + 16 * NF - 1) / (16 * NF), p.splits, nz);
+  const int out_frags = mode == kGemmSwiglu ? NF / 2 : NF;
+  dim3 grid((p.N + 16 * out_frags - 1) / (16 * out_frags), p.splits, nz);
   if (mode == kGemmArgmax)
     hipLaunchKernelGGL((gemm_stream_kernel<MT, NF, kGemmArgmax>), grid, dim3(256), 0, st, p);
+  else if (mode == kGemmSwiglu)
+    hipLaunchKernelGGL((gemm_stream_kernel<MT, NF, kGemmSwiglu>), grid, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((gemm_stream_kernel<MT, NF, kGemmPartial>), grid, dim3(256), 0, st, p);
   return hipGetLastError();

@@ -11,8 +11,10 @@ namespace dfl {
 constexpr int kMaxZ = 16;       // weight matrices batched in one GEMM launch
 constexpr int kMaxLayers = 16;  // draft layers supported
 
-// Y = A * W^T, bf16 in, fp32 accumulate. Rows n < n_split of the logical W
-// come from W0[z] (row n), rows n >= n_split from W1[z] (row n - n_split).
+// Y = A * W^T, bf16 in, fp32 accumulate. W matrices are in the packed
+// fragment layout (pack.hip). Rows n < n_split of the logical W come from
+// W0[z] (row n), rows n >= n_split from W1[z] (row n - n_split); in swiglu
+// mode W0 holds the gate rows and W1 the up rows of the N output columns.
 struct GemmParams {
   const uint16_t* A;  // [M, K] activations, row stride lda
   long long lda;
@@ -34,9 +36,16 @@ struct GemmParams {
   unsigned long long* keys;
   float* dbg;  // optional logits [M, ld_dbg]
   long long ld_dbg;
+  // swiglu output (splits == 1): out[m][n] = bf16(silu(gate) * up)
+  uint16_t* out;
+  long long ld_out;
 };
 
-enum GemmMode { kGemmPartial = 0, kGemmArgmax = 1 };
+enum GemmMode { kGemmPartial = 0, kGemmArgmax = 1, kGemmSwiglu = 2 };
+
+// Packs a row-major bf16 matrix [rows, cols] (rows % 16 == 0, cols % 32 == 0)
+// into the fragment layout used by the weight-streaming GEMM.
+hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int rows, int cols, hipStream_t st);
 
 hipError_t launch_gemm_stream(const GemmParams& p, int mt, int nf, int mode, int nz,
                               hipStream_t st);
@@ -48,9 +57,9 @@ struct AttnParams {
   const int32_t* ctx_len;
   const int32_t* status;
   int batch, Hq, Hkv, B, max_ctx;
-  int chunk;   // keys per workgroup (multiple of 64)
-  int n_chunks;
-  int gb_pad;  // query rows per (b, g), padded to 16
+  int n_chunks;  // key chunks per (b, g) (grid x, <= 64); chunk length per sequence
+                 // = max(64, L_b + B split n_chunks ways, rounded up to 64)
+  int gb_pad;    // query rows per (b, g), padded to 16
   float scale_log2;
   float* pm;   // [batch][Hkv][n_chunks][gb_pad]
   float* pl;
@@ -65,7 +74,7 @@ struct MergeParams {
   const float* po;
   const int32_t* ctx_len;
   const int32_t* status;
-  int batch, Hq, Hkv, B, D, chunk, n_chunks, gb_pad;
+  int batch, Hq, Hkv, B, D, n_chunks, gb_pad;
   uint16_t* out;  // [batch*B, Hq*D]
 };
 
@@ -124,15 +133,6 @@ struct QkvPostParams {
 };
 
 hipError_t launch_qkv_post(const QkvPostParams& p, hipStream_t st);
-
-struct SwigluParams {
-  const float* P;  // [splits][rows][2I]: gate at n < I, up at n >= I
-  long long p_s_stride;
-  int splits, rows, I;
-  uint16_t* out;   // [rows, I]
-};
-
-hipError_t launch_swiglu(const SwigluParams& p, hipStream_t st);
 
 struct InjectPostParams {
   const float* P;  // [layer][split][c1 - c0][2*Hkv*D], row = commit index - c0

@@ -1,6 +1,6 @@
 // Row-wise kernels of the draft step (gfx950): embedding + RMSNorm, split-K
 // reduction + residual + RMSNorm, per-head q/k RMSNorm + RoPE + KV-cache
-// append, SwiGLU, the inject epilogue (k-norm + RoPE + cache scatter + commit
+// append, the inject epilogue (k-norm + RoPE + cache scatter + commit
 // of ctx_len), and the unpacking of argmax keys into draft tokens.
 //
 // All are bound by a few kilobytes per row; they exist to keep every fp32
@@ -16,12 +16,50 @@ namespace {
 constexpr int kErrCapacity = -5;  // DFLASH_ERR_CAPACITY
 constexpr int kErrShape = -2;     // DFLASH_ERR_SHAPE
 
+constexpr int kRowThreads = 512;
+constexpr int kMaxC4 = 4;     // float4 columns per thread: rows of up to 8192
+constexpr int kSplitBatch = 8;  // split partials loaded together
+
+__device__ __forceinline__ float block_sum_512(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kRowThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+// Adds the split partials of row m, columns 4*i4.., to v. All loads of a
+// batch of splits are issued before any add, so the row costs one memory
+// round trip per kSplitBatch splits.
+__device__ __forceinline__ void add_splits(f32x4_t (&v)[kMaxC4], const float* P, long long s_stride,
+                                           int splits, long long row_off, int n4) {
+  for (int s0 = 0; s0 < splits; s0 += kSplitBatch) {
+    f32x4_t t[kMaxC4][kSplitBatch];
+#pragma unroll
+    for (int c = 0; c < kMaxC4; ++c) {
+      const int i4 = threadIdx.x + c * kRowThreads;
+#pragma unroll
+      for (int j = 0; j < kSplitBatch; ++j)
+        t[c][j] = (i4 < n4 && s0 + j < splits)
+                      ? *reinterpret_cast<const f32x4_t*>(P + (long long)(s0 + j) * s_stride + row_off + 4 * i4)
+                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxC4; ++c)
+#pragma unroll
+      for (int j = 0; j < kSplitBatch; ++j) v[c] += t[c][j];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // block row embedding: x = E[token], u = bf16(RMSNorm(x) * g_in of layer 0)
 // Row j of sequence b holds the anchor (j = 0) or the mask id. The j == 0
 // workgroup also records the sequence's capacity status.
-__global__ __launch_bounds__(256) void embed_kernel(const EmbedParams p) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(kRowThreads) void embed_kernel(const EmbedParams p) {
+  __shared__ float red[kRowThreads / 64];
   const int m = blockIdx.x;
   const int b = m / p.B, j = m % p.B;
   const int L = p.ctx_len[b];
@@ -31,56 +69,66 @@ __global__ __launch_bounds__(256) void embed_kernel(const EmbedParams p) {
   if (j == 0 && threadIdx.x == 0) p.status[b] = cap_bad ? kErrCapacity : (tok_bad ? kErrShape : 0);
   if (tok_bad) tok = 0;
   const bf16_t* e = p.embed + (long long)tok * p.H;
-  float* x = p.x + (long long)m * p.H;
+  const int n4 = p.H / 4;
+  f32x4_t v[kMaxC4];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < p.H; i += 256) {
-    const float v = bf2f(e[i]);
-    x[i] = v;
-    if (p.dbg) p.dbg[(long long)m * p.H + i] = v;
-    ss += v * v;
+#pragma unroll
+  for (int c = 0; c < kMaxC4; ++c) {
+    const int i4 = threadIdx.x + c * kRowThreads;
+    v[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (i4 < n4) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(e + 4 * i4);
+      v[c] = f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+      *reinterpret_cast<f32x4_t*>(p.x + (long long)m * p.H + 4 * i4) = v[c];
+      if (p.dbg) *reinterpret_cast<f32x4_t*>(p.dbg + (long long)m * p.H + 4 * i4) = v[c];
+    }
+    ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
   }
-  ss = block_sum_256(ss, red);
+  ss = block_sum_512(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)p.H + p.eps);
-  bf16_t* u = p.u + (long long)m * p.H;
-  for (int i = threadIdx.x; i < p.H; i += 256) u[i] = f2bf(x[i] * inv * bf2f(p.gain[i]));
+#pragma unroll
+  for (int c = 0; c < kMaxC4; ++c) {
+    const int i4 = threadIdx.x + c * kRowThreads;
+    if (i4 < n4) {
+      const u32x2 gw = *reinterpret_cast<const u32x2*>(p.gain + 4 * i4);
+      const u32x2 o = u32x2{pack_bf2(v[c][0] * inv * __uint_as_float(gw.x << 16),
+                                     v[c][1] * inv * __uint_as_float(gw.x & 0xFFFF0000u)),
+                            pack_bf2(v[c][2] * inv * __uint_as_float(gw.y << 16),
+                                     v[c][3] * inv * __uint_as_float(gw.y & 0xFFFF0000u))};
+      *reinterpret_cast<u32x2*>(p.u + (long long)m * p.H + 4 * i4) = o;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // y = (x +=) sum of split partials; out = bf16(RMSNorm(y) * gain)
-__global__ __launch_bounds__(256) void row_norm_kernel(const RowNormParams p) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(kRowThreads) void row_norm_kernel(const RowNormParams p) {
+  __shared__ float red[kRowThreads / 64];
   const int m = blockIdx.x;
-  const int n = p.n;
-  constexpr int kPer = 16;  // the first 16*256 columns stay in registers
-  auto load = [&](int i) {
-    float v = 0.f;
-    if (p.P) {
-      const float* src = p.P + (long long)m * n + i;
-      for (int s = 0; s < p.splits; ++s) v += src[(long long)s * p.p_s_stride];
-    }
-    if (p.x) {
-      float* xp = p.x + (long long)m * n + i;
-      v += *xp;
-      *xp = v;
-    }
-    if (p.dbg) p.dbg[(long long)m * n + i] = v;
-    return v;
-  };
-  float vals[kPer];
+  const int n = p.n, n4 = n / 4;
+  const long long row_off = (long long)m * n;
+  f32x4_t v[kMaxC4];
+#pragma unroll
+  for (int c = 0; c < kMaxC4; ++c) {
+    const int i4 = threadIdx.x + c * kRowThreads;
+    v[c] = (p.x && i4 < n4) ? *reinterpret_cast<const f32x4_t*>(p.x + row_off + 4 * i4)
+                            : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  if (p.P) add_splits(v, p.P, p.p_s_stride, p.splits, row_off, n4);
   float ss = 0.f;
 #pragma unroll
-  for (int c = 0; c < kPer; ++c) {
-    const int i = threadIdx.x + c * 256;
-    vals[c] = i < n ? load(i) : 0.f;
-    ss += vals[c] * vals[c];
+  for (int c = 0; c < kMaxC4; ++c) {
+    const int i4 = threadIdx.x + c * kRowThreads;
+    if (i4 < n4) {
+      if (p.x) *reinterpret_cast<f32x4_t*>(p.x + row_off + 4 * i4) = v[c];
+      if (p.dbg) *reinterpret_cast<f32x4_t*>(p.dbg + row_off + 4 * i4) = v[c];
+    }
+    ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
   }
-  for (int i = threadIdx.x + kPer * 256; i < n; i += 256) {
-    const float v = load(i);
-    ss += v * v;
-  }
-  ss = block_sum_256(ss, red);
+  ss = block_sum_512(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)n + p.eps);
-  bf16_t* out = nullptr;
+  bf16_t* out;
   if (p.final_mode) {
     const int b = m / p.B, j = m % p.B;
     if (j == 0) return;
@@ -88,23 +136,40 @@ __global__ __launch_bounds__(256) void row_norm_kernel(const RowNormParams p) {
     out = p.out + (long long)row * n;
     if (threadIdx.x == 0) p.keys[row] = 0ull;
   } else {
-    out = p.out + (long long)m * n;
+    out = p.out + row_off;
   }
 #pragma unroll
-  for (int c = 0; c < kPer; ++c) {
-    const int i = threadIdx.x + c * 256;
-    if (i < n) out[i] = f2bf(vals[c] * inv * bf2f(p.gain[i]));
-  }
-  for (int i = threadIdx.x + kPer * 256; i < n; i += 256) {
-    float v;
-    if (p.x) {
-      v = p.x[(long long)m * n + i];
-    } else {
-      v = 0.f;
-      const float* src = p.P + (long long)m * n + i;
-      for (int s = 0; s < p.splits; ++s) v += src[(long long)s * p.p_s_stride];
+  for (int c = 0; c < kMaxC4; ++c) {
+    const int i4 = threadIdx.x + c * kRowThreads;
+    if (i4 < n4) {
+      const u32x2 gw = *reinterpret_cast<const u32x2*>(p.gain + 4 * i4);
+      const u32x2 o = u32x2{pack_bf2(v[c][0] * inv * __uint_as_float(gw.x << 16),
+                                     v[c][1] * inv * __uint_as_float(gw.x & 0xFFFF0000u)),
+                            pack_bf2(v[c][2] * inv * __uint_as_float(gw.y << 16),
+                                     v[c][3] * inv * __uint_as_float(gw.y & 0xFFFF0000u))};
+      *reinterpret_cast<u32x2*>(out + 4 * i4) = o;
     }
-    out[i] = f2bf(v * inv * bf2f(p.gain[i]));
+  }
+}
+
+// Sum over splits of two values per lane (pair i, i + D/2 of one head).
+__device__ __forceinline__ void sum_pair(const float* src, long long s_stride, int splits, int half,
+                                         bool active, float& x1, float& x2) {
+  x1 = 0.f;
+  x2 = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += kSplitBatch) {
+    float a[kSplitBatch], c[kSplitBatch];
+#pragma unroll
+    for (int j = 0; j < kSplitBatch; ++j) {
+      const bool ok = active && s0 + j < splits;
+      a[j] = ok ? src[(long long)(s0 + j) * s_stride] : 0.f;
+      c[j] = ok ? src[(long long)(s0 + j) * s_stride + half] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kSplitBatch; ++j) {
+      x1 += a[j];
+      x2 += c[j];
+    }
   }
 }
 
@@ -125,14 +190,9 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
   const int D = p.D, half = D >> 1;
   const int width = nh * D;
   const bool active = lane < half;
-  float x1 = 0.f, x2 = 0.f;
-  if (active) {
-    const float* src = p.P + (long long)m * width + head * D + lane;
-    for (int s = 0; s < p.splits; ++s) {
-      x1 += src[(long long)s * p.p_s_stride];
-      x2 += src[(long long)s * p.p_s_stride + half];
-    }
-  }
+  float x1, x2;
+  sum_pair(p.P + (long long)m * width + head * D + (active ? lane : 0), p.p_s_stride, p.splits, half,
+           active, x1, x2);
   if (head >= p.Hq + p.Hkv) {  // v
     if (active) {
       const int g = head - p.Hq - p.Hkv;
@@ -163,23 +223,6 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// s = silu(gate) * up from split partials; silu(z) = z / (1 + e^-z)
-__global__ __launch_bounds__(256) void swiglu_kernel(const SwigluParams p) {
-  const long long total = (long long)p.rows * p.I;
-  for (long long e = blockIdx.x * 256ll + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
-    const int m = (int)(e / p.I), i = (int)(e % p.I);
-    const float* src = p.P + (long long)m * 2 * p.I + i;
-    float gsum = 0.f, usum = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
-      gsum += src[(long long)s * p.p_s_stride];
-      usum += src[(long long)s * p.p_s_stride + p.I];
-    }
-    const float silu = gsum / (1.0f + __expf(-gsum));
-    p.out[e] = f2bf(silu * usum);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // KV injection epilogue: for commit row i and layer l, k = RoPE(RMSNorm_head(
 // W_k c)), v = W_v c, scattered to (seq, pos); ctx_len[seq] grows to pos + 1.
 __global__ __launch_bounds__(256) void inject_post_kernel(const InjectPostParams p) {
@@ -198,14 +241,9 @@ __global__ __launch_bounds__(256) void inject_post_kernel(const InjectPostParams
   const int width = 2 * p.Hkv * D;
   const bool active = lane < half;
   for (int head = wave; head < 2 * p.Hkv; head += 4) {
-    float x1 = 0.f, x2 = 0.f;
-    if (active) {
-      const float* s0 = p.P + (long long)l * p.p_z_stride + (long long)(i - p.c0) * width + head * D + lane;
-      for (int s = 0; s < p.splits; ++s) {
-        x1 += s0[(long long)s * p.p_s_stride];
-        x2 += s0[(long long)s * p.p_s_stride + half];
-      }
-    }
+    float x1, x2;
+    sum_pair(p.P + (long long)l * p.p_z_stride + (long long)(i - p.c0) * width + head * D + (active ? lane : 0),
+             p.p_s_stride, p.splits, half, active, x1, x2);
     const int g = head < p.Hkv ? head : head - p.Hkv;
     const long long off = ((((long long)l * p.batch + seq) * p.Hkv + g) * p.max_ctx + pos) * D;
     if (head >= p.Hkv) {
@@ -241,26 +279,20 @@ __global__ __launch_bounds__(256) void unpack_draft_kernel(const unsigned long l
 }  // namespace
 
 hipError_t launch_embed(const EmbedParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(embed_kernel, dim3(p.batch * p.B), dim3(256), 0, st, p);
+  if (p.H > kRowThreads * 4 * kMaxC4 || p.H % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(embed_kernel, dim3(p.batch * p.B), dim3(kRowThreads), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_row_norm(const RowNormParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(row_norm_kernel, dim3(p.rows), dim3(256), 0, st, p);
+  if (p.n > kRowThreads * 4 * kMaxC4 || p.n % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(row_norm_kernel, dim3(p.rows), dim3(kRowThreads), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_qkv_post(const QkvPostParams& p, hipStream_t st) {
   const int nh = p.Hq + 2 * p.Hkv;
   hipLaunchKernelGGL(qkv_post_kernel, dim3((nh + 3) / 4, p.batch * p.B), dim3(256), 0, st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu(const SwigluParams& p, hipStream_t st) {
-  const long long total = (long long)p.rows * p.I;
-  long long blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

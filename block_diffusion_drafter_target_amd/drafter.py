@@ -25,6 +25,22 @@ def _torch():
     return torch
 
 
+# matrices the weight-streaming GEMM reads, stored in the packed fragment layout
+PACKED = ("lm_head", "w_fc", "w_qkv", "w_o", "w_gate", "w_up", "w_down")
+
+
+def is_packed(name: str) -> bool:
+    return name.split(".")[-1] in PACKED
+
+
+def pack_matrix(t, stream=None):
+    """Device bf16 row-major [rows, cols] -> new tensor in the packed layout."""
+    out = _torch().empty_like(t)
+    bd.dflash_pack_matrix(t.data_ptr(), out.data_ptr(), t.shape[0], t.shape[1],
+                          _torch().cuda.current_stream().cuda_stream if stream is None else stream)
+    return out
+
+
 def to_device_bf16(a: np.ndarray, device):
     """bf16 bits (uint16) or fp32 on the bf16 grid -> torch bf16 tensor on device."""
     torch = _torch()
@@ -49,11 +65,13 @@ class Drafter:
         B = cfg.block
         self.max_rows = max_rows if max_rows is not None else batch * B
         self.rope_max = rope_max or max_ctx
-        # weights (device bf16); torch tensors are kept so the pointers stay valid
+        # weights (device bf16, GEMM matrices packed); the tensors are kept so the
+        # pointers stay valid
         self.w = {}
         for name, arr in weights.items():
             t = arr if hasattr(arr, "data_ptr") else to_device_bf16(np.asarray(arr), self.device)
-            self.w[name] = t
+            self.w[name] = pack_matrix(t) if is_packed(name) else t
+            del t
         rope = np.empty(self.rope_max * (cfg.head_dim // 2) * 2, np.float32)
         bd.dflash_rope_table(rope.ctypes.data_as(C.c_void_p), self.rope_max, cfg.head_dim, cfg.rope_theta)
         self.rope = torch.from_numpy(rope).to(self.device)

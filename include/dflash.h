@@ -67,7 +67,8 @@ typedef struct dflash_config {
   float rms_eps;
 } dflash_config;
 
-/* One draft layer; all device bf16.
+/* One draft layer; all device bf16. Matrices are [out, in] in the packed
+ * fragment layout written by dflash_pack_matrix; gains are plain vectors.
  *   g_in [H], g_post [H], g_q [D], g_k [D]     RMSNorm gains
  *   w_qkv [(Hq+2Hkv)*D, H]  rows: q heads, then k heads, then v heads
  *   w_o   [H, Hq*D]
@@ -86,8 +87,9 @@ typedef struct dflash_layer_weights {
 } dflash_layer_weights;
 
 /* Whole drafter; device pointers unless noted.
- *   embed, lm_head [V, H] bf16 (the target's, shared)
- *   w_fc [H, n_tap*H] bf16, columns tap-major; g_fc [H], g_final [H] bf16
+ *   embed [V, H] bf16 row-major; lm_head [V, H] bf16 packed (the target's
+ *         embedding and head, shared)
+ *   w_fc [H, n_tap*H] bf16 packed, columns tap-major; g_fc [H], g_final [H]
  *   layers: HOST array of n_layers entries (copied at create)
  *   rope: device fp32 [rope_max_pos, D/2, 2] = (cos, sin) of pos*theta^(-2i/D),
  *         as written by dflash_rope_table. */
@@ -128,6 +130,17 @@ void dflash_model_destroy(dflash_model* m);
 /* Host helper: cos/sin table for RoPE, computed in double and rounded to
  * float. out: host float[max_pos * head_dim/2 * 2]. */
 dflash_status dflash_rope_table(float* out, int32_t max_pos, int32_t head_dim, float theta);
+
+/* Packed fragment layout of a weight matrix. src: device bf16 row-major
+ * [rows, cols]; dst: device bf16, same size, not overlapping src. rows must be
+ * a multiple of 16 and cols of 32. The 16-row x 32-column block (rg, kc) of W
+ * is stored contiguously (1 KB) at block index rg*(cols/32) + kc, element
+ *   dst[((rg*(cols/32) + kc)*64 + 16*g + r)*8 + e] = W[16*rg + r][32*kc + 8*g + e]
+ * for r < 16, g < 4, e < 8: the operand order of the 16x16x32 bf16 MFMA, so a
+ * wavefront reads one block with one fully used 1 KB load. Enqueued on
+ * stream. */
+dflash_status dflash_pack_matrix(const void* src, void* dst, int32_t rows, int32_t cols,
+                                 void* stream);
 
 /* Workspace (device scratch, caller-allocated) needed by calls that handle up
  * to max_batch sequences, a cache of max_ctx slots and up to max_rows context
@@ -203,6 +216,30 @@ dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,
                                    int32_t* accept_len, int32_t* anchor_out, int32_t* emitted,
                                    int32_t* n_emit, int32_t* done, int32_t* commit_rows,
                                    int32_t* n_commit, void* stream);
+
+/* Kernel timing for benchmarks. dflash_profile_enable(mask) times the phases
+ * whose bit (1 << phase) is set in mask (0 switches timing off): every launch
+ * of such a phase is bracketed by two HIP events recorded on the call's
+ * stream (hipEventCreate objects owned by the library; no device memory).
+ * Process-wide, off by default, not thread-safe; enabling clears earlier
+ * records.
+ * dflash_profile_read waits for the recorded events and returns the summed
+ * duration (ms) and the number of launches of one phase. */
+typedef enum dflash_phase {
+  DFLASH_PHASE_LM_HEAD = 0,   /* LM-head GEMM with fused argmax (S10) */
+  DFLASH_PHASE_ATTENTION = 1, /* block attention kernel (S6, without the merge) */
+  DFLASH_PHASE_QKV = 2,       /* q/k/v projection GEMM (S4) */
+  DFLASH_PHASE_O = 3,         /* o projection GEMM (S7) */
+  DFLASH_PHASE_GATE_UP = 4,   /* gate/up GEMM (S8) */
+  DFLASH_PHASE_DOWN = 5,      /* down projection GEMM (S9) */
+  DFLASH_PHASE_FUSE = 6,      /* fusion GEMM (S1) */
+  DFLASH_PHASE_INJECT = 7,    /* injection GEMM (S2) */
+  DFLASH_PHASE_VERIFY = 8,    /* verify kernel (S11) */
+  DFLASH_N_PHASES = 9
+} dflash_phase;
+
+dflash_status dflash_profile_enable(uint32_t phase_mask);
+dflash_status dflash_profile_read(int32_t phase, double* total_ms, int32_t* launches);
 
 const char* dflash_status_string(dflash_status s);
 

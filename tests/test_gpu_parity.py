@@ -48,6 +48,20 @@ def gpu_cache(dr, l, b, L):
     return k, v
 
 
+def test_pack_matrix_layout(gpu_lib):
+    """The packed fragment layout, element by element (bit exact)."""
+    torch = _torch()
+    from block_diffusion_drafter_target_amd.drafter import pack_matrix
+    gh.log("[pack] 48 x 96 and 160 x 4096")
+    for rows, cols in ((48, 96), (160, 4096)):
+        w = np.random.default_rng(rows).integers(0, 1 << 16, size=(rows, cols), dtype=np.uint16)
+        t = torch.from_numpy(w.view(np.int16)).cuda()
+        got = pack_matrix(t.view(torch.bfloat16)).view(torch.int16).cpu().numpy().view(np.uint16)
+        # [rg][kc][g][r][e] = W[16 rg + r][32 kc + 8 g + e]
+        want = w.reshape(rows // 16, 16, cols // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(rows, cols)
+        assert np.array_equal(got.reshape(rows, cols), want)
+
+
 @pytest.mark.parametrize("shape", sorted(gh.SHAPES))
 def test_fuse_ctx_parity(gpu_lib, shape):
     torch = _torch()
