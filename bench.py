@@ -89,6 +89,10 @@ def main():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the same steps captured in one HIP graph")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it",
@@ -160,6 +164,7 @@ def main():
         step(targets[1 + i])
     torch.cuda.synchronize()
     assert int(dr.status.abs().max()) == 0, "a sequence ran out of cache"
+    after_warmup = {k: getattr(dr, k).clone() for k in ("ctx_len", "anchor_out", "commit_rows", "n_commit")}
     bd.dflash_profile_enable(["lm_head"])
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -176,6 +181,29 @@ def main():
     # the replay accepted exactly the recorded prefix lengths
     assert dr.accept_len.cpu().numpy().tolist() == m_all[args.warmup + args.steps].cpu().numpy().tolist()
 
+    graph_ms = None
+    if args.graph:
+        # the same timed steps, launched as one captured graph from the same state
+        end_state = {k: getattr(dr, k).clone() for k in ("ctx_len", "anchor_out", "commit_rows", "n_commit")}
+        for k, v in after_warmup.items():
+            getattr(dr, k).copy_(v)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(targets[1 + args.warmup + i])
+        for k, v in after_warmup.items():
+            getattr(dr, k).copy_(v)
+        torch.cuda.synchronize()
+        start.record()
+        graph.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        graph_ms = start.elapsed_time(stop) / args.steps
+        for k, v in end_state.items():
+            assert torch.equal(getattr(dr, k), v), f"graph replay diverged from the eager steps ({k})"
+        del graph
+
     bd.dflash_profile_enable(list(bd.PHASES))
     for i in range(n_break):
         step(targets[1 + args.warmup + args.steps + i])
@@ -188,12 +216,22 @@ def main():
                             "us_per_launch": round(1e3 * t / n, 2)}
     bd.dflash_profile_enable([])
 
+    if args.calib_copy_mb:
+        # a plain copy of known size: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of
+        # this kernel calibrate the counters against bytes actually moved
+        src = torch.ones(args.calib_copy_mb << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # roofline of the dominant kernel: the LM head streams V*H bf16 weights
     Ml = batch * (B - 1)
     lm_bytes = V * H * 2 + Ml * H * 2 + Ml * 8
     lm_us = 1e3 * lm_ms / max(1, lm_n)
     achieved = lm_bytes / (lm_us * 1e-6) / 1e9
-    roofline = {"kernel": "gemm_stream_kernel<1,4,argmax> (LM head + fused argmax)", "bound": "hbm",
+    roofline = {"kernel": "gemm_stream_kernel<1,2,argmax> (LM head + fused argmax)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "bytes_per_launch": lm_bytes, "us_per_launch": round(lm_us, 2)}
@@ -220,6 +258,7 @@ def main():
         "step_weight_bytes": step_weight_bytes,
         "step_weight_stream_frac": round(step_weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "ingest_ms": round(ingest_ms, 3),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "phases": phases,
     }
     if not args.no_cpu_baseline:

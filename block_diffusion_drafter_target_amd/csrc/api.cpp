@@ -57,7 +57,7 @@ struct Scope {
 constexpr int kMaxBatch = 4096;
 constexpr int kRowChunk = 1024;  // rows per fuse / inject GEMM pass
 constexpr int kGemmRows = 64;    // rows per weight-streaming GEMM launch
-constexpr int kTargetWGs = 384;  // workgroups a split-K GEMM launch aims for
+constexpr int kTargetWGs = 768;  // workgroups a split-K GEMM launch aims for
 
 inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -67,14 +67,14 @@ struct GemmPlan {
 };
 
 // Tile shape and split-K for Y = A W^T with up to kGemmRows rows per launch.
-// NF = 4 weight fragments per workgroup when one activation tile suffices
-// (the widest tile the register file holds without spills), else 2. Split-K
-// only in partial mode, to bring the grid to about kTargetWGs workgroups.
+// NF = 2 weight fragments per workgroup (measured best on MI355X with cold
+// caches: more waves in flight beat wider tiles). Split-K only in partial
+// mode, to bring the grid to about kTargetWGs workgroups.
 GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
   GemmPlan g;
   const int rows = std::min(M, kGemmRows);
   g.mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
-  g.nf = g.mt == 1 ? 4 : 2;
+  g.nf = 2;
   const int out_frags = mode == dfl::kGemmSwiglu ? g.nf / 2 : g.nf;
   const long long tiles = cdiv(N, 16 * out_frags) * nz;
   const int kblocks = (int)cdiv(K, 128);
@@ -87,6 +87,12 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
   g.splits = (int)cdiv(kblocks, per);
   g.k_per_split = per * 128;
   return g;
+}
+
+// Workgroup tiles of the LM-head GEMM (one argmax key per tile and row).
+int lm_tiles(const dflash_config& c) {
+  const GemmPlan g = plan_gemm(1, c.vocab, c.hidden, 1, dfl::kGemmArgmax);
+  return (int)cdiv(c.vocab, 16 * g.nf);
 }
 
 // Partial buffer (floats) that run_gemm needs for M rows.
@@ -107,7 +113,8 @@ struct GemmCall {
   int M = 0, N = 0, K = 0, nz = 1;
   int mode = dfl::kGemmPartial;
   float* P = nullptr;                 // partial mode
-  unsigned long long* keys = nullptr; // argmax mode
+  unsigned long long* keys = nullptr; // argmax mode: [tiles][ld_keys]
+  long long ld_keys = 0;
   float* dbg = nullptr;
   long long ld_dbg = 0;
   uint16_t* out = nullptr;            // swiglu mode
@@ -143,6 +150,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     p.k_per_split = g.k_per_split;
     if (c.mode == dfl::kGemmArgmax) {
       p.keys = c.keys + m0;
+      p.ld_keys = c.ld_keys;
       p.dbg = c.dbg ? c.dbg + (long long)m0 * c.ld_dbg : nullptr;
       p.ld_dbg = c.ld_dbg;
     } else if (c.mode == dfl::kGemmSwiglu) {
@@ -199,7 +207,7 @@ DraftWs draft_ws(const dflash_config& c, int batch, int max_ctx) {
   w.ao = take(Mb * qw * 2);
   w.s = take(Mb * c.intermediate * 2);
   w.ulm = take(Ml * H * 2);
-  w.keys = take(Ml * 8);
+  w.keys = take((size_t)lm_tiles(c) * Ml * 8);
   const long long att_rows = (long long)batch * c.n_kv_heads * a.n_chunks * a.gb_pad;
   w.pm = take(att_rows * 4);
   w.pl = take(att_rows * 4);
@@ -638,7 +646,6 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
       rn.out = ulm;
       rn.final_mode = 1;
       rn.B = B;
-      rn.keys = keys;
     }
     if ((e = dfl::launch_row_norm(rn, st)) != hipSuccess) return DFLASH_ERR_HIP;
   }
@@ -654,6 +661,7 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
   gl.K = H;
   gl.mode = dfl::kGemmArgmax;
   gl.keys = keys;
+  gl.ld_keys = Ml;
   gl.dbg = dbg_logits;
   gl.ld_dbg = c.vocab;
   {
@@ -661,7 +669,7 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     e = run_gemm(gl, st, nullptr);
   }
   if (e != hipSuccess) return DFLASH_ERR_HIP;
-  return hip_status(dfl::launch_unpack_draft(keys, kv->status, batch, B, draft, st));
+  return hip_status(dfl::launch_argmax_finish(keys, lm_tiles(c), kv->status, batch, B, draft, st));
 }
 
 dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,

@@ -32,8 +32,10 @@ struct GemmParams {
   // partial-sum output: P[z][s][m][n], fp32
   float* P;
   long long p_z_stride, p_s_stride;
-  // argmax output (splits == 1): keys[m] = max over n of argmax_key(y[m][n], n)
+  // argmax output (splits == 1): keys[tile * ld_keys + m] = max over the
+  // tile's n of argmax_key(y[m][n], n); tile = blockIdx.x
   unsigned long long* keys;
+  long long ld_keys;
   float* dbg;  // optional logits [M, ld_dbg]
   long long ld_dbg;
   // swiglu output (splits == 1): out[m][n] = bf16(silu(gate) * up)
@@ -83,8 +85,8 @@ hipError_t launch_attn_merge(const MergeParams& p, hipStream_t st);
 // Row-wise RMSNorm with optional residual add of split partials.
 //   x[m] (fp32, [rows, n]) += sum_s P[s][m] when residual; else y = sum_s P[s][m]
 //   out[m] = bf16(rmsnorm(x or y) * gain)
-// Final mode (lm_rows): rows j >= 1 of each block go to out[b*(B-1)+j-1] and
-// their argmax keys are cleared; row j == 0 writes nothing.
+// Final mode: rows j >= 1 of each block go to out[b*(B-1)+j-1]; row j == 0
+// writes nothing.
 struct RowNormParams {
   float* x;            // residual stream or NULL
   const float* P;      // partials [splits][rows][n] or NULL
@@ -96,7 +98,6 @@ struct RowNormParams {
   uint16_t* out;       // bf16 [rows, n] (or [batch*(B-1), n] in final mode)
   float* dbg;          // optional fp32 copy of x after the add, [rows, n]
   int final_mode, B;
-  unsigned long long* keys;
 };
 
 hipError_t launch_row_norm(const RowNormParams& p, hipStream_t st);
@@ -155,8 +156,10 @@ struct InjectPostParams {
 
 hipError_t launch_inject_post(const InjectPostParams& p, hipStream_t st);
 
-hipError_t launch_unpack_draft(const unsigned long long* keys, const int32_t* status, int batch,
-                               int B, int32_t* draft, hipStream_t st);
+// draft[b][j-1] = index of max over tiles of keys[tile * (batch*(B-1)) + row],
+// row = b*(B-1) + j-1; -1 for a sequence whose status is nonzero.
+hipError_t launch_argmax_finish(const unsigned long long* keys, int n_tiles, const int32_t* status,
+                                int batch, int B, int32_t* draft, hipStream_t st);
 
 struct VerifyParams {
   const int32_t* draft;

@@ -1,7 +1,7 @@
 // Row-wise kernels of the draft step (gfx950): embedding + RMSNorm, split-K
 // reduction + residual + RMSNorm, per-head q/k RMSNorm + RoPE + KV-cache
 // append, the inject epilogue (k-norm + RoPE + cache scatter + commit
-// of ctx_len), and the unpacking of argmax keys into draft tokens.
+// of ctx_len), and the final argmax over the LM-head tiles.
 //
 // All are bound by a few kilobytes per row; they exist to keep every fp32
 // statistic (RMSNorm sums, residual stream, RoPE) on the device between the
@@ -134,7 +134,6 @@ __global__ __launch_bounds__(kRowThreads) void row_norm_kernel(const RowNormPara
     if (j == 0) return;
     const int row = b * (p.B - 1) + j - 1;
     out = p.out + (long long)row * n;
-    if (threadIdx.x == 0) p.keys[row] = 0ull;
   } else {
     out = p.out + row_off;
   }
@@ -267,13 +266,29 @@ __global__ __launch_bounds__(256) void inject_post_kernel(const InjectPostParams
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void unpack_draft_kernel(const unsigned long long* keys,
-                                                           const int32_t* status, int batch, int B,
-                                                           int32_t* draft) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= batch * (B - 1)) return;
-  const int b = e / (B - 1);
-  draft[e] = status[b] != 0 ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(keys[e] & 0xFFFFFFFFull));
+// draft token of one LM row: the maximum key over the LM-head tiles (largest
+// logit, lowest index on ties), unpacked to the index.
+__global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long long* keys, int n_tiles,
+                                                            const int32_t* status, int batch, int B,
+                                                            int32_t* draft) {
+  __shared__ unsigned long long red[4];
+  const int row = blockIdx.x;
+  const int rows = batch * (B - 1);
+  unsigned long long best = 0ull;
+  for (int t = threadIdx.x; t < n_tiles; t += 256) best = max(best, keys[(long long)t * rows + row]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long other = __shfl_xor(best, o);
+    best = max(best, other);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    best = max(max(red[0], red[1]), max(red[2], red[3]));
+    const int b = row / (B - 1);
+    draft[row] = status[b] != 0 ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+  }
 }
 
 }  // namespace
@@ -302,10 +317,9 @@ hipError_t launch_inject_post(const InjectPostParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_unpack_draft(const unsigned long long* keys, const int32_t* status, int batch,
-                               int B, int32_t* draft, hipStream_t st) {
-  const int n = batch * (B - 1);
-  hipLaunchKernelGGL(unpack_draft_kernel, dim3((n + 255) / 256), dim3(256), 0, st, keys, status,
+hipError_t launch_argmax_finish(const unsigned long long* keys, int n_tiles, const int32_t* status,
+                                int batch, int B, int32_t* draft, hipStream_t st) {
+  hipLaunchKernelGGL(argmax_finish_kernel, dim3(batch * (B - 1)), dim3(256), 0, st, keys, n_tiles, status,
                      batch, B, draft);
   return hipGetLastError();
 }
