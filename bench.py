@@ -35,6 +35,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes of the LM-head kernel from the committed rocprofv3 PMC summary,
+    or None when the kernel source changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    src = os.path.join(root, "block_diffusion_drafter_target_amd", "csrc", "gemm_stream.hip")
+    summary = os.path.join(root, "profiles", "lm_head_argmax_c2_pmc.txt")
+    try:
+        kv = dict(line.split(": ", 1) for line in open(summary).read().splitlines() if ": " in line)
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256", "").strip() != sha:
+        return None
+    return int(kv["traffic_fetch_bytes"]) + int(kv["traffic_write_bytes"])
+
+
 def synth_target(torch, draft, m, rnd, vocab):
     """Target argmax rows [batch, B] whose accepted prefix with draft is m."""
     batch, bm1 = draft.shape
@@ -233,7 +250,7 @@ def main():
     achieved = lm_bytes / (lm_us * 1e-6) / 1e9
     roofline = {"kernel": "gemm_stream_kernel<1,2,argmax> (LM head + fused argmax)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "bytes_per_launch": lm_bytes, "us_per_launch": round(lm_us, 2)}
     # whole-step weight streaming, for context
     layer_bytes = 2 * H * (cfg.qkv_width + cfg.q_width + 2 * cfg.intermediate) + 2 * cfg.intermediate * H
