@@ -104,6 +104,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2")
+    ap.add_argument("--block", type=int, default=0, help="override the block size")
+    ap.add_argument("--batch", type=int, default=0, help="override the batch")
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -122,6 +124,10 @@ def main():
     from block_diffusion_drafter_target_amd import binding as bd
 
     cfg = synth.CONFIGS[args.config]
+    if args.block:
+        cfg = cfg.with_(block=args.block)
+    if args.batch:
+        cfg = cfg.with_(batch=args.batch)
     B, V, H, batch = cfg.block, cfg.vocab, cfg.hidden, cfg.batch
     lens = synth.make_ctx_lens(cfg)
     n_break = min(args.steps, 20)  # steps of the per-phase breakdown pass

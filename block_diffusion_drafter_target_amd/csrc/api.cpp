@@ -55,7 +55,7 @@ struct Scope {
 }  // namespace prof
 
 constexpr int kMaxBatch = 4096;
-constexpr int kRowChunk = 1024;  // rows per fuse / inject GEMM pass
+constexpr int kRowChunk = 4096;  // rows per fuse / inject GEMM pass
 constexpr int kGemmRows = 64;    // rows per weight-streaming GEMM launch
 constexpr int kTargetWGs = 768;  // workgroups a split-K GEMM launch aims for
 
@@ -63,15 +63,36 @@ inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct GemmPlan {
+  bool tiled;  // LDS-tiled kernel over all rows (M > kGemmRows) or streaming kernel per 64 rows
   int mt, nf, splits, k_per_split;
 };
 
-// Tile shape and split-K for Y = A W^T with up to kGemmRows rows per launch.
-// NF = 2 weight fragments per workgroup (measured best on MI355X with cold
-// caches: more waves in flight beat wider tiles). Split-K only in partial
-// mode, to bring the grid to about kTargetWGs workgroups.
+constexpr int kTileTargetWGs = 512;  // workgroups a split-K tiled launch aims for
+
+// Kernel, tile shape and split-K for Y = A W^T.
+// Up to kGemmRows rows: the weight-streaming kernel with NF = 2 weight
+// fragments per workgroup (measured best on MI355X with cold caches: more
+// waves in flight beat wider tiles); split-K only in partial mode, to bring
+// the grid to about kTargetWGs workgroups. More rows: the LDS-tiled kernel.
 GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
   GemmPlan g;
+  if (M > kGemmRows) {
+    g.tiled = true;
+    g.mt = g.nf = 0;
+    const long long n_tiles = mode == dfl::kGemmSwiglu ? cdiv(N, 64) : cdiv(N, 128);
+    const long long base = n_tiles * cdiv(M, 128) * nz;
+    const int slabs = (int)cdiv(K, 64);
+    int s = 1;
+    if (mode == dfl::kGemmPartial) {
+      s = (int)std::max<long long>(1, cdiv(kTileTargetWGs, base));
+      s = std::min(s, std::max(1, slabs / 2));  // at least two 64-k slabs per split
+    }
+    const int per = (int)cdiv(slabs, s);
+    g.splits = (int)cdiv(slabs, per);
+    g.k_per_split = per * 64;
+    return g;
+  }
+  g.tiled = false;
   const int rows = std::min(M, kGemmRows);
   g.mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   g.nf = 2;
@@ -89,10 +110,11 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
   return g;
 }
 
-// Workgroup tiles of the LM-head GEMM (one argmax key per tile and row).
-int lm_tiles(const dflash_config& c) {
-  const GemmPlan g = plan_gemm(1, c.vocab, c.hidden, 1, dfl::kGemmArgmax);
-  return (int)cdiv(c.vocab, 16 * g.nf);
+// Workgroup column tiles of the LM-head GEMM for M rows (one argmax key per
+// tile and row).
+int lm_tiles(const dflash_config& c, int M) {
+  const GemmPlan g = plan_gemm(M, c.vocab, c.hidden, 1, dfl::kGemmArgmax);
+  return (int)(g.tiled ? cdiv(c.vocab, 128) : cdiv(c.vocab, 16 * g.nf));
 }
 
 // Partial buffer (floats) that run_gemm needs for M rows.
@@ -126,6 +148,36 @@ struct GemmCall {
 hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
   const GemmPlan g = plan_gemm(c.M, c.N, c.K, c.nz, c.mode);
   if (splits) *splits = g.splits;
+  if (g.tiled) {
+    GemmParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.A = c.A;
+    p.lda = c.lda;
+    p.a_idx = c.a_idx;
+    p.a_idx_stride = c.a_idx_stride;
+    p.a_idx_max = c.a_idx_max;
+    for (int z = 0; z < c.nz; ++z) {
+      p.W0[z] = c.W0[z];
+      p.W1[z] = c.W1[z] ? c.W1[z] : c.W0[z];
+    }
+    p.ldw = c.ldw;
+    p.n_split = (c.W1[0] && c.mode != dfl::kGemmSwiglu) ? c.n_split : c.N;
+    p.M = c.M;
+    p.N = c.N;
+    p.K = c.K;
+    p.splits = g.splits;
+    p.k_per_split = g.k_per_split;
+    p.keys = c.keys;
+    p.ld_keys = c.ld_keys;
+    p.dbg = c.dbg;
+    p.ld_dbg = c.ld_dbg;
+    p.out = c.out;
+    p.ld_out = c.ld_out;
+    p.P = c.P;
+    p.p_s_stride = (long long)c.M * c.N;
+    p.p_z_stride = (long long)g.splits * c.M * c.N;
+    return dfl::launch_gemm_tile(p, c.mode, c.nz, st);
+  }
   for (int m0 = 0; m0 < c.M; m0 += kGemmRows) {
     GemmParams p;
     std::memset(&p, 0, sizeof(p));
@@ -207,7 +259,7 @@ DraftWs draft_ws(const dflash_config& c, int batch, int max_ctx) {
   w.ao = take(Mb * qw * 2);
   w.s = take(Mb * c.intermediate * 2);
   w.ulm = take(Ml * H * 2);
-  w.keys = take((size_t)lm_tiles(c) * Ml * 8);
+  w.keys = take((size_t)lm_tiles(c, (int)Ml) * Ml * 8);
   const long long att_rows = (long long)batch * c.n_kv_heads * a.n_chunks * a.gb_pad;
   w.pm = take(att_rows * 4);
   w.pl = take(att_rows * 4);
@@ -669,7 +721,7 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     e = run_gemm(gl, st, nullptr);
   }
   if (e != hipSuccess) return DFLASH_ERR_HIP;
-  return hip_status(dfl::launch_argmax_finish(keys, lm_tiles(c), kv->status, batch, B, draft, st));
+  return hip_status(dfl::launch_argmax_finish(keys, lm_tiles(c, Ml), kv->status, batch, B, draft, st));
 }
 
 dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,

@@ -75,6 +75,13 @@ SHAPES = {
     "b12": synth.DraftConfig(name="b12", hidden=256, n_layers=2, n_q_heads=8, n_kv_heads=2,
                              head_dim=64, intermediate=512, vocab=512, n_tap=2, block=12,
                              batch=3, ctx_len=0),
+
+    # 9 sequences x 16 rows = 144 block rows: the LDS-tiled GEMM with two row
+    # tiles (the second ragged), LM head over 135 rows
+    "tiled-b9": synth.DraftConfig(name="tiled-b9", hidden=384, n_layers=2, n_q_heads=12, n_kv_heads=4,
+                                  head_dim=64, intermediate=640, vocab=1040, n_tap=2, block=16,
+                                  batch=9, ctx_len=0),
 }
 
-CTX = {"gqa-d128": [1, 300, 777, 0, 64], "g8-d64": [500, 33], "b12": [129, 0, 64]}
+CTX = {"gqa-d128": [1, 300, 777, 0, 64], "g8-d64": [500, 33], "b12": [129, 0, 64],
+       "tiled-b9": [17, 260, 0, 64, 1, 333, 90, 128, 2]}

@@ -71,7 +71,7 @@ def test_fuse_ctx_parity(gpu_lib, shape):
     full = synth.make_weights(cfg)
     WO = gh.oracle_weights(W)
     ocfg = ref.OracleConfig.from_any(cfg)
-    n = 100  # two GEMM row chunks, ragged
+    n = 300  # tiled GEMM: three row tiles, the last ragged
     taps = synth.make_taps(cfg, n, tid=7)
     dr = Drafter(cfg, full, batch=1, max_ctx=64, max_rows=n)
     ctx = dr.fuse_ctx(torch.from_numpy(taps.view(np.int16)).view(torch.bfloat16).cuda(), n,
