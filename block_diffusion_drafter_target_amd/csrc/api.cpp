@@ -70,26 +70,27 @@ struct GemmPlan {
 constexpr int kTileTargetWGs = 512;  // workgroups a split-K tiled launch aims for
 
 // Kernel, tile shape and split-K for Y = A W^T.
-// Up to kGemmRows rows: the weight-streaming kernel with NF = 2 weight
+// Up to kGemmRows rows (or K < 128): the weight-streaming kernel with NF = 2 weight
 // fragments per workgroup (measured best on MI355X with cold caches: more
 // waves in flight beat wider tiles); split-K only in partial mode, to bring
-// the grid to about kTargetWGs workgroups. More rows: the LDS-tiled kernel.
+// the grid to about kTargetWGs workgroups. More rows: the tiled kernel
+// (activations shared through LDS).
 GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
   GemmPlan g;
-  if (M > kGemmRows) {
+  if (M > kGemmRows && K >= 128) {
     g.tiled = true;
     g.mt = g.nf = 0;
     const long long n_tiles = mode == dfl::kGemmSwiglu ? cdiv(N, 64) : cdiv(N, 128);
     const long long base = n_tiles * cdiv(M, 128) * nz;
-    const int slabs = (int)cdiv(K, 64);
+    const int slabs = (int)cdiv(K, 128);
     int s = 1;
     if (mode == dfl::kGemmPartial) {
       s = (int)std::max<long long>(1, cdiv(kTileTargetWGs, base));
-      s = std::min(s, std::max(1, slabs / 2));  // at least two 64-k slabs per split
+      s = std::min(s, std::max(1, slabs / 2));  // at least two 128-k slabs per split
     }
     const int per = (int)cdiv(slabs, s);
     g.splits = (int)cdiv(slabs, per);
-    g.k_per_split = per * 64;
+    g.k_per_split = per * 128;
     return g;
   }
   g.tiled = false;

@@ -52,8 +52,9 @@ hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int rows, int cols, h
 hipError_t launch_gemm_stream(const GemmParams& p, int mt, int nf, int mode, int nz,
                               hipStream_t st);
 
-// LDS-tiled variant for M > 64 (128 x 128 tiles, one launch over all rows;
-// k_per_split a multiple of 64). Argmax keys: one per 128-column tile.
+// Tiled variant for M > 64 (128 x 128 tiles, one launch over all rows;
+// K >= 128, k_per_split a multiple of 128). Argmax keys: one per 128-column
+// tile.
 hipError_t launch_gemm_tile(const GemmParams& p, int mode, int nz, hipStream_t st);
 
 struct AttnParams {
