@@ -221,7 +221,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
 }
 
 struct AttnPlan {
-  int n_chunks, gb_pad;
+  int n_chunks, slice, gb_pad;
 };
 
 // Key chunks per (sequence, kv head): enough workgroups for the chip
@@ -234,6 +234,8 @@ AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx) {
   long long n = cdiv(512, units);
   n = std::min<long long>(n, cdiv(max_ctx, 64));
   a.n_chunks = (int)std::max<long long>(1, std::min<long long>(n, 64));
+  // 128-key slices keep twice the bytes in flight once chunks are long
+  a.slice = cdiv(max_ctx, a.n_chunks) >= 512 ? 128 : 64;
   return a;
 }
 
@@ -596,6 +598,7 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     at.B = B;
     at.max_ctx = kv->max_ctx;
     at.n_chunks = ap.n_chunks;
+    at.slice = ap.slice;
     at.gb_pad = ap.gb_pad;
     at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     at.pm = pm;
@@ -619,6 +622,7 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     mp.B = B;
     mp.D = D;
     mp.n_chunks = ap.n_chunks;
+    mp.slice = ap.slice;
     mp.gb_pad = ap.gb_pad;
     mp.out = ao;
     if ((e = dfl::launch_attn_merge(mp, st)) != hipSuccess) return DFLASH_ERR_HIP;

@@ -28,38 +28,39 @@ namespace dfl {
 
 namespace {
 
-constexpr int kSlice = 64;           // keys per LDS slice
-constexpr int kVtStride = kSlice + 4;  // bf16 per transposed V row (8-byte pad)
-
-// Keys per chunk of a sequence with Lk keys split n_chunks ways.
-__device__ __forceinline__ int chunk_len(int Lk, int n_chunks) {
+// Keys per chunk of a sequence with Lk keys split n_chunks ways, a multiple of
+// the slice length.
+__device__ __forceinline__ int chunk_len(int Lk, int n_chunks, int slice) {
   const int c = (Lk + n_chunks - 1) / n_chunks;
-  return max(kSlice, (c + kSlice - 1) / kSlice * kSlice);
+  return max(slice, (c + slice - 1) / slice * slice);
 }
 
-template <int D>
+// SL keys per LDS slice (64 for short chunks, 128 to keep more bytes in
+// flight on long ones).
+template <int D, int SL>
 struct Slice {
   static constexpr int DC = D / 8;  // 16-byte chunks per key row
-  static constexpr int KL = kSlice * DC / 256;
-  static constexpr int VL = (kSlice / 2) * DC / 256;
+  static constexpr int KL = SL * DC / 256;
+  static constexpr int VL = (SL / 2) * DC / 256;
+  static constexpr int VT = SL + 4;  // bf16 per transposed V row (8-byte pad)
 };
 
 // Global -> registers: the K and V rows of keys [k0, k0 + 64), clamped to the
 // last valid key (clamped rows are masked out of the softmax).
-template <int D>
-__device__ __forceinline__ void load_slice(u32x4 (&kreg)[Slice<D>::KL], u32x4 (&va)[Slice<D>::VL],
-                                           u32x4 (&vb)[Slice<D>::VL], const bf16_t* kc,
+template <int D, int SL>
+__device__ __forceinline__ void load_slice(u32x4 (&kreg)[(Slice<D, SL>::KL)], u32x4 (&va)[(Slice<D, SL>::VL)],
+                                           u32x4 (&vb)[(Slice<D, SL>::VL)], const bf16_t* kc,
                                            const bf16_t* vc, int k0, int k_end) {
-  constexpr int DC = Slice<D>::DC;
+  constexpr int DC = Slice<D, SL>::DC;
 #pragma unroll
-  for (int t = 0; t < Slice<D>::KL; ++t) {
+  for (int t = 0; t < Slice<D, SL>::KL; ++t) {
     const int e = threadIdx.x + t * 256;
     const int key = e / DC, ch = e % DC;
     const int kidx = min(k0 + key, k_end - 1);
     kreg[t] = *reinterpret_cast<const u32x4*>(kc + (long long)kidx * D + ch * 8);
   }
 #pragma unroll
-  for (int t = 0; t < Slice<D>::VL; ++t) {
+  for (int t = 0; t < Slice<D, SL>::VL; ++t) {
     const int e = threadIdx.x + t * 256;
     const int kp = e / DC, ch = e % DC;
     const int k0i = min(k0 + 2 * kp, k_end - 1), k1i = min(k0 + 2 * kp + 1, k_end - 1);
@@ -68,49 +69,52 @@ __device__ __forceinline__ void load_slice(u32x4 (&kreg)[Slice<D>::KL], u32x4 (&
   }
 }
 
+template <int VT>
 __device__ __forceinline__ void store_vpair(bf16_t* vt, int d, int kp, uint32_t a, uint32_t b) {
   // a holds keys 2kp's elements (d, d+1), b the same of key 2kp+1
-  *reinterpret_cast<uint32_t*>(vt + d * kVtStride + 2 * kp) = (a & 0xFFFFu) | (b << 16);
-  *reinterpret_cast<uint32_t*>(vt + (d + 1) * kVtStride + 2 * kp) = (a >> 16) | (b & 0xFFFF0000u);
+  *reinterpret_cast<uint32_t*>(vt + d * VT + 2 * kp) = (a & 0xFFFFu) | (b << 16);
+  *reinterpret_cast<uint32_t*>(vt + (d + 1) * VT + 2 * kp) = (a >> 16) | (b & 0xFFFF0000u);
 }
 
 // Registers -> LDS: K row-major with the 16-byte chunk index XOR (key & 7);
 // V transposed to [d][key] so that a lane reads 4 keys of one d in 8 bytes.
-template <int D>
-__device__ __forceinline__ void store_slice(u32x4* ks, bf16_t* vt, const u32x4 (&kreg)[Slice<D>::KL],
-                                            const u32x4 (&va)[Slice<D>::VL],
-                                            const u32x4 (&vb)[Slice<D>::VL]) {
-  constexpr int DC = Slice<D>::DC;
+template <int D, int SL>
+__device__ __forceinline__ void store_slice(u32x4* ks, bf16_t* vt, const u32x4 (&kreg)[(Slice<D, SL>::KL)],
+                                            const u32x4 (&va)[(Slice<D, SL>::VL)],
+                                            const u32x4 (&vb)[(Slice<D, SL>::VL)]) {
+  constexpr int DC = Slice<D, SL>::DC;
+  constexpr int VT = Slice<D, SL>::VT;
 #pragma unroll
-  for (int t = 0; t < Slice<D>::KL; ++t) {
+  for (int t = 0; t < Slice<D, SL>::KL; ++t) {
     const int e = threadIdx.x + t * 256;
     const int key = e / DC, ch = e % DC;
     ks[key * DC + (ch ^ (key & 7))] = kreg[t];
   }
 #pragma unroll
-  for (int t = 0; t < Slice<D>::VL; ++t) {
+  for (int t = 0; t < Slice<D, SL>::VL; ++t) {
     const int e = threadIdx.x + t * 256;
     const int kp = e / DC, ch = e % DC;
-    store_vpair(vt, ch * 8 + 0, kp, va[t].x, vb[t].x);
-    store_vpair(vt, ch * 8 + 2, kp, va[t].y, vb[t].y);
-    store_vpair(vt, ch * 8 + 4, kp, va[t].z, vb[t].z);
-    store_vpair(vt, ch * 8 + 6, kp, va[t].w, vb[t].w);
+    store_vpair<VT>(vt, ch * 8 + 0, kp, va[t].x, vb[t].x);
+    store_vpair<VT>(vt, ch * 8 + 2, kp, va[t].y, vb[t].y);
+    store_vpair<VT>(vt, ch * 8 + 4, kp, va[t].z, vb[t].z);
+    store_vpair<VT>(vt, ch * 8 + 6, kp, va[t].w, vb[t].w);
   }
 }
 
-template <int D, int QPW>
+template <int D, int QPW, int SL>
 __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
-  constexpr int DC = Slice<D>::DC;
-  constexpr int KL = Slice<D>::KL;
-  constexpr int VL = Slice<D>::VL;
+  constexpr int DC = Slice<D, SL>::DC;
+  constexpr int KL = Slice<D, SL>::KL;
+  constexpr int VL = Slice<D, SL>::VL;
+  constexpr int VT = Slice<D, SL>::VT;
   static_assert(KL >= 1 && VL >= 1, "slice too small");
-  __shared__ __align__(16) u32x4 ks[kSlice * DC];
-  __shared__ __align__(16) bf16_t vt[D * kVtStride];
+  __shared__ __align__(16) u32x4 ks[SL * DC];
+  __shared__ __align__(16) bf16_t vt[D * VT];
 
   const int b = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
   if (p.status[b] != 0) return;
   const int Lk = p.ctx_len[b] + p.B;
-  const int chunk = chunk_len(Lk, p.n_chunks);
+  const int chunk = chunk_len(Lk, p.n_chunks, SL);
   const int k_start = c * chunk;
   if (k_start >= Lk) return;
   const int k_end = min(Lk, k_start + chunk);
@@ -151,20 +155,21 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
 
   u32x4 kreg[KL], va[VL], vb[VL];
 
-  load_slice<D>(kreg, va, vb, kc, vc, k_start, k_end);
-  for (int k0 = k_start; k0 < k_end; k0 += kSlice) {
-    store_slice<D>(ks, vt, kreg, va, vb);
+  load_slice<D, SL>(kreg, va, vb, kc, vc, k_start, k_end);
+  for (int k0 = k_start; k0 < k_end; k0 += SL) {
+    store_slice<D, SL>(ks, vt, kreg, va, vb);
     __syncthreads();
     // prefetch the next slice (past the end it re-reads the last key: valid
     // memory, never used)
-    load_slice<D>(kreg, va, vb, kc, vc, k0 + kSlice, k_end);
+    load_slice<D, SL>(kreg, va, vb, kc, vc, k0 + SL, k_end);
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       const int qt = wave + 4 * i;
       if (qt >= QT) continue;
-      f32x4_t sacc[4];
+      constexpr int KT = SL / 16;  // 16-key tiles per slice
+      f32x4_t sacc[KT];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
         sacc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         const int key = kt * 16 + r;
 #pragma unroll
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
       }
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = k0 + kt * 16 + 4 * gq + e;
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
       const float alpha = exp2f(mrun[i] - mnew);
       float rs = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float pv = exp2f(sacc[kt][e] - mnew);
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) o[i][dt] *= alpha;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < KT / 2; ++h) {
         u32x4 pb;
         pb.x = pack_bf2(sacc[2 * h][0], sacc[2 * h][1]);
         pb.y = pack_bf2(sacc[2 * h][2], sacc[2 * h][3]);
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
         pb.w = pack_bf2(sacc[2 * h + 1][2], sacc[2 * h + 1][3]);
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-          const bf16_t* row = vt + (dt * 16 + r) * kVtStride + 32 * h + 4 * gq;
+          const bf16_t* row = vt + (dt * 16 + r) * VT + 32 * h + 4 * gq;
           const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
           const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
@@ -256,7 +261,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const int G = p.Hq / p.Hkv;
   const int g = h / G, rr = (h % G) * p.B + j;
   const int Lk = p.ctx_len[b] + p.B;
-  const int nch = min(p.n_chunks, (Lk + chunk_len(Lk, p.n_chunks) - 1) / chunk_len(Lk, p.n_chunks));
+  const int cl = chunk_len(Lk, p.n_chunks, p.slice);
+  const int nch = min(p.n_chunks, (Lk + cl - 1) / cl);
   const long long base = ((long long)b * p.Hkv + g) * p.n_chunks;
   const float mc = lane < nch ? p.pm[(base + lane) * p.gb_pad + rr] : -__builtin_inff();
   const float lc = lane < nch ? p.pl[(base + lane) * p.gb_pad + rr] : 0.f;
@@ -287,19 +293,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   if (p.D > 64) out[lane + 64] = f2bf(o1 * inv);
 }
 
-template <int D>
-hipError_t launch_d(const AttnParams& p, hipStream_t st) {
+template <int D, int SL>
+hipError_t launch_ds(const AttnParams& p, hipStream_t st) {
   dim3 grid(p.n_chunks, p.Hkv, p.batch);
   const int qt = p.gb_pad / 16;
   if (qt <= 4)
-    hipLaunchKernelGGL((attn_kernel<D, 1>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((attn_kernel<D, 1, SL>), grid, dim3(256), 0, st, p);
   else if (qt <= 8)
-    hipLaunchKernelGGL((attn_kernel<D, 2>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((attn_kernel<D, 2, SL>), grid, dim3(256), 0, st, p);
   else if (qt <= 16)
-    hipLaunchKernelGGL((attn_kernel<D, 4>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((attn_kernel<D, 4, SL>), grid, dim3(256), 0, st, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttnParams& p, hipStream_t st) {
+  if (p.slice == 128) return launch_ds<D, 128>(p, st);
+  if (p.slice == 64) return launch_ds<D, 64>(p, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

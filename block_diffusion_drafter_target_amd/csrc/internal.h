@@ -65,7 +65,8 @@ struct AttnParams {
   const int32_t* status;
   int batch, Hq, Hkv, B, max_ctx;
   int n_chunks;  // key chunks per (b, g) (grid x, <= 64); chunk length per sequence
-                 // = max(64, L_b + B split n_chunks ways, rounded up to 64)
+                 // = max(slice, L_b + B split n_chunks ways, rounded up to slice)
+  int slice;     // keys per LDS slice: 64 or 128
   int gb_pad;    // query rows per (b, g), padded to 16
   float scale_log2;
   float* pm;   // [batch][Hkv][n_chunks][gb_pad]
@@ -81,7 +82,7 @@ struct MergeParams {
   const float* po;
   const int32_t* ctx_len;
   const int32_t* status;
-  int batch, Hq, Hkv, B, D, n_chunks, gb_pad;
+  int batch, Hq, Hkv, B, D, n_chunks, slice, gb_pad;
   uint16_t* out;  // [batch*B, Hq*D]
 };
 
