@@ -234,8 +234,10 @@ AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx) {
   long long n = cdiv(512, units);
   n = std::min<long long>(n, cdiv(max_ctx, 64));
   a.n_chunks = (int)std::max<long long>(1, std::min<long long>(n, 64));
-  // 128-key slices keep twice the bytes in flight once chunks are long
-  a.slice = cdiv(max_ctx, a.n_chunks) >= 512 ? 128 : 64;
+  // 128-key slices keep twice the bytes in flight once chunks are long (not
+  // with four 16-query tiles per wave at D = 128: those registers allow 64)
+  const bool wide_ok = !(c.head_dim == 128 && a.gb_pad > 128);
+  a.slice = wide_ok && cdiv(max_ctx, a.n_chunks) >= 512 ? 128 : 64;
   return a;
 }
 

@@ -101,8 +101,17 @@ __device__ __forceinline__ void store_slice(u32x4* ks, bf16_t* vt, const u32x4 (
   }
 }
 
+// Waves per SIMD the register budget targets: two where a wave's accumulators,
+// queries and scores fit 256 registers, else one (QPW = 4, or D = 128 with two
+// query tiles per wave).
+template <int D, int QPW>
+struct AttnOcc {
+  static constexpr int kWaves = (QPW >= 4 || (D == 128 && QPW >= 2)) ? 1 : 2;
+};
+
 template <int D, int QPW, int SL>
-__global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(AttnOcc<D, QPW>::kWaves, AttnOcc<D, QPW>::kWaves)))
+void attn_kernel(const AttnParams p) {
   constexpr int DC = Slice<D, SL>::DC;
   constexpr int KL = Slice<D, SL>::KL;
   constexpr int VL = Slice<D, SL>::VL;
@@ -162,43 +171,53 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
     // prefetch the next slice (past the end it re-reads the last key: valid
     // memory, never used)
     load_slice<D, SL>(kreg, va, vb, kc, vc, k0 + SL, k_end);
+    constexpr int KT = SL / 16;  // 16-key tiles per slice
+    // S^T tiles of every query tile of the wave; each K fragment is read from
+    // LDS once and feeds all of them
+    f32x4_t sacc[QPW][KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int i = 0; i < QPW; ++i) sacc[i][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int key = kt * 16 + r;
+#pragma unroll
+      for (int ds = 0; ds < D / 32; ++ds) {
+        const u32x4 a = ks[key * DC + ((ds * 4 + gq) ^ (key & 7))];
+#pragma unroll
+        for (int i = 0; i < QPW; ++i) sacc[i][kt] = mfma16x16x32(a, qreg[i][ds], sacc[i][kt]);
+      }
+    }
+    // keys past the end exist only in the chunk's last slice
+    if (k0 + SL > k_end) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (k0 + kt * 16 + 4 * gq + e >= k_end)
+#pragma unroll
+            for (int i = 0; i < QPW; ++i) sacc[i][kt][e] = -__builtin_inff();
+    }
+    // online softmax on raw scores: the running max is kept in scaled base-2
+    // units, and max(s) * c == max(s * c) for the positive scale c
+    u32x4 pb[QPW][KT / 2];
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
-      const int qt = wave + 4 * i;
-      if (qt >= QT) continue;
-      constexpr int KT = SL / 16;  // 16-key tiles per slice
-      f32x4_t sacc[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        sacc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int key = kt * 16 + r;
-#pragma unroll
-        for (int ds = 0; ds < D / 32; ++ds) {
-          const u32x4 a = ks[key * DC + ((ds * 4 + gq) ^ (key & 7))];
-          sacc[kt] = mfma16x16x32(a, qreg[i][ds], sacc[kt]);
-        }
-      }
       float mx = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = k0 + kt * 16 + 4 * gq + e;
-          const float sv = key < k_end ? sacc[kt][e] * p.scale_log2 : -__builtin_inff();
-          sacc[kt][e] = sv;
-          mx = fmaxf(mx, sv);
-        }
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[i][kt][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[i], mx);
-      const float alpha = exp2f(mrun[i] - mnew);
+      const float mnew = fmaxf(mrun[i], mx * p.scale_log2);
+      const float alpha = fast_exp2(mrun[i] - mnew);
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pv = exp2f(sacc[kt][e] - mnew);
-          sacc[kt][e] = pv;
+          const float pv = fast_exp2(__builtin_fmaf(sacc[i][kt][e], p.scale_log2, -mnew));
+          sacc[i][kt][e] = pv;
           rs += pv;
         }
       rs += __shfl_xor(rs, 16);
@@ -207,21 +226,26 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
       mrun[i] = mnew;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) o[i][dt] *= alpha;
+      // P^T as the B operand: keys 32h + 4gq.. and 32h + 16 + 4gq.. of lane
+      // group gq, the same key order as the V^T operand below
 #pragma unroll
-      for (int h = 0; h < KT / 2; ++h) {
-        u32x4 pb;
-        pb.x = pack_bf2(sacc[2 * h][0], sacc[2 * h][1]);
-        pb.y = pack_bf2(sacc[2 * h][2], sacc[2 * h][3]);
-        pb.z = pack_bf2(sacc[2 * h + 1][0], sacc[2 * h + 1][1]);
-        pb.w = pack_bf2(sacc[2 * h + 1][2], sacc[2 * h + 1][3]);
+      for (int h = 0; h < KT / 2; ++h)
+        pb[i][h] = u32x4{pack_bf2(sacc[i][2 * h][0], sacc[i][2 * h][1]),
+                         pack_bf2(sacc[i][2 * h][2], sacc[i][2 * h][3]),
+                         pack_bf2(sacc[i][2 * h + 1][0], sacc[i][2 * h + 1][1]),
+                         pack_bf2(sacc[i][2 * h + 1][2], sacc[i][2 * h + 1][3])};
+    }
+    // O^T += V^T P^T; each V^T fragment is read once for all query tiles
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const bf16_t* row = vt + (dt * 16 + r) * VT + 32 * h + 4 * gq;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
-          const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
-          o[i][dt] = mfma16x16x32(a, pb, o[i][dt]);
-        }
+    for (int h = 0; h < KT / 2; ++h) {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const bf16_t* row = vt + (dt * 16 + r) * VT + 32 * h + 4 * gq;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
+        const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int i = 0; i < QPW; ++i) o[i][dt] = mfma16x16x32(a, pb[i][h], o[i][dt]);
       }
     }
     __syncthreads();
@@ -267,7 +291,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const float mc = lane < nch ? p.pm[(base + lane) * p.gb_pad + rr] : -__builtin_inff();
   const float lc = lane < nch ? p.pl[(base + lane) * p.gb_pad + rr] : 0.f;
   const float M = wave_max(mc);
-  const float w = lane < nch ? exp2f(mc - M) : 0.f;
+  const float w = lane < nch ? fast_exp2(mc - M) : 0.f;
   const float l = wave_sum(w * lc);
   float o0 = 0.f, o1 = 0.f;
   for (int c0 = 0; c0 < nch; c0 += 8) {
@@ -301,9 +325,11 @@ hipError_t launch_ds(const AttnParams& p, hipStream_t st) {
     hipLaunchKernelGGL((attn_kernel<D, 1, SL>), grid, dim3(256), 0, st, p);
   else if (qt <= 8)
     hipLaunchKernelGGL((attn_kernel<D, 2, SL>), grid, dim3(256), 0, st, p);
-  else if (qt <= 16)
-    hipLaunchKernelGGL((attn_kernel<D, 4, SL>), grid, dim3(256), 0, st, p);
-  else
+  else if (qt <= 16) {
+    // four query tiles per wave at D = 128 fit the registers with 64-key slices only
+    if constexpr (D == 128 && SL == 128) return hipErrorInvalidValue;
+    else hipLaunchKernelGGL((attn_kernel<D, 4, SL>), grid, dim3(256), 0, st, p);
+  } else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -25,9 +25,17 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return (bf16_t)(u >> 16);
 }
 
+// Two fp32 -> packed bf16 pair (lo in the low half), round to nearest even, by
+// gfx950's packed conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{lo, hi}), bf2_t));
 }
+
+// 2^x by the hardware exponential (no denormal range fix-up: results below
+// 2^-126 may flush to zero, which the softmax weights tolerate).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).
 // Operand layout: lane l supplies row (A) / column (B) l%16 and the eight
