@@ -136,7 +136,7 @@ struct GemmCall {
   int M = 0, N = 0, K = 0, nz = 1;
   int mode = dfl::kGemmPartial;
   float* P = nullptr;                 // partial mode
-  unsigned long long* keys = nullptr; // argmax mode: [tiles][ld_keys]
+  unsigned long long* keys = nullptr; // argmax mode: [M][ld_keys], one key per column tile
   long long ld_keys = 0;
   float* dbg = nullptr;
   long long ld_dbg = 0;
@@ -202,7 +202,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     p.splits = g.splits;
     p.k_per_split = g.k_per_split;
     if (c.mode == dfl::kGemmArgmax) {
-      p.keys = c.keys + m0;
+      p.keys = c.keys + (long long)m0 * c.ld_keys;
       p.ld_keys = c.ld_keys;
       p.dbg = c.dbg ? c.dbg + (long long)m0 * c.ld_dbg : nullptr;
       p.ld_dbg = c.ld_dbg;
@@ -573,6 +573,7 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     qp.gq = static_cast<const uint16_t*>(L.g_q);
     qp.gk = static_cast<const uint16_t*>(L.g_k);
     qp.rope = m->w.rope;
+    qp.rope_max = m->w.rope_max_pos;
     qp.ctx_len = kv->ctx_len;
     qp.status = kv->status;
     qp.batch = batch;
@@ -720,7 +721,7 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
   gl.K = H;
   gl.mode = dfl::kGemmArgmax;
   gl.keys = keys;
-  gl.ld_keys = Ml;
+  gl.ld_keys = lm_tiles(c, Ml);
   gl.dbg = dbg_logits;
   gl.ld_dbg = c.vocab;
   {

@@ -143,9 +143,11 @@ void attn_kernel(const AttnParams p) {
     rr = rr < GB ? rr : GB - 1;
     const int hl = rr / p.B, j = rr % p.B;
     const bf16_t* qrow = p.q + ((long long)(b * p.B + j) * p.Hq + g * G + hl) * D + gq * 8;
+    // rows past GB read the last row (valid memory); padded tiles are zeroed
+    // by a select, not a guarded load
+    const uint32_t keep = qt < QT ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds)
-      qreg[i][ds] = qt < QT ? *reinterpret_cast<const u32x4*>(qrow + ds * 32) : u32x4{0, 0, 0, 0};
+    for (int ds = 0; ds < D / 32; ++ds) qreg[i][ds] = *reinterpret_cast<const u32x4*>(qrow + ds * 32) & keep;
   }
 
   float mrun[QPW], lrun[QPW];
@@ -269,8 +271,11 @@ void attn_kernel(const AttnParams p) {
 
 // o[m][h] = sum_c exp2(m_c - M) O_c / sum_c exp2(m_c - M) l_c over the chunks
 // that hold keys of the sequence. One wave per (row, head); lane c holds
-// chunk c's statistics, and the D outputs accumulate over chunks with the
-// loads of eight chunks issued together.
+// chunk c's statistics, lane d output elements d and d + 64. The statistics
+// and the first kMergeBatch chunks' partial outputs are loaded in one round
+// trip; the weights are applied once the wave's maximum is known.
+constexpr int kMergeBatch = 32;
+
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = blockIdx.y;
@@ -278,43 +283,61 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   if (h >= p.Hq) return;
   const int b = m / p.B, j = m % p.B;
   bf16_t* out = p.out + ((long long)m * p.Hq + h) * p.D;
-  if (p.status[b] != 0) {
-    for (int d = lane; d < p.D; d += 64) out[d] = 0;
-    return;
-  }
+  const int st = p.status[b];
   const int G = p.Hq / p.Hkv;
   const int g = h / G, rr = (h % G) * p.B + j;
   const int Lk = p.ctx_len[b] + p.B;
   const int cl = chunk_len(Lk, p.n_chunks, p.slice);
-  const int nch = min(p.n_chunks, (Lk + cl - 1) / cl);
+  const int nch = max(0, min(p.n_chunks, (Lk + cl - 1) / cl));
   const long long base = ((long long)b * p.Hkv + g) * p.n_chunks;
-  const float mc = lane < nch ? p.pm[(base + lane) * p.gb_pad + rr] : -__builtin_inff();
-  const float lc = lane < nch ? p.pl[(base + lane) * p.gb_pad + rr] : 0.f;
+  const bool two = p.D > 64;
+  // Loads are unconditional at clamped chunk indexes: a guarded load becomes a
+  // branch, and the compiler waits for every outstanding load where branches
+  // join. Chunks past nch carry weight 0.
+  const int clast = max(nch - 1, 0);
+  const int d2 = two ? lane + 64 : lane;
+  const long long sl = (base + min(lane, clast)) * p.gb_pad + rr;
+  float mc = p.pm[sl];
+  float lc = p.pl[sl];
+  float a[kMergeBatch], bb[kMergeBatch];
+  auto load = [&](int c0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kMergeBatch; ++t) {
+      const float* po = p.po + ((base + min(c0 + t, clast)) * p.gb_pad + rr) * p.D;
+      a[t] = po[lane];
+      bb[t] = po[d2];
+    }
+  };
+  load(0);
+  // keep the whole batch of loads ahead of the reductions below
+  __builtin_amdgcn_sched_barrier(0);
+  if (lane >= nch) {
+    mc = -__builtin_inff();
+    lc = 0.f;
+  }
   const float M = wave_max(mc);
   const float w = lane < nch ? fast_exp2(mc - M) : 0.f;
   const float l = wave_sum(w * lc);
   float o0 = 0.f, o1 = 0.f;
-  for (int c0 = 0; c0 < nch; c0 += 8) {
-    float a[8], bb[8], wc[8];
+  for (int c0 = 0; c0 < nch; c0 += kMergeBatch) {
+    if (c0 > 0) load(c0);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int c = c0 + t;
-      wc[t] = __shfl(w, c < 64 ? c : 63);
-      const float* po = p.po + ((base + (c < nch ? c : 0)) * p.gb_pad + rr) * p.D;
-      a[t] = c < nch ? po[lane] : 0.f;
-      bb[t] = (c < nch && p.D > 64) ? po[lane + 64] : 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < kMergeBatch; ++t) {
+      const float wc = __shfl(w, (c0 + t) & 63);
       if (c0 + t < nch) {
-        o0 += wc[t] * a[t];
-        o1 += wc[t] * bb[t];
+        o0 += wc * a[t];
+        o1 += wc * bb[t];
       }
     }
   }
+  if (st != 0) {
+    out[lane] = 0;
+    if (two) out[lane + 64] = 0;
+    return;
+  }
   const float inv = 1.0f / l;
   out[lane] = f2bf(o0 * inv);
-  if (p.D > 64) out[lane + 64] = f2bf(o1 * inv);
+  if (two) out[lane + 64] = f2bf(o1 * inv);
 }
 
 template <int D, int SL>

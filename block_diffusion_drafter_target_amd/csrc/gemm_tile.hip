@@ -198,7 +198,7 @@ void gemm_tile_kernel(const GemmParams p) {
     for (int i = threadIdx.x; i < kBM; i += 256) {
       const int m = m0 + i;
       if (m < p.M)
-        p.keys[(long long)blockIdx.x * p.ld_keys + m] =
+        p.keys[(long long)m * p.ld_keys + blockIdx.x] =
             max(max(kbest[0][i], kbest[1][i]), max(kbest[2][i], kbest[3][i]));
     }
   }

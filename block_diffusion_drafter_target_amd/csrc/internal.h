@@ -129,7 +129,8 @@ struct QkvPostParams {
   int splits;
   const uint16_t* gq;
   const uint16_t* gk;
-  const float* rope;  // [max_pos][D/2][2]
+  const float* rope;  // [rope_max][D/2][2]
+  int rope_max;
   const int32_t* ctx_len;
   const int32_t* status;
   int batch, B, Hq, Hkv, D, max_ctx;

@@ -33,25 +33,39 @@ __device__ __forceinline__ float block_sum_512(float v, float* red) {
 
 // Adds the split partials of row m, columns 4*i4.., to v. All loads of a
 // batch of splits are issued before any add, so the row costs one memory
-// round trip per kSplitBatch splits.
+// round trip per kSplitBatch splits. Loads are unconditional at clamped
+// addresses (a guarded load becomes a branch, and the compiler waits for
+// every outstanding load where branches join); out-of-range values are
+// dropped by a select.
 __device__ __forceinline__ void add_splits(f32x4_t (&v)[kMaxC4], const float* P, long long s_stride,
-                                           int splits, long long row_off, int n4) {
+                                           int splits, long long row_off, int n4, float keep_v) {
   for (int s0 = 0; s0 < splits; s0 += kSplitBatch) {
     f32x4_t t[kMaxC4][kSplitBatch];
 #pragma unroll
     for (int c = 0; c < kMaxC4; ++c) {
-      const int i4 = threadIdx.x + c * kRowThreads;
+      const int i4 = min(threadIdx.x + c * kRowThreads, n4 - 1);
 #pragma unroll
-      for (int j = 0; j < kSplitBatch; ++j)
-        t[c][j] = (i4 < n4 && s0 + j < splits)
-                      ? *reinterpret_cast<const f32x4_t*>(P + (long long)(s0 + j) * s_stride + row_off + 4 * i4)
-                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kSplitBatch; ++j) {
+        const int sj = min(s0 + j, splits - 1);
+        t[c][j] = *reinterpret_cast<const f32x4_t*>(P + (long long)sj * s_stride + row_off + 4 * i4);
+      }
+    }
+    if (s0 == 0) {
+#pragma unroll
+      for (int c = 0; c < kMaxC4; ++c) v[c] *= keep_v;
     }
 #pragma unroll
     for (int c = 0; c < kMaxC4; ++c)
 #pragma unroll
-      for (int j = 0; j < kSplitBatch; ++j) v[c] += t[c][j];
+      for (int j = 0; j < kSplitBatch; ++j)
+        if (threadIdx.x + c * kRowThreads < n4 && s0 + j < splits) v[c] += t[c][j];
   }
+}
+
+// Unpacks four bf16 (two 32-bit words) to fp32.
+__device__ __forceinline__ f32x4_t bf4_to_f32(u32x2 w) {
+  return f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                 __uint_as_float(w.y & 0xFFFF0000u)};
 }
 
 // ---------------------------------------------------------------------------
@@ -70,16 +84,21 @@ __global__ __launch_bounds__(kRowThreads) void embed_kernel(const EmbedParams p)
   if (tok_bad) tok = 0;
   const bf16_t* e = p.embed + (long long)tok * p.H;
   const int n4 = p.H / 4;
+  // unconditional loads at clamped columns (see add_splits)
+  u32x2 ew[kMaxC4], gw[kMaxC4];
+#pragma unroll
+  for (int c = 0; c < kMaxC4; ++c) {
+    const int i4 = min(threadIdx.x + c * kRowThreads, n4 - 1);
+    ew[c] = *reinterpret_cast<const u32x2*>(e + 4 * i4);
+    gw[c] = *reinterpret_cast<const u32x2*>(p.gain + 4 * i4);
+  }
   f32x4_t v[kMaxC4];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < kMaxC4; ++c) {
     const int i4 = threadIdx.x + c * kRowThreads;
-    v[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    v[c] = i4 < n4 ? bf4_to_f32(ew[c]) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (i4 < n4) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(e + 4 * i4);
-      v[c] = f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
       *reinterpret_cast<f32x4_t*>(p.x + (long long)m * p.H + 4 * i4) = v[c];
       if (p.dbg) *reinterpret_cast<f32x4_t*>(p.dbg + (long long)m * p.H + 4 * i4) = v[c];
     }
@@ -91,35 +110,46 @@ __global__ __launch_bounds__(kRowThreads) void embed_kernel(const EmbedParams p)
   for (int c = 0; c < kMaxC4; ++c) {
     const int i4 = threadIdx.x + c * kRowThreads;
     if (i4 < n4) {
-      const u32x2 gw = *reinterpret_cast<const u32x2*>(p.gain + 4 * i4);
-      const u32x2 o = u32x2{pack_bf2(v[c][0] * inv * __uint_as_float(gw.x << 16),
-                                     v[c][1] * inv * __uint_as_float(gw.x & 0xFFFF0000u)),
-                            pack_bf2(v[c][2] * inv * __uint_as_float(gw.y << 16),
-                                     v[c][3] * inv * __uint_as_float(gw.y & 0xFFFF0000u))};
+      const f32x4_t g = bf4_to_f32(gw[c]);
+      const u32x2 o = u32x2{pack_bf2(v[c][0] * inv * g[0], v[c][1] * inv * g[1]),
+                            pack_bf2(v[c][2] * inv * g[2], v[c][3] * inv * g[3])};
       *reinterpret_cast<u32x2*>(p.u + (long long)m * p.H + 4 * i4) = o;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// y = (x +=) sum of split partials; out = bf16(RMSNorm(y) * gain)
+// y = (x +=) sum of split partials (at least one split); out =
+// bf16(RMSNorm(y) * gain)
 __global__ __launch_bounds__(kRowThreads) void row_norm_kernel(const RowNormParams p) {
   __shared__ float red[kRowThreads / 64];
   const int m = blockIdx.x;
   const int n = p.n, n4 = n / 4;
   const long long row_off = (long long)m * n;
+  // the row, its split partials and the gains are independent loads, issued
+  // unconditionally at clamped columns before the first use (see add_splits)
   f32x4_t v[kMaxC4];
+  u32x2 gw[kMaxC4];
 #pragma unroll
   for (int c = 0; c < kMaxC4; ++c) {
-    const int i4 = threadIdx.x + c * kRowThreads;
-    v[c] = (p.x && i4 < n4) ? *reinterpret_cast<const f32x4_t*>(p.x + row_off + 4 * i4)
-                            : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int i4 = min(threadIdx.x + c * kRowThreads, n4 - 1);
+    gw[c] = *reinterpret_cast<const u32x2*>(p.gain + 4 * i4);
   }
-  if (p.P) add_splits(v, p.P, p.p_s_stride, p.splits, row_off, n4);
+  // without a residual the row loads read the first split instead (valid
+  // memory, values dropped), so no branch separates them from the partials
+  const float* xs = p.x ? p.x : p.P;
+  const float keep_x = p.x ? 1.f : 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxC4; ++c) {
+    const int i4 = min(threadIdx.x + c * kRowThreads, n4 - 1);
+    v[c] = *reinterpret_cast<const f32x4_t*>(xs + row_off + 4 * i4);
+  }
+  add_splits(v, p.P, p.p_s_stride, p.splits, row_off, n4, keep_x);
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < kMaxC4; ++c) {
     const int i4 = threadIdx.x + c * kRowThreads;
+    if (i4 >= n4) v[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (i4 < n4) {
       if (p.x) *reinterpret_cast<f32x4_t*>(p.x + row_off + 4 * i4) = v[c];
       if (p.dbg) *reinterpret_cast<f32x4_t*>(p.dbg + row_off + 4 * i4) = v[c];
@@ -141,17 +171,18 @@ __global__ __launch_bounds__(kRowThreads) void row_norm_kernel(const RowNormPara
   for (int c = 0; c < kMaxC4; ++c) {
     const int i4 = threadIdx.x + c * kRowThreads;
     if (i4 < n4) {
-      const u32x2 gw = *reinterpret_cast<const u32x2*>(p.gain + 4 * i4);
-      const u32x2 o = u32x2{pack_bf2(v[c][0] * inv * __uint_as_float(gw.x << 16),
-                                     v[c][1] * inv * __uint_as_float(gw.x & 0xFFFF0000u)),
-                            pack_bf2(v[c][2] * inv * __uint_as_float(gw.y << 16),
-                                     v[c][3] * inv * __uint_as_float(gw.y & 0xFFFF0000u))};
+      const f32x4_t g = bf4_to_f32(gw[c]);
+      const u32x2 o = u32x2{pack_bf2(v[c][0] * inv * g[0], v[c][1] * inv * g[1]),
+                            pack_bf2(v[c][2] * inv * g[2], v[c][3] * inv * g[3])};
       *reinterpret_cast<u32x2*>(out + 4 * i4) = o;
     }
   }
 }
 
-// Sum over splits of two values per lane (pair i, i + D/2 of one head).
+// Sum over splits of two values per lane (pair i, i + D/2 of one head); src
+// is already clamped to a valid lane. Loads are unconditional (see
+// add_splits); lanes that hold no pair (active false) return zeros, so that
+// wave sums over the head see only its D values.
 __device__ __forceinline__ void sum_pair(const float* src, long long s_stride, int splits, int half,
                                          bool active, float& x1, float& x2) {
   x1 = 0.f;
@@ -160,15 +191,21 @@ __device__ __forceinline__ void sum_pair(const float* src, long long s_stride, i
     float a[kSplitBatch], c[kSplitBatch];
 #pragma unroll
     for (int j = 0; j < kSplitBatch; ++j) {
-      const bool ok = active && s0 + j < splits;
-      a[j] = ok ? src[(long long)(s0 + j) * s_stride] : 0.f;
-      c[j] = ok ? src[(long long)(s0 + j) * s_stride + half] : 0.f;
+      const long long off = (long long)min(s0 + j, splits - 1) * s_stride;
+      a[j] = src[off];
+      c[j] = src[off + half];
     }
 #pragma unroll
     for (int j = 0; j < kSplitBatch; ++j) {
-      x1 += a[j];
-      x2 += c[j];
+      if (s0 + j < splits) {
+        x1 += a[j];
+        x2 += c[j];
+      }
     }
+  }
+  if (!active) {
+    x1 = 0.f;
+    x2 = 0.f;
   }
 }
 
@@ -184,14 +221,23 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
   const int nh = p.Hq + 2 * p.Hkv;
   if (head >= nh) return;
   const int b = m / p.B, j = m % p.B;
-  if (p.status[b] != 0) return;
-  const int pos = p.ctx_len[b] + j;
   const int D = p.D, half = D >> 1;
   const int width = nh * D;
   const bool active = lane < half;
+  const int li = active ? lane : 0;
+  // Every load is issued before the sequence's status is known (the status
+  // only decides whether anything is stored); the RoPE row index is clamped
+  // to the table, and a sequence whose position is out of range has a
+  // capacity status from the embedding kernel.
+  const int st = p.status[b];
+  const int pos = p.ctx_len[b] + j;
   float x1, x2;
-  sum_pair(p.P + (long long)m * width + head * D + (active ? lane : 0), p.p_s_stride, p.splits, half,
-           active, x1, x2);
+  sum_pair(p.P + (long long)m * width + head * D + li, p.p_s_stride, p.splits, half, active, x1, x2);
+  const bf16_t* gain = head < p.Hq ? p.gq : p.gk;
+  const float g1 = bf2f(gain[li]), g2 = bf2f(gain[li + half]);
+  const int rpos = pos < 0 ? 0 : (pos >= p.rope_max ? p.rope_max - 1 : pos);
+  const float2 cs = reinterpret_cast<const float2*>(p.rope)[(long long)rpos * half + li];
+  if (st != 0) return;
   if (head >= p.Hq + p.Hkv) {  // v
     if (active) {
       const int g = head - p.Hq - p.Hkv;
@@ -204,10 +250,8 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
   const float ss = wave_sum(x1 * x1 + x2 * x2);
   const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
   if (!active) return;
-  const bf16_t* gain = head < p.Hq ? p.gq : p.gk;
-  const float y1 = x1 * inv * bf2f(gain[lane]);
-  const float y2 = x2 * inv * bf2f(gain[lane + half]);
-  const float2 cs = reinterpret_cast<const float2*>(p.rope)[(long long)pos * half + lane];
+  const float y1 = x1 * inv * g1;
+  const float y2 = x2 * inv * g2;
   const float o1 = y1 * cs.x - y2 * cs.y;
   const float o2 = y1 * cs.y + y2 * cs.x;
   bf16_t* dst;
@@ -224,58 +268,78 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
 // ---------------------------------------------------------------------------
 // KV injection epilogue: for commit row i and layer l, k = RoPE(RMSNorm_head(
 // W_k c)), v = W_v c, scattered to (seq, pos); ctx_len[seq] grows to pos + 1.
+// One wave per (commit row, layer, head); the split partials, the commit row
+// and the gains are loaded together, the RoPE row once the position is known.
 __global__ __launch_bounds__(256) void inject_post_kernel(const InjectPostParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = p.c0 + blockIdx.x, l = blockIdx.y;
-  int nc = *p.n_commit;
-  nc = nc < 0 ? 0 : (nc > p.max_commit ? p.max_commit : nc);
-  if (i >= nc || i >= p.c1) return;
-  const int src = p.commit_rows[3 * i], seq = p.commit_rows[3 * i + 1], pos = p.commit_rows[3 * i + 2];
-  if (src < 0 || src >= p.n_ctx_rows || seq < 0 || seq >= p.batch) return;
-  if (pos < 0 || pos >= p.max_ctx || pos >= p.rope_max) {
-    if (l == 0 && threadIdx.x == 0) p.status[seq] = kErrCapacity;
-    return;
-  }
+  const int head = blockIdx.z * 4 + wave;
+  if (head >= 2 * p.Hkv) return;
   const int D = p.D, half = D >> 1;
   const int width = 2 * p.Hkv * D;
   const bool active = lane < half;
-  for (int head = wave; head < 2 * p.Hkv; head += 4) {
-    float x1, x2;
-    sum_pair(p.P + (long long)l * p.p_z_stride + (long long)(i - p.c0) * width + head * D + (active ? lane : 0),
-             p.p_s_stride, p.splits, half, active, x1, x2);
-    const int g = head < p.Hkv ? head : head - p.Hkv;
-    const long long off = ((((long long)l * p.batch + seq) * p.Hkv + g) * p.max_ctx + pos) * D;
-    if (head >= p.Hkv) {
-      if (active) {
-        p.vc[off + lane] = f2bf(x1);
-        p.vc[off + lane + half] = f2bf(x2);
-      }
-      continue;
+  const int li = active ? lane : 0;
+  int nc = *p.n_commit;
+  const int src = p.commit_rows[3 * i], seq = p.commit_rows[3 * i + 1], pos = p.commit_rows[3 * i + 2];
+  float x1, x2;
+  sum_pair(p.P + (long long)l * p.p_z_stride + (long long)(i - p.c0) * width + head * D + li, p.p_s_stride,
+           p.splits, half, active, x1, x2);
+  const float g1 = bf2f(p.gk[l][li]), g2 = bf2f(p.gk[l][li + half]);
+  const int rpos = pos < 0 ? 0 : (pos >= p.rope_max ? p.rope_max - 1 : pos);
+  const float2 cs = reinterpret_cast<const float2*>(p.rope)[(long long)rpos * half + li];
+  nc = nc < 0 ? 0 : (nc > p.max_commit ? p.max_commit : nc);
+  if (i >= nc || i >= p.c1) return;
+  if (src < 0 || src >= p.n_ctx_rows || seq < 0 || seq >= p.batch) return;
+  const bool first = l == 0 && blockIdx.z == 0 && threadIdx.x == 0;
+  if (pos < 0 || pos >= p.max_ctx || pos >= p.rope_max) {
+    if (first) p.status[seq] = kErrCapacity;
+    return;
+  }
+  const int g = head < p.Hkv ? head : head - p.Hkv;
+  const long long off = ((((long long)l * p.batch + seq) * p.Hkv + g) * p.max_ctx + pos) * D;
+  if (head >= p.Hkv) {
+    if (active) {
+      p.vc[off + lane] = f2bf(x1);
+      p.vc[off + lane + half] = f2bf(x2);
     }
+  } else {
     const float ss = wave_sum(x1 * x1 + x2 * x2);
     const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
     if (active) {
-      const float y1 = x1 * inv * bf2f(p.gk[l][lane]);
-      const float y2 = x2 * inv * bf2f(p.gk[l][lane + half]);
-      const float2 cs = reinterpret_cast<const float2*>(p.rope)[(long long)pos * half + lane];
+      const float y1 = x1 * inv * g1;
+      const float y2 = x2 * inv * g2;
       p.kc[off + lane] = f2bf(y1 * cs.x - y2 * cs.y);
       p.kc[off + lane + half] = f2bf(y1 * cs.y + y2 * cs.x);
     }
   }
-  if (l == 0 && threadIdx.x == 0) atomicMax(p.ctx_len + seq, pos + 1);
+  if (first) atomicMax(p.ctx_len + seq, pos + 1);
 }
 
 // ---------------------------------------------------------------------------
 // draft token of one LM row: the maximum key over the LM-head tiles (largest
-// logit, lowest index on ties), unpacked to the index.
-__global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long long* keys, int n_tiles,
-                                                            const int32_t* status, int batch, int B,
-                                                            int32_t* draft) {
-  __shared__ unsigned long long red[4];
+// logit, lowest index on ties), unpacked to the index. keys[row][tile]; 1024
+// threads with kFinishBatch loads in flight each cover 8192 tiles per round
+// trip.
+constexpr int kFinishThreads = 1024;
+constexpr int kFinishBatch = 8;
+
+__global__ __launch_bounds__(kFinishThreads) void argmax_finish_kernel(const unsigned long long* keys,
+                                                                       int n_tiles, const int32_t* status,
+                                                                       int batch, int B, int32_t* draft) {
+  __shared__ unsigned long long red[kFinishThreads / 64];
   const int row = blockIdx.x;
-  const int rows = batch * (B - 1);
+  const unsigned long long* kr = keys + (long long)row * n_tiles;
   unsigned long long best = 0ull;
-  for (int t = threadIdx.x; t < n_tiles; t += 256) best = max(best, keys[(long long)t * rows + row]);
+  for (int t0 = threadIdx.x; t0 < n_tiles; t0 += kFinishThreads * kFinishBatch) {
+    unsigned long long k[kFinishBatch];
+#pragma unroll
+    for (int u = 0; u < kFinishBatch; ++u) {
+      const int t = t0 + u * kFinishThreads;
+      k[u] = t < n_tiles ? kr[t] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kFinishBatch; ++u) best = max(best, k[u]);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const unsigned long long other = __shfl_xor(best, o);
@@ -285,7 +349,9 @@ __global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long 
   if (lane == 0) red[wave] = best;
   __syncthreads();
   if (threadIdx.x == 0) {
-    best = max(max(red[0], red[1]), max(red[2], red[3]));
+#pragma unroll
+    for (int w = 1; w < kFinishThreads / 64; ++w) best = max(best, red[w]);
+    best = max(best, red[0]);
     const int b = row / (B - 1);
     draft[row] = status[b] != 0 ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
   }
@@ -300,7 +366,7 @@ hipError_t launch_embed(const EmbedParams& p, hipStream_t st) {
 }
 
 hipError_t launch_row_norm(const RowNormParams& p, hipStream_t st) {
-  if (p.n > kRowThreads * 4 * kMaxC4 || p.n % 4) return hipErrorInvalidValue;
+  if (p.n > kRowThreads * 4 * kMaxC4 || p.n % 4 || !p.P || p.splits < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(row_norm_kernel, dim3(p.rows), dim3(kRowThreads), 0, st, p);
   return hipGetLastError();
 }
@@ -313,14 +379,14 @@ hipError_t launch_qkv_post(const QkvPostParams& p, hipStream_t st) {
 
 hipError_t launch_inject_post(const InjectPostParams& p, hipStream_t st) {
   if (p.c1 <= p.c0) return hipSuccess;
-  hipLaunchKernelGGL(inject_post_kernel, dim3(p.c1 - p.c0, p.n_layers), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(inject_post_kernel, dim3(p.c1 - p.c0, p.n_layers, (2 * p.Hkv + 3) / 4), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_argmax_finish(const unsigned long long* keys, int n_tiles, const int32_t* status,
                                 int batch, int B, int32_t* draft, hipStream_t st) {
-  hipLaunchKernelGGL(argmax_finish_kernel, dim3(batch * (B - 1)), dim3(256), 0, st, keys, n_tiles, status,
-                     batch, B, draft);
+  hipLaunchKernelGGL(argmax_finish_kernel, dim3(batch * (B - 1)), dim3(kFinishThreads), 0, st, keys, n_tiles,
+                     status, batch, B, draft);
   return hipGetLastError();
 }
 
