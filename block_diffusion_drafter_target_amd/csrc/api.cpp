@@ -56,36 +56,56 @@ struct Scope {
 
 constexpr int kMaxBatch = 4096;
 constexpr int kRowChunk = 4096;  // rows per fuse / inject GEMM pass
-constexpr int kGemmRows = 64;    // rows per weight-streaming GEMM launch
+constexpr int kGemmRows = 64;    // rows per weight-streaming GEMM launch (at most)
 constexpr int kTargetWGs = 768;  // workgroups a split-K GEMM launch aims for
 
 inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct GemmPlan {
-  bool tiled;  // LDS-tiled kernel over all rows (M > kGemmRows) or streaming kernel per 64 rows
-  int mt, nf, splits, k_per_split;
+  bool tiled;  // LDS-tiled kernel over all rows, or the streaming kernel per kGemmRows rows
+  int mt, nf;  // streaming: activation tiles and weight fragments per workgroup
+  int ng;      // tiled: weight row groups per wave (64*ng columns per workgroup); mt: 16-row tiles
+  int splits, k_per_split;
+  bool swiglu_split;  // SwiGLU as split-K partials over [gate; up] plus a combine pass
 };
 
-constexpr int kTileTargetWGs = 512;  // workgroups a split-K tiled launch aims for
+constexpr int kStreamMaxRows = 32;   // more rows take the tiled kernel
+constexpr int kSwigluMinWGs = 128;   // fewer single-pass SwiGLU workgroups: split-K path
 
 // Kernel, tile shape and split-K for Y = A W^T.
-// Up to kGemmRows rows (or K < 128): the weight-streaming kernel with NF = 2 weight
-// fragments per workgroup (measured best on MI355X with cold caches: more
-// waves in flight beat wider tiles); split-K only in partial mode, to bring
-// the grid to about kTargetWGs workgroups. More rows: the tiled kernel
-// (activations shared through LDS).
+// Up to kStreamMaxRows rows (or K < 128): the weight-streaming kernel with
+// NF = 2 weight fragments per workgroup (measured best on MI355X with cold
+// caches: more waves in flight beat wider tiles); split-K only in partial
+// mode, to bring the grid to about kTargetWGs workgroups. More rows: the
+// tiled kernel (activations shared through LDS) with 64 or 128 activation
+// rows per tile. Its split-K partials cost 2*splits*M/K bytes per weight
+// byte: with one row tile (HBM-bound) splits aim for 256 workgroups, and
+// 64-row tiles use 64-column tiles so that fewer splits fill the grid; with
+// several row tiles (MFMA-bound) they aim for 512, two per CU (all measured
+// on MI355X against the alternatives). A SwiGLU pass whose single-split grid
+// would be too small to stream the weights runs as a partial-mode GEMM over
+// the concatenated gate and up rows and a combine pass.
 GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
   GemmPlan g;
-  if (M > kGemmRows && K >= 128) {
+  g.swiglu_split = false;
+  if (M > kStreamMaxRows && K >= 128) {
     g.tiled = true;
-    g.mt = g.nf = 0;
-    const long long n_tiles = mode == dfl::kGemmSwiglu ? cdiv(N, 64) : cdiv(N, 128);
-    const long long base = n_tiles * cdiv(M, 128) * nz;
+    g.nf = 0;
+    g.mt = M <= 64 ? 4 : 8;
+    const long long m_tiles = cdiv(M, 16 * g.mt);
+    if (mode == dfl::kGemmSwiglu && cdiv(N, 64) * m_tiles * nz < kSwigluMinWGs) {
+      GemmPlan p = plan_gemm(M, 2 * N, K, nz, dfl::kGemmPartial);
+      p.swiglu_split = true;
+      return p;
+    }
+    g.ng = (mode == dfl::kGemmPartial && g.mt == 4) ? 1 : 2;
+    const long long n_tiles = mode == dfl::kGemmSwiglu ? cdiv(N, 64) : cdiv(N, 64 * g.ng);
+    const long long base = n_tiles * m_tiles * nz;
     const int slabs = (int)cdiv(K, 128);
     int s = 1;
     if (mode == dfl::kGemmPartial) {
-      s = (int)std::max<long long>(1, cdiv(kTileTargetWGs, base));
+      s = (int)std::max<long long>(1, cdiv(m_tiles > 1 ? 512 : 256, base));  // see above
       s = std::min(s, std::max(1, slabs / 2));  // at least two 128-k slabs per split
     }
     const int per = (int)cdiv(slabs, s);
@@ -94,9 +114,15 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
     return g;
   }
   g.tiled = false;
+  g.ng = 0;
   const int rows = std::min(M, kGemmRows);
   g.mt = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
   g.nf = 2;
+  if (mode == dfl::kGemmSwiglu && cdiv(N, 16) * nz < kSwigluMinWGs) {
+    GemmPlan p = plan_gemm(M, 2 * N, K, nz, dfl::kGemmPartial);
+    p.swiglu_split = true;
+    return p;
+  }
   const int out_frags = mode == dfl::kGemmSwiglu ? g.nf / 2 : g.nf;
   const long long tiles = cdiv(N, 16 * out_frags) * nz;
   const int kblocks = (int)cdiv(K, 128);
@@ -115,12 +141,14 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
 // tile and row).
 int lm_tiles(const dflash_config& c, int M) {
   const GemmPlan g = plan_gemm(M, c.vocab, c.hidden, 1, dfl::kGemmArgmax);
-  return (int)(g.tiled ? cdiv(c.vocab, 128) : cdiv(c.vocab, 16 * g.nf));
+  return (int)(g.tiled ? cdiv(c.vocab, 64 * g.ng) : cdiv(c.vocab, 16 * g.nf));
 }
 
-// Partial buffer (floats) that run_gemm needs for M rows.
-size_t gemm_partial_floats(int M, int N, int K, int nz) {
-  const GemmPlan g = plan_gemm(M, N, K, nz, dfl::kGemmPartial);
+// Partial buffer (floats) that run_gemm needs for M rows in the given mode
+// (a split SwiGLU keeps partials of its 2N gate and up columns).
+size_t gemm_partial_floats(int M, int N, int K, int nz, int mode = dfl::kGemmPartial) {
+  const GemmPlan g = plan_gemm(M, N, K, nz, mode);
+  if (mode == dfl::kGemmSwiglu) return g.swiglu_split ? (size_t)nz * g.splits * M * 2 * N : 0;
   return (size_t)nz * g.splits * M * N;
 }
 
@@ -135,8 +163,8 @@ struct GemmCall {
   int n_split = 0;
   int M = 0, N = 0, K = 0, nz = 1;
   int mode = dfl::kGemmPartial;
-  float* P = nullptr;                 // partial mode
-  unsigned long long* keys = nullptr; // argmax mode: [M][ld_keys], one key per column tile
+  float* P = nullptr;                 // partial mode, and SwiGLU when split
+  unsigned long long* keys = nullptr; // argmax mode: [tiles][ld_keys], one key per column tile and row
   long long ld_keys = 0;
   float* dbg = nullptr;
   long long ld_dbg = 0;
@@ -149,6 +177,26 @@ struct GemmCall {
 hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
   const GemmPlan g = plan_gemm(c.M, c.N, c.K, c.nz, c.mode);
   if (splits) *splits = g.splits;
+  if (g.swiglu_split) {
+    // partials of [gate; up] (2N columns), then silu(gate) * up
+    GemmCall pc = c;
+    pc.mode = dfl::kGemmPartial;
+    pc.N = 2 * c.N;
+    pc.n_split = c.N;
+    pc.out = nullptr;
+    int sp = 0;
+    hipError_t e = run_gemm(pc, st, &sp);
+    if (e != hipSuccess) return e;
+    dfl::SwigluCombineParams sc;
+    sc.P = c.P;
+    sc.p_s_stride = (long long)c.M * 2 * c.N;
+    sc.splits = sp;
+    sc.rows = c.M;
+    sc.n = c.N;
+    sc.out = c.out;
+    sc.ld_out = c.ld_out;
+    return dfl::launch_swiglu_combine(sc, st);
+  }
   if (g.tiled) {
     GemmParams p;
     std::memset(&p, 0, sizeof(p));
@@ -177,7 +225,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     p.P = c.P;
     p.p_s_stride = (long long)c.M * c.N;
     p.p_z_stride = (long long)g.splits * c.M * c.N;
-    return dfl::launch_gemm_tile(p, c.mode, c.nz, st);
+    return dfl::launch_gemm_tile(p, g.ng, g.mt, c.mode, c.nz, st);
   }
   for (int m0 = 0; m0 < c.M; m0 += kGemmRows) {
     GemmParams p;
@@ -202,7 +250,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     p.splits = g.splits;
     p.k_per_split = g.k_per_split;
     if (c.mode == dfl::kGemmArgmax) {
-      p.keys = c.keys + (long long)m0 * c.ld_keys;
+      p.keys = c.keys + m0;
       p.ld_keys = c.ld_keys;
       p.dbg = c.dbg ? c.dbg + (long long)m0 * c.ld_dbg : nullptr;
       p.ld_dbg = c.ld_dbg;
@@ -273,19 +321,30 @@ DraftWs draft_ws(const dflash_config& c, int batch, int max_ctx) {
   pf = std::max(pf, gemm_partial_floats((int)Mb, qkvw, H, 1));
   pf = std::max(pf, gemm_partial_floats((int)Mb, H, qw, 1));
   pf = std::max(pf, gemm_partial_floats((int)Mb, H, c.intermediate, 1));
+  pf = std::max(pf, gemm_partial_floats((int)Mb, c.intermediate, H, 1, dfl::kGemmSwiglu));
   w.P = take(pf * 4);
   w.total = off;
   return w;
 }
 
+// Partial buffer of a fuse or inject call of up to `rows` rows, processed in
+// chunks of kRowChunk rows. The split count depends on the chunk's row count
+// and a shorter chunk can take more splits, so the buffer covers the largest
+// need over every chunk size a call can produce (a full chunk, or any
+// remainder below it).
+size_t chunked_partial_bytes(int rows, int N, int K, int nz) {
+  size_t worst = 0;
+  const int top = std::min(std::max(rows, 1), kRowChunk);
+  for (int r = 1; r <= top; ++r) worst = std::max(worst, gemm_partial_floats(r, N, K, nz));
+  return align256(worst * 4);
+}
+
 size_t fuse_ws(const dflash_config& c, int rows) {
-  const int r = std::min(rows, kRowChunk);
-  return align256(gemm_partial_floats(r, c.hidden, c.n_tap * c.hidden, 1) * 4);
+  return chunked_partial_bytes(rows, c.hidden, c.n_tap * c.hidden, 1);
 }
 
 size_t inject_ws(const dflash_config& c, int rows) {
-  const int r = std::min(rows, kRowChunk);
-  return align256(gemm_partial_floats(r, 2 * c.n_kv_heads * c.head_dim, c.hidden, c.n_layers) * 4);
+  return chunked_partial_bytes(rows, 2 * c.n_kv_heads * c.head_dim, c.hidden, c.n_layers);
 }
 
 dflash_status hip_status(hipError_t e) { return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP; }
@@ -669,6 +728,7 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     gg.mode = dfl::kGemmSwiglu;
     gg.out = sb;
     gg.ld_out = I;
+    gg.P = P;
     {
       prof::Scope ps(DFLASH_PHASE_GATE_UP, st);
       e = run_gemm(gg, st, nullptr);
@@ -721,7 +781,7 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
   gl.K = H;
   gl.mode = dfl::kGemmArgmax;
   gl.keys = keys;
-  gl.ld_keys = lm_tiles(c, Ml);
+  gl.ld_keys = Ml;
   gl.dbg = dbg_logits;
   gl.ld_dbg = c.vocab;
   {

@@ -272,11 +272,12 @@ void attn_kernel(const AttnParams p) {
 // o[m][h] = sum_c exp2(m_c - M) O_c / sum_c exp2(m_c - M) l_c over the chunks
 // that hold keys of the sequence. One wave per (row, head); lane c holds
 // chunk c's statistics, lane d output elements d and d + 64. The statistics
-// and the first kMergeBatch chunks' partial outputs are loaded in one round
-// trip; the weights are applied once the wave's maximum is known.
-constexpr int kMergeBatch = 32;
-
+// and the first NB chunks' partial outputs are loaded in one round trip (NB
+// covers the plan's chunk count up to 32); the weights are applied once the
+// wave's maximum is known.
+template <int NB>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
+  constexpr int kMergeBatch = NB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = blockIdx.y;
   const int h = blockIdx.x * 4 + wave;
@@ -375,7 +376,15 @@ hipError_t launch_attention(const AttnParams& p, int D, hipStream_t st) {
 
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t st) {
   if (p.n_chunks < 1 || p.n_chunks > 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3((p.Hq + 3) / 4, p.batch * p.B), dim3(256), 0, st, p);
+  const dim3 grid((p.Hq + 3) / 4, p.batch * p.B);
+  if (p.n_chunks <= 4)
+    hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(256), 0, st, p);
+  else if (p.n_chunks <= 8)
+    hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(256), 0, st, p);
+  else if (p.n_chunks <= 16)
+    hipLaunchKernelGGL(merge_kernel<16>, grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(merge_kernel<32>, grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@
 //     grid z batches independent weight matrices;
 //   * argmax mode (one split) reduces each row's logits over the workgroup's
 //     columns to a packed (value, index) key and writes one key per row and
-//     workgroup, keys[row][tile] (no atomics: 15 rows would serialize
+//     workgroup, keys[tile][row] (no atomics: 15 rows would serialize
 //     thousands of atomics);
 //     logits are never written unless a debug buffer is given;
 //   * swiglu mode (one split) pairs gate rows (W0) and up rows (W1) of the same
@@ -185,7 +185,7 @@ void gemm_stream_kernel(const GemmParams p) {
       unsigned long long best = kbest[0][m];
 #pragma unroll
       for (int f = 1; f < kOutFrags; ++f) best = max(best, kbest[f][m]);
-      p.keys[(long long)m * p.ld_keys + blockIdx.x] = best;
+      p.keys[(long long)blockIdx.x * p.ld_keys + m] = best;
     }
   }
 }

@@ -1,23 +1,25 @@
-// Tiled bf16 MFMA GEMM for more activation rows (64 < M), gfx950.
+// Tiled bf16 MFMA GEMM for more activation rows (32 < M), gfx950.
 //
 // Y[m][n] = sum_k A[m][k] * W[n][k] with W in the packed fragment layout and A
 // row-major (optionally gathered rows). Up to a few hundred rows the product is
 // still bound by streaming W from HBM, so W takes the streaming kernel's path
 // and only the activations are shared through LDS:
-//   * workgroup (4 waves) = 128 weight rows (each wave 2 fragment groups of 16
-//     rows) x 128 activation rows (8 MFMA tiles per wave) x the split's k range;
+//   * workgroup (4 waves) = 64*NG weight rows (each wave NG fragment groups of
+//     16 rows) x 16*MT activation rows (MT MFMA tiles per wave) x the split's k
+//     range (NG = 1 halves the column tile, so fewer K splits, and their fp32
+//     partials, fill the chip);
 //   * each wave loads its weight fragments straight into MFMA operand
 //     registers with non-temporal 16-byte loads (one fully used 1 KB line per
 //     operand), 128 k per slab, one slab ahead of the MFMAs;
-//   * the 128 x 128 activation slab (32 KB) is loaded by all threads, stored to
-//     LDS with the 16-byte chunk index XOR (row & 7), double buffered; each
-//     wave reads all 8 activation tiles from it (64 MFMAs per 8 weight loads);
+//   * the 16*MT x 128 activation slab is loaded by all threads, stored to LDS
+//     with the 16-byte chunk index XOR (row & 7), double buffered; each wave
+//     reads all MT activation tiles from it (MT MFMAs per weight load);
 //   * a grid column of row tiles shares its weights through L2 when the
 //     column count is a multiple of the 8 XCDs (consecutive block ids go to
 //     consecutive XCDs);
 //   * epilogues as in the streaming kernel: split partials, SwiGLU (a wave's
 //     two groups are the gate and up rows of 16 output columns) and one
-//     argmax key per (128-column tile, row).
+//     argmax key per (column tile, row).
 #include "common.h"
 #include "internal.h"
 
@@ -25,17 +27,30 @@ namespace dfl {
 
 namespace {
 
-constexpr int kBN = 128;  // weight rows per workgroup (4 waves x 2 groups x 16)
-constexpr int kBM = 128;  // activation rows per workgroup (8 MFMA tiles)
 constexpr int kBK = 128;  // k per slab (4 MFMA steps)
-constexpr int kMT = kBM / 16;
-constexpr int kXWords = kBM * kBK / 8;  // 16-byte words per activation slab (2048)
 
-template <int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NG weight row groups (16 rows each) per wave, MT activation tiles (16 rows
+// each) per workgroup: the workgroup covers 64*NG weight rows and 16*MT
+// activation rows.
+template <int NG, int MT>
+struct TileShape {
+  static constexpr int kBN = 64 * NG;
+  static constexpr int kBM = 16 * MT;
+  static constexpr int kXWords = kBM * kBK / 8;  // 16-byte words per activation slab
+  static constexpr int kXPer = kXWords / 256;    // words each thread copies
+  // waves per SIMD the registers and LDS allow
+  static constexpr int kWaves = (NG == 2 && MT == 8) ? 2 : (MT == 8 ? 2 : 3);
+};
+
+template <int NG, int MT, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TileShape<NG, MT>::kWaves,
+                                                                      TileShape<NG, MT>::kWaves)))
 void gemm_tile_kernel(const GemmParams p) {
-  __shared__ __align__(16) u32x4 sx[2][kXWords];  // 2 x 32 KB
-  __shared__ unsigned long long kbest[4][kBM];
+  using T = TileShape<NG, MT>;
+  constexpr int kBN = T::kBN, kBM = T::kBM, kXWords = T::kXWords, kXPer = T::kXPer;
+  static_assert(MODE != kGemmSwiglu || NG == 2, "SwiGLU pairs a wave's two groups");
+  __shared__ __align__(16) u32x4 sx[2][kXWords];
+  __shared__ unsigned long long kbest[MODE == kGemmArgmax ? 4 : 1][kBM];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -47,17 +62,17 @@ void gemm_tile_kernel(const GemmParams p) {
   const int kend = min(p.K, kbeg + p.k_per_split);
   const long long frag_row = (long long)(p.K / 32) * 512;
 
-  // this wave's two weight row groups
-  const bf16_t* wrow[2];
+  // this wave's weight row groups
+  const bf16_t* wrow[NG];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < NG; ++f) {
     const bf16_t* base;
     int grp;
     if (MODE == kGemmSwiglu) {  // f = 0: gate rows, f = 1: up rows of the same 16 columns
       grp = min((int)blockIdx.x * 64 + wave * 16, p.N - 16) >> 4;
       base = f == 0 ? p.W0[z] : p.W1[z];
     } else {
-      const int n = min((int)blockIdx.x * kBN + (wave * 2 + f) * 16, p.N - 16);
+      const int n = min((int)blockIdx.x * kBN + (wave * NG + f) * 16, p.N - 16);
       base = n < p.n_split ? p.W0[z] : p.W1[z];
       grp = (n < p.n_split ? n : n - p.n_split) >> 4;
     }
@@ -65,10 +80,10 @@ void gemm_tile_kernel(const GemmParams p) {
   }
   // activation rows this thread copies into LDS: words e = tid + 256*i,
   // row e / 16, chunk e % 16 (all threads share one chunk index)
-  const bf16_t* xsrc[kXWords / 256];
+  const bf16_t* xsrc[kXPer];
   const int xch = (threadIdx.x & 15) * 8;
 #pragma unroll
-  for (int i = 0; i < kXWords / 256; ++i) {
+  for (int i = 0; i < kXPer; ++i) {
     const int e = threadIdx.x + 256 * i;
     int m = min(m0 + (e >> 4), p.M - 1);
     if (p.a_idx) {
@@ -79,35 +94,35 @@ void gemm_tile_kernel(const GemmParams p) {
   }
 
   const int klast = p.K - 32;
-  u32x4 w[2][4], xs[kXWords / 256];
+  u32x4 w[NG][4], xs[kXPer];
   auto load = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int kk = min(k0 + 32 * u, klast);
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < NG; ++f)
         w[f][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[f] + (long long)(kk >> 5) * 512));
     }
     // k past the end (K % 128 == 64 on the last slab) re-reads the row's last
     // chunk; those values are masked where they are used
     const int kx = min(k0 + xch, p.K - 8);
 #pragma unroll
-    for (int i = 0; i < kXWords / 256; ++i) xs[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kx);
+    for (int i = 0; i < kXPer; ++i) xs[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kx);
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kXWords / 256; ++i) {
+    for (int i = 0; i < kXPer; ++i) {
       const int e = threadIdx.x + 256 * i;
       const int row = e >> 4, ch = e & 15;
       sx[buf][row * 16 + (ch ^ (row & 7))] = xs[i];
     }
   };
 
-  f32x4_t acc[2][kMT];
+  f32x4_t acc[NG][MT];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < NG; ++f)
 #pragma unroll
-    for (int t = 0; t < kMT; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < MT; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   int buf = 0;
   if (kbeg < kend) {
@@ -116,9 +131,9 @@ void gemm_tile_kernel(const GemmParams p) {
     __syncthreads();
   }
   for (int k0 = kbeg; k0 < kend; k0 += kBK) {
-    u32x4 wc[2][4];
+    u32x4 wc[NG][4];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < NG; ++f)
 #pragma unroll
       for (int u = 0; u < 4; ++u) wc[f][u] = w[f][u];
     const bool more = k0 + kBK < kend;
@@ -127,11 +142,11 @@ void gemm_tile_kernel(const GemmParams p) {
     for (int u = 0; u < 4; ++u) {
       const uint32_t keep = (k0 + 32 * u < kend) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-      for (int t = 0; t < kMT; ++t) {
+      for (int t = 0; t < MT; ++t) {
         const int row = t * 16 + r;
         const u32x4 b = sx[buf][row * 16 + ((u * 4 + g) ^ (row & 7))] & keep;
-        acc[0][t] = mfma16x16x32(wc[0][u], b, acc[0][t]);
-        acc[1][t] = mfma16x16x32(wc[1][u], b, acc[1][t]);
+#pragma unroll
+        for (int f = 0; f < NG; ++f) acc[f][t] = mfma16x16x32(wc[f][u], b, acc[f][t]);
       }
     }
     if (more) {
@@ -143,37 +158,37 @@ void gemm_tile_kernel(const GemmParams p) {
 
   if (MODE == kGemmPartial) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < NG; ++f)
 #pragma unroll
-      for (int t = 0; t < kMT; ++t) {
+      for (int t = 0; t < MT; ++t) {
         const int m = m0 + t * 16 + r;
-        const int nb = blockIdx.x * kBN + (wave * 2 + f) * 16 + 4 * g;
+        const int nb = blockIdx.x * kBN + (wave * NG + f) * 16 + 4 * g;
         if (m < p.M && nb < p.N)
           *reinterpret_cast<f32x4_t*>(p.P + (long long)z * p.p_z_stride + (long long)s * p.p_s_stride +
                                       (long long)m * p.N + nb) = acc[f][t];
       }
   } else if (MODE == kGemmSwiglu) {
 #pragma unroll
-    for (int t = 0; t < kMT; ++t) {
+    for (int t = 0; t < MT; ++t) {
       const int m = m0 + t * 16 + r;
       const int nb = blockIdx.x * 64 + wave * 16 + 4 * g;
       if (m < p.M && nb < p.N) {
         float sv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[i] = acc[0][t][i] / (1.0f + __expf(-acc[0][t][i])) * acc[1][t][i];
+        for (int i = 0; i < 4; ++i) sv[i] = acc[0][t][i] / (1.0f + __expf(-acc[0][t][i])) * acc[NG - 1][t][i];
         *reinterpret_cast<u32x2*>(p.out + (long long)m * p.ld_out + nb) =
             u32x2{pack_bf2(sv[0], sv[1]), pack_bf2(sv[2], sv[3])};
       }
     }
   } else {
 #pragma unroll
-    for (int t = 0; t < kMT; ++t) {
+    for (int t = 0; t < MT; ++t) {
       const int m = m0 + t * 16 + r;
       float bv = -__builtin_inff();
       int bn = 0x7FFFFFFF;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int nb = blockIdx.x * kBN + (wave * 2 + f) * 16 + 4 * g;
+      for (int f = 0; f < NG; ++f) {
+        const int nb = blockIdx.x * kBN + (wave * NG + f) * 16 + 4 * g;
         if (p.dbg && m < p.M && nb < p.N) *reinterpret_cast<f32x4_t*>(p.dbg + (long long)m * p.ld_dbg + nb) = acc[f][t];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -198,26 +213,41 @@ void gemm_tile_kernel(const GemmParams p) {
     for (int i = threadIdx.x; i < kBM; i += 256) {
       const int m = m0 + i;
       if (m < p.M)
-        p.keys[(long long)m * p.ld_keys + blockIdx.x] =
+        p.keys[(long long)blockIdx.x * p.ld_keys + m] =
             max(max(kbest[0][i], kbest[1][i]), max(kbest[2][i], kbest[3][i]));
     }
   }
 }
 
-}  // namespace
-
-hipError_t launch_gemm_tile(const GemmParams& p, int mode, int nz, hipStream_t st) {
-  if (p.K % 64 || p.K < kBK || p.k_per_split % kBK) return hipErrorInvalidValue;
-  const int m_tiles = (p.M + kBM - 1) / kBM;
-  const int n_tiles = mode == kGemmSwiglu ? (p.N + 63) / 64 : (p.N + kBN - 1) / kBN;
+template <int NG, int MT>
+hipError_t launch_shape(const GemmParams& p, int mode, int nz, hipStream_t st) {
+  using T = TileShape<NG, MT>;
+  const int m_tiles = (p.M + T::kBM - 1) / T::kBM;
+  const int n_tiles = mode == kGemmSwiglu ? (p.N + 63) / 64 : (p.N + T::kBN - 1) / T::kBN;
   dim3 grid(n_tiles, m_tiles * p.splits, nz);
   if (mode == kGemmArgmax)
-    hipLaunchKernelGGL(gemm_tile_kernel<kGemmArgmax>, grid, dim3(256), 0, st, p);
-  else if (mode == kGemmSwiglu)
-    hipLaunchKernelGGL(gemm_tile_kernel<kGemmSwiglu>, grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmArgmax>), grid, dim3(256), 0, st, p);
+  else if (mode == kGemmPartial)
+    hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmPartial>), grid, dim3(256), 0, st, p);
+  else if constexpr (NG == 2)
+    hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmSwiglu>), grid, dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL(gemm_tile_kernel<kGemmPartial>, grid, dim3(256), 0, st, p);
+    return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_tile_cols(int ng) { return 64 * ng; }
+int gemm_tile_rows(int mt) { return 16 * mt; }
+
+hipError_t launch_gemm_tile(const GemmParams& p, int ng, int mt, int mode, int nz, hipStream_t st) {
+  if (p.K % 64 || p.K < kBK || p.k_per_split % kBK) return hipErrorInvalidValue;
+  if (ng == 2 && mt == 8) return launch_shape<2, 8>(p, mode, nz, st);
+  if (ng == 1 && mt == 8) return launch_shape<1, 8>(p, mode, nz, st);
+  if (ng == 2 && mt == 4) return launch_shape<2, 4>(p, mode, nz, st);
+  if (ng == 1 && mt == 4) return launch_shape<1, 4>(p, mode, nz, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dfl

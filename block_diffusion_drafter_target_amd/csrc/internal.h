@@ -55,7 +55,20 @@ hipError_t launch_gemm_stream(const GemmParams& p, int mt, int nf, int mode, int
 // Tiled variant for M > 64 (128 x 128 tiles, one launch over all rows;
 // K >= 128, k_per_split a multiple of 128). Argmax keys: one per 128-column
 // tile.
-hipError_t launch_gemm_tile(const GemmParams& p, int mode, int nz, hipStream_t st);
+// Tiled kernel: ng weight row groups per wave (64*ng columns per workgroup),
+// mt 16-row activation tiles per workgroup; (ng, mt) in {1, 2} x {4, 8}.
+hipError_t launch_gemm_tile(const GemmParams& p, int ng, int mt, int mode, int nz, hipStream_t st);
+
+// out[m][c] = bf16(silu(g) * u), g and u the split sums of P[s][m][c] and
+// P[s][m][n + c] (gate and up partials of a split SwiGLU GEMM).
+struct SwigluCombineParams {
+  const float* P;
+  long long p_s_stride;
+  int splits, rows, n;
+  uint16_t* out;
+  long long ld_out;
+};
+hipError_t launch_swiglu_combine(const SwigluCombineParams& p, hipStream_t st);
 
 struct AttnParams {
   const uint16_t* q;  // [batch*B, Hq, D]

@@ -1,7 +1,8 @@
 // Row-wise kernels of the draft step (gfx950): embedding + RMSNorm, split-K
 // reduction + residual + RMSNorm, per-head q/k RMSNorm + RoPE + KV-cache
 // append, the inject epilogue (k-norm + RoPE + cache scatter + commit
-// of ctx_len), and the final argmax over the LM-head tiles.
+// of ctx_len), the final argmax over the LM-head tiles, and the combine pass
+// of a split SwiGLU.
 //
 // All are bound by a few kilobytes per row; they exist to keep every fp32
 // statistic (RMSNorm sums, residual stream, RoPE) on the device between the
@@ -317,9 +318,9 @@ __global__ __launch_bounds__(256) void inject_post_kernel(const InjectPostParams
 
 // ---------------------------------------------------------------------------
 // draft token of one LM row: the maximum key over the LM-head tiles (largest
-// logit, lowest index on ties), unpacked to the index. keys[row][tile]; 1024
-// threads with kFinishBatch loads in flight each cover 8192 tiles per round
-// trip.
+// logit, lowest index on ties), unpacked to the index. keys[tile][row] (each
+// GEMM workgroup writes its rows contiguously); 1024 threads with
+// kFinishBatch loads in flight each cover 8192 tiles per round trip.
 constexpr int kFinishThreads = 1024;
 constexpr int kFinishBatch = 8;
 
@@ -328,14 +329,14 @@ __global__ __launch_bounds__(kFinishThreads) void argmax_finish_kernel(const uns
                                                                        int batch, int B, int32_t* draft) {
   __shared__ unsigned long long red[kFinishThreads / 64];
   const int row = blockIdx.x;
-  const unsigned long long* kr = keys + (long long)row * n_tiles;
+  const int rows = batch * (B - 1);
   unsigned long long best = 0ull;
   for (int t0 = threadIdx.x; t0 < n_tiles; t0 += kFinishThreads * kFinishBatch) {
     unsigned long long k[kFinishBatch];
 #pragma unroll
     for (int u = 0; u < kFinishBatch; ++u) {
       const int t = t0 + u * kFinishThreads;
-      k[u] = t < n_tiles ? kr[t] : 0ull;
+      k[u] = keys[(long long)min(t, n_tiles - 1) * rows + row];
     }
 #pragma unroll
     for (int u = 0; u < kFinishBatch; ++u) best = max(best, k[u]);
@@ -357,7 +358,47 @@ __global__ __launch_bounds__(kFinishThreads) void argmax_finish_kernel(const uns
   }
 }
 
+// ---------------------------------------------------------------------------
+// split SwiGLU: each thread sums the splits of four gate and four up columns
+// of one row (loads of a batch of splits issued together, clamped), then
+// writes bf16 silu(g) * u.
+__global__ __launch_bounds__(256) void swiglu_combine_kernel(const SwigluCombineParams p) {
+  const int m = blockIdx.y;
+  const int n4 = p.n / 4;
+  const int c4 = blockIdx.x * 256 + threadIdx.x;
+  const int cc = min(c4, n4 - 1);
+  const float* base = p.P + (long long)m * 2 * p.n + 4 * cc;
+  f32x4_t gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < p.splits; s0 += kSplitBatch) {
+    f32x4_t tg[kSplitBatch], tu[kSplitBatch];
+#pragma unroll
+    for (int j = 0; j < kSplitBatch; ++j) {
+      const float* src = base + (long long)min(s0 + j, p.splits - 1) * p.p_s_stride;
+      tg[j] = *reinterpret_cast<const f32x4_t*>(src);
+      tu[j] = *reinterpret_cast<const f32x4_t*>(src + p.n);
+    }
+#pragma unroll
+    for (int j = 0; j < kSplitBatch; ++j)
+      if (s0 + j < p.splits) {
+        gs += tg[j];
+        us += tu[j];
+      }
+  }
+  if (c4 >= n4) return;
+  float sv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sv[i] = gs[i] / (1.0f + __expf(-gs[i])) * us[i];
+  *reinterpret_cast<u32x2*>(p.out + (long long)m * p.ld_out + 4 * c4) =
+      u32x2{pack_bf2(sv[0], sv[1]), pack_bf2(sv[2], sv[3])};
+}
+
 }  // namespace
+
+hipError_t launch_swiglu_combine(const SwigluCombineParams& p, hipStream_t st) {
+  if (p.n % 4 || p.splits < 1 || p.rows < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(swiglu_combine_kernel, dim3((p.n / 4 + 255) / 256, p.rows), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_embed(const EmbedParams& p, hipStream_t st) {
   if (p.H > kRowThreads * 4 * kMaxC4 || p.H % 4) return hipErrorInvalidValue;

@@ -81,6 +81,14 @@ SHAPES = {
     "tiled-b9": synth.DraftConfig(name="tiled-b9", hidden=384, n_layers=2, n_q_heads=12, n_kv_heads=4,
                                   head_dim=64, intermediate=640, vocab=1040, n_tap=2, block=16,
                                   batch=9, ctx_len=0),
+    # wide MLP (I = 8192): single-pass SwiGLU in the tiled kernel at batch 10
+    # (160 rows, two row tiles) and in the streaming kernel at batch 2
+    "mlp-wide": synth.DraftConfig(name="mlp-wide", hidden=256, n_layers=1, n_q_heads=4, n_kv_heads=2,
+                                  head_dim=64, intermediate=8192, vocab=1024, n_tap=2, block=16,
+                                  batch=10, ctx_len=0),
+    "mlp-wide-b2": synth.DraftConfig(name="mlp-wide-b2", hidden=256, n_layers=1, n_q_heads=4, n_kv_heads=2,
+                                     head_dim=64, intermediate=8192, vocab=1024, n_tap=2, block=16,
+                                     batch=2, ctx_len=0),
     # long contexts: 128-key attention slices (chunks of >= 512 keys), G = 8, D = 64
     "long-d64": synth.DraftConfig(name="long-d64", hidden=512, n_layers=1, n_q_heads=64, n_kv_heads=8,
                                   head_dim=64, intermediate=512, vocab=1024, n_tap=2, block=16,
@@ -93,4 +101,5 @@ SHAPES = {
 
 CTX = {"gqa-d128": [1, 300, 777, 0, 64], "g8-d64": [500, 33], "b12": [129, 0, 64],
        "tiled-b9": [17, 260, 0, 64, 1, 333, 90, 128, 2],
-       "long-d64": [8900, 8500, 8193, 100], "long-d128": [16900, 16000, 9000, 3]}
+       "long-d64": [8900, 8500, 8193, 100], "long-d128": [16900, 16000, 9000, 3],
+       "mlp-wide": [40, 0, 17, 300, 64, 1, 129, 90, 33, 7], "mlp-wide-b2": [70, 250]}
