@@ -254,7 +254,11 @@ def main():
     lm_bytes = V * H * 2 + Ml * H * 2 + Ml * 8
     lm_us = 1e3 * lm_ms / max(1, lm_n)
     achieved = lm_bytes / (lm_us * 1e-6) / 1e9
-    roofline = {"kernel": "gemm_stream_kernel<1,2,argmax> (LM head + fused argmax)", "bound": "hbm",
+    # the library streams up to 32 LM rows per workgroup tile; more take the
+    # LDS-tiled kernel (64- or 128-row tiles)
+    lm_kernel = (f"gemm_stream_kernel<{1 if Ml <= 16 else 2},2,argmax>" if Ml <= 32 else
+                 f"gemm_tile_kernel<2,{4 if Ml <= 64 else 8},argmax>")
+    roofline = {"kernel": f"{lm_kernel} (LM head + fused argmax)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "bytes_per_launch": lm_bytes, "us_per_launch": round(lm_us, 2)}
