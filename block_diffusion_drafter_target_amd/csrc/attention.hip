@@ -7,10 +7,11 @@
 // is bound by streaming K/V from HBM; MFMA keeps the arithmetic far below that
 // bound.
 //
-// Decomposition: workgroup (4 waves) = (b, g, key chunk). Each sequence's
-// L_b + B keys are split into at most n_chunks chunks of a multiple of 64 keys,
-// sized on the device from ctx_len, so the work follows the real context
-// rather than the cache capacity; chunks past the end exit at once. The chunk is walked in 64-key slices
+// Decomposition: workgroup (4 waves) = (b, g, key chunk). The chunk length is
+// one for the batch, sized on the device from the longest sequence's
+// L_b + B keys, so the work follows the real context rather than the cache
+// capacity and a ragged batch stays balanced; chunks past a sequence's end
+// exit at once. The chunk is walked in 64- or 128-key slices
 // staged through LDS (K row-major with a 16-byte XOR swizzle, V transposed),
 // the next slice's global loads issued before the current slice's math.
 // Wave w owns query tiles w, w+4, ... (16 query rows each).
@@ -28,10 +29,17 @@ namespace dfl {
 
 namespace {
 
-// Keys per chunk of a sequence with Lk keys split n_chunks ways, a multiple of
-// the slice length.
-__device__ __forceinline__ int chunk_len(int Lk, int n_chunks, int slice) {
-  const int c = (Lk + n_chunks - 1) / n_chunks;
+// Keys per chunk: one length for the whole batch, the longest sequence's keys
+// split n_chunks ways and rounded up to whole slices. A shorter sequence uses
+// fewer chunks, so no workgroup holds more than one chunk of keys however
+// ragged the batch is.
+__device__ __forceinline__ int chunk_len(const int32_t* ctx_len, int batch, int B, int n_chunks, int slice) {
+  if (n_chunks == 1) return 0x7FFFFFFF;
+  int lmax = 0;
+  for (int i = threadIdx.x & 63; i < batch; i += 64) lmax = max(lmax, ctx_len[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lmax = max(lmax, __shfl_xor(lmax, o));
+  const int c = (max(lmax, 0) + B + n_chunks - 1) / n_chunks;
   return max(slice, (c + slice - 1) / slice * slice);
 }
 
@@ -45,8 +53,9 @@ struct Slice {
   static constexpr int VT = SL + 4;  // bf16 per transposed V row (8-byte pad)
 };
 
-// Global -> registers: the K and V rows of keys [k0, k0 + 64), clamped to the
-// last valid key (clamped rows are masked out of the softmax).
+// Global -> registers: the K and V rows of keys [k0, k0 + SL), clamped to the
+// last valid key (clamped rows are masked out of the softmax). K/V are read
+// once per step, so the loads are non-temporal.
 template <int D, int SL>
 __device__ __forceinline__ void load_slice(u32x4 (&kreg)[(Slice<D, SL>::KL)], u32x4 (&va)[(Slice<D, SL>::VL)],
                                            u32x4 (&vb)[(Slice<D, SL>::VL)], const bf16_t* kc,
@@ -57,15 +66,15 @@ __device__ __forceinline__ void load_slice(u32x4 (&kreg)[(Slice<D, SL>::KL)], u3
     const int e = threadIdx.x + t * 256;
     const int key = e / DC, ch = e % DC;
     const int kidx = min(k0 + key, k_end - 1);
-    kreg[t] = *reinterpret_cast<const u32x4*>(kc + (long long)kidx * D + ch * 8);
+    kreg[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + (long long)kidx * D + ch * 8));
   }
 #pragma unroll
   for (int t = 0; t < Slice<D, SL>::VL; ++t) {
     const int e = threadIdx.x + t * 256;
     const int kp = e / DC, ch = e % DC;
     const int k0i = min(k0 + 2 * kp, k_end - 1), k1i = min(k0 + 2 * kp + 1, k_end - 1);
-    va[t] = *reinterpret_cast<const u32x4*>(vc + (long long)k0i * D + ch * 8);
-    vb[t] = *reinterpret_cast<const u32x4*>(vc + (long long)k1i * D + ch * 8);
+    va[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + (long long)k0i * D + ch * 8));
+    vb[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + (long long)k1i * D + ch * 8));
   }
 }
 
@@ -123,10 +132,10 @@ void attn_kernel(const AttnParams p) {
   const int b = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
   if (p.status[b] != 0) return;
   const int Lk = p.ctx_len[b] + p.B;
-  const int chunk = chunk_len(Lk, p.n_chunks, SL);
+  const int chunk = chunk_len(p.ctx_len, p.batch, p.B, p.n_chunks, SL);
   const int k_start = c * chunk;
   if (k_start >= Lk) return;
-  const int k_end = min(Lk, k_start + chunk);
+  const int k_end = (int)min((long long)Lk, (long long)k_start + chunk);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, gq = lane >> 4;
@@ -288,8 +297,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const int G = p.Hq / p.Hkv;
   const int g = h / G, rr = (h % G) * p.B + j;
   const int Lk = p.ctx_len[b] + p.B;
-  const int cl = chunk_len(Lk, p.n_chunks, p.slice);
-  const int nch = max(0, min(p.n_chunks, (Lk + cl - 1) / cl));
+  const int cl = chunk_len(p.ctx_len, p.batch, p.B, p.n_chunks, p.slice);
+  const int nch = max(0, min(p.n_chunks, (int)(((long long)Lk + cl - 1) / cl)));
   const long long base = ((long long)b * p.Hkv + g) * p.n_chunks;
   const bool two = p.D > 64;
   // Loads are unconditional at clamped chunk indexes: a guarded load becomes a
