@@ -215,6 +215,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     p.N = c.N;
     p.K = c.K;
     p.splits = g.splits;
+    p.n_mats = c.nz;
     p.k_per_split = g.k_per_split;
     p.keys = c.keys;
     p.ld_keys = c.ld_keys;
@@ -248,6 +249,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     p.N = c.N;
     p.K = c.K;
     p.splits = g.splits;
+    p.n_mats = c.nz;
     p.k_per_split = g.k_per_split;
     if (c.mode == dfl::kGemmArgmax) {
       p.keys = c.keys + m0;

@@ -14,9 +14,9 @@
 //   * the 16*MT x 128 activation slab is loaded by all threads, stored to LDS
 //     with the 16-byte chunk index XOR (row & 7), double buffered; each wave
 //     reads all MT activation tiles from it (MT MFMAs per weight load);
-//   * a grid column of row tiles shares its weights through L2 when the
-//     column count is a multiple of the 8 XCDs (consecutive block ids go to
-//     consecutive XCDs);
+//   * the row tiles of one weight tile are consecutive workgroups of one XCD
+//     (block ids go round-robin to the 8 XCDs), so they run together and
+//     share the weights through that XCD's L2 and the Infinity Cache;
 //   * epilogues as in the streaming kernel: split partials, SwiGLU (a wave's
 //     two groups are the gate and up rows of 16 output columns) and one
 //     argmax key per (column tile, row).
@@ -42,7 +42,10 @@ struct TileShape {
   static constexpr int kWaves = (NG == 2 && MT == 8) ? 2 : (MT == 8 ? 2 : 3);
 };
 
-template <int NG, int MT, int MODE>
+// SHARED: several row tiles read each weight tile, so weights take plain
+// loads and stay in L2 for the sibling workgroups; otherwise they are read
+// once and loaded non-temporally (both measured best in their case).
+template <int NG, int MT, int MODE, bool SHARED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TileShape<NG, MT>::kWaves,
                                                                       TileShape<NG, MT>::kWaves)))
 void gemm_tile_kernel(const GemmParams p) {
@@ -54,9 +57,18 @@ void gemm_tile_kernel(const GemmParams p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int z = blockIdx.z;
+  // XCD-aware tile order: workgroup l runs on XCD l % 8, the XCD's own
+  // sequence number is l / 8. The row tiles that share a weight tile (one
+  // "column": column tile, split, matrix) are consecutive on one XCD, so they
+  // run together and the weights come from HBM once.
   const int m_tiles = (p.M + kBM - 1) / kBM;
-  const int mt = blockIdx.y % m_tiles, s = blockIdx.y / m_tiles;
+  const int n_tiles = MODE == kGemmSwiglu ? (p.N + 63) / 64 : (p.N + kBN - 1) / kBN;
+  const int xseq = blockIdx.x >> 3;
+  const int mt = xseq % m_tiles;
+  const int col = (xseq / m_tiles) * 8 + (blockIdx.x & 7);
+  if (col >= n_tiles * p.splits * p.n_mats) return;
+  const int bx = col % n_tiles;
+  const int s = (col / n_tiles) % p.splits, z = col / (n_tiles * p.splits);
   const int m0 = mt * kBM;
   const int kbeg = s * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
@@ -69,10 +81,10 @@ void gemm_tile_kernel(const GemmParams p) {
     const bf16_t* base;
     int grp;
     if (MODE == kGemmSwiglu) {  // f = 0: gate rows, f = 1: up rows of the same 16 columns
-      grp = min((int)blockIdx.x * 64 + wave * 16, p.N - 16) >> 4;
+      grp = min(bx * 64 + wave * 16, p.N - 16) >> 4;
       base = f == 0 ? p.W0[z] : p.W1[z];
     } else {
-      const int n = min((int)blockIdx.x * kBN + (wave * NG + f) * 16, p.N - 16);
+      const int n = min(bx * kBN + (wave * NG + f) * 16, p.N - 16);
       base = n < p.n_split ? p.W0[z] : p.W1[z];
       grp = (n < p.n_split ? n : n - p.n_split) >> 4;
     }
@@ -101,7 +113,8 @@ void gemm_tile_kernel(const GemmParams p) {
       const int kk = min(k0 + 32 * u, klast);
 #pragma unroll
       for (int f = 0; f < NG; ++f)
-        w[f][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[f] + (long long)(kk >> 5) * 512));
+        w[f][u] = SHARED ? *reinterpret_cast<const u32x4*>(wrow[f] + (long long)(kk >> 5) * 512)
+                         : __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[f] + (long long)(kk >> 5) * 512));
     }
     // k past the end (K % 128 == 64 on the last slab) re-reads the row's last
     // chunk; those values are masked where they are used
@@ -162,7 +175,7 @@ void gemm_tile_kernel(const GemmParams p) {
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const int m = m0 + t * 16 + r;
-        const int nb = blockIdx.x * kBN + (wave * NG + f) * 16 + 4 * g;
+        const int nb = bx * kBN + (wave * NG + f) * 16 + 4 * g;
         if (m < p.M && nb < p.N)
           *reinterpret_cast<f32x4_t*>(p.P + (long long)z * p.p_z_stride + (long long)s * p.p_s_stride +
                                       (long long)m * p.N + nb) = acc[f][t];
@@ -171,7 +184,7 @@ void gemm_tile_kernel(const GemmParams p) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int m = m0 + t * 16 + r;
-      const int nb = blockIdx.x * 64 + wave * 16 + 4 * g;
+      const int nb = bx * 64 + wave * 16 + 4 * g;
       if (m < p.M && nb < p.N) {
         float sv[4];
 #pragma unroll
@@ -188,7 +201,7 @@ void gemm_tile_kernel(const GemmParams p) {
       int bn = 0x7FFFFFFF;
 #pragma unroll
       for (int f = 0; f < NG; ++f) {
-        const int nb = blockIdx.x * kBN + (wave * NG + f) * 16 + 4 * g;
+        const int nb = bx * kBN + (wave * NG + f) * 16 + 4 * g;
         if (p.dbg && m < p.M && nb < p.N) *reinterpret_cast<f32x4_t*>(p.dbg + (long long)m * p.ld_dbg + nb) = acc[f][t];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -213,10 +226,23 @@ void gemm_tile_kernel(const GemmParams p) {
     for (int i = threadIdx.x; i < kBM; i += 256) {
       const int m = m0 + i;
       if (m < p.M)
-        p.keys[(long long)blockIdx.x * p.ld_keys + m] =
+        p.keys[(long long)bx * p.ld_keys + m] =
             max(max(kbest[0][i], kbest[1][i]), max(kbest[2][i], kbest[3][i]));
     }
   }
+}
+
+template <int NG, int MT, bool SHARED>
+hipError_t launch_kind(const GemmParams& p, int mode, dim3 grid, hipStream_t st) {
+  if (mode == kGemmArgmax)
+    hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmArgmax, SHARED>), grid, dim3(256), 0, st, p);
+  else if (mode == kGemmPartial)
+    hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmPartial, SHARED>), grid, dim3(256), 0, st, p);
+  else if constexpr (NG == 2)
+    hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmSwiglu, SHARED>), grid, dim3(256), 0, st, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 template <int NG, int MT>
@@ -224,16 +250,12 @@ hipError_t launch_shape(const GemmParams& p, int mode, int nz, hipStream_t st) {
   using T = TileShape<NG, MT>;
   const int m_tiles = (p.M + T::kBM - 1) / T::kBM;
   const int n_tiles = mode == kGemmSwiglu ? (p.N + 63) / 64 : (p.N + T::kBN - 1) / T::kBN;
-  dim3 grid(n_tiles, m_tiles * p.splits, nz);
-  if (mode == kGemmArgmax)
-    hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmArgmax>), grid, dim3(256), 0, st, p);
-  else if (mode == kGemmPartial)
-    hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmPartial>), grid, dim3(256), 0, st, p);
-  else if constexpr (NG == 2)
-    hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmSwiglu>), grid, dim3(256), 0, st, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (p.n_mats != nz) return hipErrorInvalidValue;
+  // columns rounded up to the 8 XCDs; the padding workgroups exit at once
+  const long long cols8 = ((long long)n_tiles * p.splits * nz + 7) / 8 * 8;
+  if (cols8 * m_tiles > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(cols8 * m_tiles));
+  return m_tiles > 1 ? launch_kind<NG, MT, true>(p, mode, grid, st) : launch_kind<NG, MT, false>(p, mode, grid, st);
 }
 
 }  // namespace

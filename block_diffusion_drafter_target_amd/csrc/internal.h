@@ -29,11 +29,12 @@ struct GemmParams {
   int M, N, K;
   int k_per_split;  // k range of one split (multiple of 128)
   int splits;
+  int n_mats;       // weight matrices batched in one launch (W0[z], W1[z], z < n_mats)
   // partial-sum output: P[z][s][m][n], fp32
   float* P;
   long long p_z_stride, p_s_stride;
   // argmax output (splits == 1): keys[tile * ld_keys + m] = max over the
-  // tile's n of argmax_key(y[m][n], n); tile = blockIdx.x
+  // column tile's n of argmax_key(y[m][n], n)
   unsigned long long* keys;
   long long ld_keys;
   float* dbg;  // optional logits [M, ld_dbg]
