@@ -77,7 +77,9 @@ constexpr int kSwigluMinWGs = 128;   // fewer single-pass SwiGLU workgroups: spl
 // Up to kStreamMaxRows rows (or K < 128): the weight-streaming kernel with
 // NF = 2 weight fragments per workgroup (measured best on MI355X with cold
 // caches: more waves in flight beat wider tiles); split-K only in partial
-// mode, to bring the grid to about kTargetWGs workgroups. More rows: the
+// mode, to bring the grid to about kTargetWGs workgroups (1024 when there are
+// at most 128 column tiles: longer splits per workgroup measured slower
+// there). More rows: the
 // tiled kernel (activations shared through LDS) with 64 or 128 activation
 // rows per tile. Its split-K partials cost 2*splits*M/K bytes per weight
 // byte: with one row tile (HBM-bound) splits aim for 256 workgroups, and
@@ -128,7 +130,7 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
   const int kblocks = (int)cdiv(K, 128);
   int s = 1;
   if (mode == dfl::kGemmPartial) {
-    s = (int)std::max<long long>(1, cdiv(kTargetWGs, tiles));
+    s = (int)std::max<long long>(1, cdiv(tiles <= 128 ? 1024 : kTargetWGs, tiles));
     s = std::min(s, std::max(1, kblocks / 4));  // at least one 128-k block per wave
   }
   const int per = (int)cdiv(kblocks, s);
@@ -275,6 +277,7 @@ struct AttnPlan {
 };
 
 constexpr int kAttnTargetWGs = 512;  // attention workgroups when every sequence is at full length
+constexpr int kAttnMaxChunks = 32;   // per (sequence, kv head): 64 measured slower at batch 1
 
 // Key chunks per (sequence, kv head): about kAttnTargetWGs workgroups (one per
 // CU slot at two per CU) if every sequence were as long as the longest, without
@@ -288,7 +291,7 @@ AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx) {
   const long long units = (long long)batch * c.n_kv_heads;
   long long n = cdiv(kAttnTargetWGs, units);
   n = std::min<long long>(n, cdiv(max_ctx, 64));
-  a.n_chunks = (int)std::max<long long>(1, std::min<long long>(n, 64));
+  a.n_chunks = (int)std::max<long long>(1, std::min<long long>(n, kAttnMaxChunks));
   // 128-key slices keep twice the bytes in flight once chunks are long (not
   // with four 16-query tiles per wave at D = 128: those registers allow 64)
   const bool wide_ok = !(c.head_dim == 128 && a.gb_pad > 128);
