@@ -12,7 +12,8 @@
 // L_b + B keys, so the work follows the real context rather than the cache
 // capacity and a ragged batch stays balanced; chunks past a sequence's end
 // exit at once. The chunk is walked in 64- or 128-key slices
-// staged through LDS (K row-major with a 16-byte XOR swizzle, V transposed),
+// staged through LDS (K row-major with a 16-byte XOR swizzle over the row's
+// chunks, V transposed),
 // the next slice's global loads issued before the current slice's math.
 // Wave w owns query tiles w, w+4, ... (16 query rows each).
 //   S^T = K Q^T    A = K slice rows (LDS), B = Q^T (registers for the chunk)
@@ -85,7 +86,7 @@ __device__ __forceinline__ void store_vpair(bf16_t* vt, int d, int kp, uint32_t 
   *reinterpret_cast<uint32_t*>(vt + (d + 1) * VT + 2 * kp) = (a >> 16) | (b & 0xFFFF0000u);
 }
 
-// Registers -> LDS: K row-major with the 16-byte chunk index XOR (key & 7);
+// Registers -> LDS: K row-major with the 16-byte chunk index XOR (key & (DC-1));
 // V transposed to [d][key] so that a lane reads 4 keys of one d in 8 bytes.
 template <int D, int SL>
 __device__ __forceinline__ void store_slice(u32x4* ks, bf16_t* vt, const u32x4 (&kreg)[(Slice<D, SL>::KL)],
@@ -97,7 +98,7 @@ __device__ __forceinline__ void store_slice(u32x4* ks, bf16_t* vt, const u32x4 (
   for (int t = 0; t < Slice<D, SL>::KL; ++t) {
     const int e = threadIdx.x + t * 256;
     const int key = e / DC, ch = e % DC;
-    ks[key * DC + (ch ^ (key & 7))] = kreg[t];
+    ks[key * DC + (ch ^ (key & (DC - 1)))] = kreg[t];
   }
 #pragma unroll
   for (int t = 0; t < Slice<D, SL>::VL; ++t) {
@@ -193,7 +194,7 @@ void attn_kernel(const AttnParams p) {
       const int key = kt * 16 + r;
 #pragma unroll
       for (int ds = 0; ds < D / 32; ++ds) {
-        const u32x4 a = ks[key * DC + ((ds * 4 + gq) ^ (key & 7))];
+        const u32x4 a = ks[key * DC + ((ds * 4 + gq) ^ (key & (DC - 1)))];
 #pragma unroll
         for (int i = 0; i < QPW; ++i) sacc[i][kt] = mfma16x16x32(a, qreg[i][ds], sacc[i][kt]);
       }

@@ -12,7 +12,8 @@
 //     registers with non-temporal 16-byte loads (one fully used 1 KB line per
 //     operand), 128 k per slab, one slab ahead of the MFMAs;
 //   * the 16*MT x 128 activation slab is loaded by all threads, stored to LDS
-//     with the 16-byte chunk index XOR (row & 7), double buffered; each wave
+//     with the 16-byte chunk index XOR (row & 15) (the 16 lanes of one LDS
+//     cycle hit 16 different bank groups), double buffered; each wave
 //     reads all MT activation tiles from it (MT MFMAs per weight load);
 //   * the row tiles of one weight tile are consecutive workgroups of one XCD
 //     (block ids go round-robin to the 8 XCDs), so they run together and
@@ -127,7 +128,7 @@ void gemm_tile_kernel(const GemmParams p) {
     for (int i = 0; i < kXPer; ++i) {
       const int e = threadIdx.x + 256 * i;
       const int row = e >> 4, ch = e & 15;
-      sx[buf][row * 16 + (ch ^ (row & 7))] = xs[i];
+      sx[buf][row * 16 + (ch ^ (row & 15))] = xs[i];
     }
   };
 
@@ -157,7 +158,7 @@ void gemm_tile_kernel(const GemmParams p) {
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const int row = t * 16 + r;
-        const u32x4 b = sx[buf][row * 16 + ((u * 4 + g) ^ (row & 7))] & keep;
+        const u32x4 b = sx[buf][row * 16 + ((u * 4 + g) ^ (row & 15))] & keep;
 #pragma unroll
         for (int f = 0; f < NG; ++f) acc[f][t] = mfma16x16x32(wc[f][u], b, acc[f][t]);
       }
