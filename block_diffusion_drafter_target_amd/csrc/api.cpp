@@ -71,7 +71,7 @@ struct GemmPlan {
 };
 
 constexpr int kStreamMaxRows = 32;   // more rows take the tiled kernel
-constexpr int kSwigluMinWGs = 128;   // fewer single-pass SwiGLU workgroups: split-K path
+constexpr int kSwigluMinWGs = 256;   // fewer single-pass SwiGLU workgroups: split-K path
 
 // Kernel, tile shape and split-K for Y = A W^T.
 // Up to kStreamMaxRows rows (or K < 128): the weight-streaming kernel with
@@ -82,12 +82,13 @@ constexpr int kSwigluMinWGs = 128;   // fewer single-pass SwiGLU workgroups: spl
 // there). More rows: the
 // tiled kernel (activations shared through LDS) with 64 or 128 activation
 // rows per tile. Its split-K partials cost 2*splits*M/K bytes per weight
-// byte: with one row tile (HBM-bound) splits aim for 256 workgroups, and
-// 64-row tiles use 64-column tiles so that fewer splits fill the grid; with
-// several row tiles (MFMA-bound) they aim for 512, two per CU (all measured
-// on MI355X against the alternatives). A SwiGLU pass whose single-split grid
-// would be too small to stream the weights runs as a partial-mode GEMM over
-// the concatenated gate and up rows and a combine pass.
+// byte: with one row tile (HBM-bound) splits aim for 256 workgroups at 128
+// rows and 384 at 64 rows (64-row tiles also use 64-column tiles), with
+// several row tiles (MFMA-bound) for 512, two per CU (all measured on MI355X
+// against the alternatives). A SwiGLU pass whose single-split grid would have
+// fewer than 256 workgroups runs as a partial-mode GEMM over the concatenated
+// gate and up rows and a combine pass (c4: 2 splits of 128-column tiles,
+// 58 us against 71 us for the 192-workgroup single pass).
 GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
   GemmPlan g;
   g.swiglu_split = false;
@@ -107,7 +108,8 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
     const int slabs = (int)cdiv(K, 128);
     int s = 1;
     if (mode == dfl::kGemmPartial) {
-      s = (int)std::max<long long>(1, cdiv(m_tiles > 1 ? 512 : 256, base));  // see above
+      const int target = m_tiles > 1 ? 512 : (g.mt == 4 ? 384 : 256);  // see above
+      s = (int)std::max<long long>(1, cdiv(target, base));
       s = std::min(s, std::max(1, slabs / 2));  // at least two 128-k slabs per split
     }
     const int per = (int)cdiv(slabs, s);

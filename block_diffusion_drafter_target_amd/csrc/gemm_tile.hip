@@ -40,7 +40,7 @@ struct TileShape {
   static constexpr int kXWords = kBM * kBK / 8;  // 16-byte words per activation slab
   static constexpr int kXPer = kXWords / 256;    // words each thread copies
   // waves per SIMD the registers and LDS allow
-  static constexpr int kWaves = (NG == 2 && MT == 8) ? 2 : (MT == 8 ? 2 : 3);
+  static constexpr int kWaves = (NG == 4 || MT == 8) ? 2 : 3;
 };
 
 // SHARED: several row tiles read each weight tile, so weights take plain
@@ -52,7 +52,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TileShape<N
 void gemm_tile_kernel(const GemmParams p) {
   using T = TileShape<NG, MT>;
   constexpr int kBN = T::kBN, kBM = T::kBM, kXWords = T::kXWords, kXPer = T::kXPer;
-  static_assert(MODE != kGemmSwiglu || NG == 2, "SwiGLU pairs a wave's two groups");
+  static_assert(MODE != kGemmSwiglu || NG % 2 == 0, "SwiGLU pairs gate and up groups");
+  constexpr int kOut = MODE == kGemmSwiglu ? NG / 2 : NG;  // output groups per wave
+  constexpr int kBNo = 64 * kOut;                           // output columns per workgroup
   __shared__ __align__(16) u32x4 sx[2][kXWords];
   __shared__ unsigned long long kbest[MODE == kGemmArgmax ? 4 : 1][kBM];
 
@@ -63,7 +65,7 @@ void gemm_tile_kernel(const GemmParams p) {
   // "column": column tile, split, matrix) are consecutive on one XCD, so they
   // run together and the weights come from HBM once.
   const int m_tiles = (p.M + kBM - 1) / kBM;
-  const int n_tiles = MODE == kGemmSwiglu ? (p.N + 63) / 64 : (p.N + kBN - 1) / kBN;
+  const int n_tiles = (p.N + kBNo - 1) / kBNo;
   const int xseq = blockIdx.x >> 3;
   const int mt = xseq % m_tiles;
   const int col = (xseq / m_tiles) * 8 + (blockIdx.x & 7);
@@ -81,9 +83,10 @@ void gemm_tile_kernel(const GemmParams p) {
   for (int f = 0; f < NG; ++f) {
     const bf16_t* base;
     int grp;
-    if (MODE == kGemmSwiglu) {  // f = 0: gate rows, f = 1: up rows of the same 16 columns
-      grp = min(bx * 64 + wave * 16, p.N - 16) >> 4;
-      base = f == 0 ? p.W0[z] : p.W1[z];
+    if (MODE == kGemmSwiglu) {  // f < NG/2: gate rows, f >= NG/2: up rows of the same 16 columns
+      const int fo = f < kOut ? f : f - kOut;
+      grp = min(bx * kBNo + (wave * kOut + fo) * 16, p.N - 16) >> 4;
+      base = f < kOut ? p.W0[z] : p.W1[z];
     } else {
       const int n = min(bx * kBN + (wave * NG + f) * 16, p.N - 16);
       base = n < p.n_split ? p.W0[z] : p.W1[z];
@@ -183,17 +186,20 @@ void gemm_tile_kernel(const GemmParams p) {
       }
   } else if (MODE == kGemmSwiglu) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int m = m0 + t * 16 + r;
-      const int nb = bx * 64 + wave * 16 + 4 * g;
-      if (m < p.M && nb < p.N) {
-        float sv[4];
+    for (int fo = 0; fo < kOut; ++fo)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[i] = acc[0][t][i] / (1.0f + __expf(-acc[0][t][i])) * acc[NG - 1][t][i];
-        *reinterpret_cast<u32x2*>(p.out + (long long)m * p.ld_out + nb) =
-            u32x2{pack_bf2(sv[0], sv[1]), pack_bf2(sv[2], sv[3])};
+      for (int t = 0; t < MT; ++t) {
+        const int m = m0 + t * 16 + r;
+        const int nb = bx * kBNo + (wave * kOut + fo) * 16 + 4 * g;
+        if (m < p.M && nb < p.N) {
+          float sv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sv[i] = acc[fo][t][i] / (1.0f + __expf(-acc[fo][t][i])) * acc[fo + kOut][t][i];
+          *reinterpret_cast<u32x2*>(p.out + (long long)m * p.ld_out + nb) =
+              u32x2{pack_bf2(sv[0], sv[1]), pack_bf2(sv[2], sv[3])};
+        }
       }
-    }
   } else {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -239,7 +245,7 @@ hipError_t launch_kind(const GemmParams& p, int mode, dim3 grid, hipStream_t st)
     hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmArgmax, SHARED>), grid, dim3(256), 0, st, p);
   else if (mode == kGemmPartial)
     hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmPartial, SHARED>), grid, dim3(256), 0, st, p);
-  else if constexpr (NG == 2)
+  else if constexpr (NG % 2 == 0)
     hipLaunchKernelGGL((gemm_tile_kernel<NG, MT, kGemmSwiglu, SHARED>), grid, dim3(256), 0, st, p);
   else
     return hipErrorInvalidValue;
@@ -250,7 +256,8 @@ template <int NG, int MT>
 hipError_t launch_shape(const GemmParams& p, int mode, int nz, hipStream_t st) {
   using T = TileShape<NG, MT>;
   const int m_tiles = (p.M + T::kBM - 1) / T::kBM;
-  const int n_tiles = mode == kGemmSwiglu ? (p.N + 63) / 64 : (p.N + T::kBN - 1) / T::kBN;
+  const int cols = mode == kGemmSwiglu ? 32 * NG : T::kBN;  // output columns per workgroup
+  const int n_tiles = (p.N + cols - 1) / cols;
   if (p.n_mats != nz) return hipErrorInvalidValue;
   // columns rounded up to the 8 XCDs; the padding workgroups exit at once
   const long long cols8 = ((long long)n_tiles * p.splits * nz + 7) / 8 * 8;
@@ -270,6 +277,7 @@ hipError_t launch_gemm_tile(const GemmParams& p, int ng, int mt, int mode, int n
   if (ng == 1 && mt == 8) return launch_shape<1, 8>(p, mode, nz, st);
   if (ng == 2 && mt == 4) return launch_shape<2, 4>(p, mode, nz, st);
   if (ng == 1 && mt == 4) return launch_shape<1, 4>(p, mode, nz, st);
+  if (ng == 4 && mt == 4) return launch_shape<4, 4>(p, mode, nz, st);
   return hipErrorInvalidValue;
 }
 
