@@ -277,7 +277,6 @@ hipError_t launch_gemm_tile(const GemmParams& p, int ng, int mt, int mode, int n
   if (ng == 1 && mt == 8) return launch_shape<1, 8>(p, mode, nz, st);
   if (ng == 2 && mt == 4) return launch_shape<2, 4>(p, mode, nz, st);
   if (ng == 1 && mt == 4) return launch_shape<1, 4>(p, mode, nz, st);
-  if (ng == 4 && mt == 4) return launch_shape<4, 4>(p, mode, nz, st);
   return hipErrorInvalidValue;
 }
 
