@@ -61,6 +61,63 @@ def synth_target(torch, draft, m, rnd, vocab):
     return torch.where((j == m[:, None]) & (m[:, None] < bm1), (d_ext + 1) % (vocab - 1), t)
 
 
+def target_verify(cfg, W, lens, args):
+    """The target side of a step: one causal pass of the target model over the
+    B block tokens of every sequence (argmax + taps), timed over repeated
+    passes at the workload's context (each pass rewrites the same speculative
+    slots; nothing is committed)."""
+    import torch
+
+    from block_diffusion_drafter_target_amd import DeviceTarget, synth
+    from block_diffusion_drafter_target_amd import binding as bd
+
+    if not cfg.target_layers:
+        raise SystemExit(f"config {cfg.name} has no target model")
+    B, batch, H = cfg.block, cfg.batch, cfg.hidden
+    t0 = time.time()
+    TW = synth.make_target_weights(cfg, W)
+    log(f"target weights ({cfg.target_layers} layers) generated in {time.time() - t0:.1f} s")
+    L = int(lens.max())
+    tgt = DeviceTarget(cfg, TW, cfg.target_layers, cfg.tap_layers, batch=batch, max_ctx=L + 2 * B + 64, max_n=B)
+    del TW
+    # prefill every sequence's context in passes of B tokens (ragged contexts:
+    # a sequence keeps only its own length through the commit of all rows
+    # below it)
+    dev = tgt.device
+    for i0 in range(0, L, B):
+        n = min(B, L - i0)
+        toks = torch.from_numpy(np.stack([synth.make_prompt(cfg, n, seed=1000 + 7 * b + i0)
+                                          for b in range(batch)]).astype(np.int32)).to(dev)
+        tgt.pass_tokens(toks)
+        tgt.ctx_len.copy_(torch.minimum(tgt.ctx_len + n, torch.from_numpy(lens.astype(np.int32)).to(dev)))
+    torch.cuda.synchronize()
+    assert tgt.ctx_len.cpu().numpy().tolist() == lens.tolist()
+    toks = torch.from_numpy(np.stack([synth.make_prompt(cfg, B, seed=5000 + b) for b in range(batch)])
+                            .astype(np.int32)).to(dev)
+    for _ in range(3):
+        tgt.pass_tokens(toks)
+    torch.cuda.synchronize()
+    reps = max(5, min(args.steps, 50))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        tgt.pass_tokens(toks)
+    stop.record()
+    torch.cuda.synchronize()
+    us = 1e3 * start.elapsed_time(stop) / reps
+    assert int(tgt.status.abs().max()) == 0
+    V, I, NLt = cfg.vocab, cfg.intermediate, cfg.target_layers
+    layer_bytes = 2 * H * (cfg.qkv_width + cfg.q_width + 2 * I) + 2 * I * H
+    wbytes = NLt * layer_bytes + V * H * 2
+    res = {"layers": NLt, "taps": list(cfg.tap_layers), "tokens_per_pass": batch * B, "context": L,
+           "us_per_pass": round(us, 1), "weight_bytes": wbytes,
+           "weight_stream_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
+           "weight_stream_frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del tgt
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg, W, L, repeats: int):
     """The fp64 oracle's draft step on the host cores (median of repeats)."""
     from threadpoolctl import threadpool_info
@@ -108,6 +165,8 @@ def main():
     ap.add_argument("--batch", type=int, default=0, help="override the batch")
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--target-verify", action="store_true",
+                    help="also time the target's causal verify pass (Qwen3-8B-shaped 36-layer target)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--graph", action="store_true",
@@ -288,6 +347,10 @@ def main():
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "phases": phases,
     }
+    if args.target_verify:
+        del dr
+        torch.cuda.empty_cache()
+        out["target_verify"] = target_verify(cfg, W, lens, args)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(cfg, W, int(lens.max()), args.cpu_repeats)

@@ -23,7 +23,8 @@ DFLASH_ERR_HIP = -6
 EXPORTED = ("dflash_model_create", "dflash_model_destroy", "dflash_rope_table",
             "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_inject_kv",
             "dflash_draft_block", "dflash_verify_accept", "dflash_status_string",
-            "dflash_profile_enable", "dflash_profile_read", "dflash_pack_matrix")
+            "dflash_profile_enable", "dflash_profile_read", "dflash_pack_matrix",
+            "dflash_target_create", "dflash_target_forward", "dflash_kv_commit")
 
 PHASES = {"lm_head": 0, "attention": 1, "qkv": 2, "o": 3, "gate_up": 4, "down": 5, "fuse": 6,
           "inject": 7, "verify": 8}
@@ -80,6 +81,9 @@ def load() -> C.CDLL:
     lib.dflash_fuse_ctx.argtypes = [vp, vp, i32, vp, vp, sz, vp]
     lib.dflash_inject_kv.argtypes = [vp, vp, i32, vp, vp, i32, C.POINTER(dflash_kv), vp, sz, vp]
     lib.dflash_draft_block.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp, vp, sz, vp]
+    lib.dflash_target_create.argtypes = [C.POINTER(dflash_config), C.POINTER(dflash_weights), vp, C.POINTER(vp)]
+    lib.dflash_target_forward.argtypes = [vp, C.POINTER(dflash_kv), vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.dflash_kv_commit.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, i32, vp]
     lib.dflash_verify_accept.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, i32, vp, vp, vp, vp,
                                          vp, vp, vp, vp, vp]
     lib.dflash_pack_matrix.argtypes = [vp, vp, i32, i32, vp]
@@ -91,7 +95,8 @@ def load() -> C.CDLL:
     lib.dflash_status_string.argtypes = [i32]
     lib.dflash_status_string.restype = C.c_char_p
     for fn in ("dflash_model_create", "dflash_rope_table", "dflash_fuse_ctx", "dflash_inject_kv",
-               "dflash_draft_block", "dflash_verify_accept"):
+               "dflash_draft_block", "dflash_verify_accept", "dflash_target_create",
+               "dflash_target_forward", "dflash_kv_commit"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -124,6 +129,13 @@ def dflash_model_create(cfg: dflash_config, w: dflash_weights) -> int:
     return h.value
 
 
+def dflash_target_create(cfg: dflash_config, w: dflash_weights, tap_layers) -> int:
+    taps = (C.c_int32 * len(tap_layers))(*[int(t) for t in tap_layers])
+    h = C.c_void_p()
+    _check("dflash_target_create", load().dflash_target_create(C.byref(cfg), C.byref(w), taps, C.byref(h)))
+    return h.value
+
+
 def dflash_model_destroy(model: int) -> None:
     load().dflash_model_destroy(model)
 
@@ -149,6 +161,16 @@ def dflash_inject_kv(model, ctx, n_ctx_rows, commit_rows, n_commit, max_commit, 
 def dflash_draft_block(model, kv, anchor, draft, dbg_logits, dbg_hidden, ws, ws_bytes, stream) -> None:
     _check("dflash_draft_block", load().dflash_draft_block(model, C.byref(kv), anchor, draft, dbg_logits,
                                                            dbg_hidden, ws, ws_bytes, stream))
+
+
+def dflash_target_forward(model, kv, tokens, n, argmax, taps, dbg_logits, ws, ws_bytes, stream) -> None:
+    _check("dflash_target_forward", load().dflash_target_forward(model, C.byref(kv), tokens, n, argmax, taps,
+                                                                 dbg_logits, ws, ws_bytes, stream))
+
+
+def dflash_kv_commit(model, kv, commit_rows, n_commit, max_commit, stream) -> None:
+    _check("dflash_kv_commit", load().dflash_kv_commit(model, C.byref(kv), commit_rows, n_commit, max_commit,
+                                                       stream))
 
 
 def dflash_verify_accept(model, kv, draft, target_argmax, stop_ids, n_stop, budget, accept_len,

@@ -17,6 +17,8 @@ struct dflash_model {
   dflash_config cfg;
   dflash_weights w;
   std::vector<dflash_layer_weights> layers;
+  bool target = false;    // a target model (dflash_target_create): causal passes, taps
+  std::vector<int> taps;  // target: tapped layers, increasing
 };
 
 namespace {
@@ -55,6 +57,7 @@ struct Scope {
 }  // namespace prof
 
 constexpr int kMaxBatch = 4096;
+constexpr int kMaxTargetLayers = 256;
 constexpr int kRowChunk = 4096;  // rows per fuse / inject GEMM pass
 constexpr int kGemmRows = 64;    // rows per weight-streaming GEMM launch (at most)
 constexpr int kTargetWGs = 768;  // workgroups a split-K GEMM launch aims for
@@ -286,10 +289,10 @@ constexpr int kAttnMaxChunks = 32;   // per (sequence, kv head): 64 measured slo
 // chunks shorter than 64 keys of the cache. Measured on MI355X: 1024 and 2048
 // were slower at every configuration (more fp32 partials and workgroup starts
 // than the finer balance of a ragged batch wins back).
-AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx) {
+AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx, int B) {
   AttnPlan a;
   const int G = c.n_q_heads / c.n_kv_heads;
-  a.gb_pad = (int)cdiv(G * c.block, 16) * 16;
+  a.gb_pad = (int)cdiv(G * B, 16) * 16;
   const long long units = (long long)batch * c.n_kv_heads;
   long long n = cdiv(kAttnTargetWGs, units);
   n = std::min<long long>(n, cdiv(max_ctx, 64));
@@ -301,17 +304,19 @@ AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx) {
   return a;
 }
 
-// Workspace of dflash_draft_block (bytes, 256-aligned pieces).
-struct DraftWs {
+// Workspace of one pass of the layer stack over B rows per sequence, lm_rows
+// of which reach the LM head (bytes, 256-aligned pieces): a draft block
+// (B = block, lm_rows = B - 1) or a target pass (B = n, lm_rows = n).
+struct StackWs {
   size_t x, u, q, ao, s, ulm, keys, pm, pl, po, P, total;
 };
 
-DraftWs draft_ws(const dflash_config& c, int batch, int max_ctx) {
-  DraftWs w;
-  const long long Mb = (long long)batch * c.block, Ml = (long long)batch * (c.block - 1);
+StackWs stack_ws(const dflash_config& c, int batch, int max_ctx, int B, int lm_rows) {
+  StackWs w;
+  const long long Mb = (long long)batch * B, Ml = (long long)batch * lm_rows;
   const int H = c.hidden, qw = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
-  const AttnPlan a = plan_attn(c, batch, max_ctx);
+  const AttnPlan a = plan_attn(c, batch, max_ctx, B);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -387,27 +392,24 @@ const char* dflash_status_string(dflash_status s) {
   return "unknown status";
 }
 
-dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights* w,
-                                  dflash_model** out) {
-  if (!cfg || !w || !out) return DFLASH_ERR_NULL;
-  *out = nullptr;
-  const dflash_config& c = *cfg;
+namespace {
+
+// Checks shared by drafter and target models.
+dflash_status check_model(const dflash_config& c, const dflash_weights* w, int max_layers) {
   if (c.hidden <= 0 || c.n_layers <= 0 || c.n_q_heads <= 0 || c.n_kv_heads <= 0 ||
       c.head_dim <= 0 || c.intermediate <= 0 || c.vocab <= 1 || c.n_tap <= 0 || c.block <= 0)
     return DFLASH_ERR_SHAPE;
   if (c.mask_id < 0 || c.mask_id >= c.vocab) return DFLASH_ERR_SHAPE;
   if (c.n_q_heads % c.n_kv_heads != 0) return DFLASH_ERR_SHAPE;
   if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f)) return DFLASH_ERR_SHAPE;
-  if (c.block < 2 || c.block > 16) return DFLASH_ERR_UNSUPPORTED;
-  if (c.n_layers > dfl::kMaxLayers) return DFLASH_ERR_UNSUPPORTED;
+  if (c.n_layers > max_layers) return DFLASH_ERR_UNSUPPORTED;
   if (c.head_dim != 64 && c.head_dim != 128) return DFLASH_ERR_UNSUPPORTED;
   if (c.hidden % 64 || c.intermediate % 64 || (c.n_q_heads * c.head_dim) % 64 ||
       ((long long)c.n_tap * c.hidden) % 64 || c.vocab % 16)
     return DFLASH_ERR_UNSUPPORTED;
   if ((c.n_q_heads / c.n_kv_heads) * c.block > 256) return DFLASH_ERR_UNSUPPORTED;
   if (c.hidden > 8192) return DFLASH_ERR_UNSUPPORTED;  // row kernels hold a row in registers
-  if (!w->embed || !w->lm_head || !w->w_fc || !w->g_fc || !w->g_final || !w->layers || !w->rope)
-    return DFLASH_ERR_NULL;
+  if (!w->embed || !w->lm_head || !w->g_final || !w->layers || !w->rope) return DFLASH_ERR_NULL;
   if (w->rope_max_pos < 1) return DFLASH_ERR_SHAPE;
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& L = w->layers[l];
@@ -415,12 +417,51 @@ dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights
         !L.w_down)
       return DFLASH_ERR_NULL;
   }
+  return DFLASH_OK;
+}
+
+dflash_model* new_model(const dflash_config& c, const dflash_weights* w) {
   dflash_model* m = new (std::nothrow) dflash_model;
-  if (!m) return DFLASH_ERR_SHAPE;
+  if (!m) return nullptr;
   m->cfg = c;
   m->w = *w;
   m->layers.assign(w->layers, w->layers + c.n_layers);
   m->w.layers = m->layers.data();
+  return m;
+}
+
+}  // namespace
+
+dflash_status dflash_model_create(const dflash_config* cfg, const dflash_weights* w,
+                                  dflash_model** out) {
+  if (!cfg || !w || !out) return DFLASH_ERR_NULL;
+  *out = nullptr;
+  const dflash_config& c = *cfg;
+  const dflash_status st = check_model(c, w, dfl::kMaxLayers);
+  if (st != DFLASH_OK) return st;
+  if (!w->w_fc || !w->g_fc) return DFLASH_ERR_NULL;
+  if (c.block < 2 || c.block > 16) return DFLASH_ERR_UNSUPPORTED;
+  dflash_model* m = new_model(c, w);
+  if (!m) return DFLASH_ERR_SHAPE;
+  *out = m;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_target_create(const dflash_config* cfg, const dflash_weights* w, const int32_t* tap_layers,
+                                   dflash_model** out) {
+  if (!cfg || !w || !out || !tap_layers) return DFLASH_ERR_NULL;
+  *out = nullptr;
+  const dflash_config& c = *cfg;
+  const dflash_status st = check_model(c, w, kMaxTargetLayers);
+  if (st != DFLASH_OK) return st;
+  if (c.block > 64) return DFLASH_ERR_UNSUPPORTED;
+  for (int t = 0; t < c.n_tap; ++t)
+    if (tap_layers[t] < 0 || tap_layers[t] >= c.n_layers || (t > 0 && tap_layers[t] <= tap_layers[t - 1]))
+      return DFLASH_ERR_SHAPE;
+  dflash_model* m = new_model(c, w);
+  if (!m) return DFLASH_ERR_SHAPE;
+  m->target = true;
+  m->taps.assign(tap_layers, tap_layers + c.n_tap);
   *out = m;
   return DFLASH_OK;
 }
@@ -445,9 +486,17 @@ dflash_status dflash_rope_table(float* out, int32_t max_pos, int32_t head_dim, f
 size_t dflash_workspace_bytes(const dflash_model* m, int32_t max_batch, int32_t max_ctx,
                               int32_t max_rows) {
   if (!m || max_batch < 1 || max_ctx < 1 || max_rows < 0) return 0;
-  size_t n = draft_ws(m->cfg, max_batch, max_ctx).total;
-  n = std::max(n, fuse_ws(m->cfg, std::max(1, max_rows)));
-  n = std::max(n, inject_ws(m->cfg, std::max(1, max_rows)));
+  const dflash_config& c = m->cfg;
+  if (m->target) {
+    // a target pass of any n <= block rows per sequence (split counts, and so
+    // partial sizes, need not grow with n)
+    size_t n = 0;
+    for (int b = 1; b <= c.block; ++b) n = std::max(n, stack_ws(c, max_batch, max_ctx, b, b).total);
+    return n;
+  }
+  size_t n = stack_ws(c, max_batch, max_ctx, c.block, c.block - 1).total;
+  n = std::max(n, fuse_ws(c, std::max(1, max_rows)));
+  n = std::max(n, inject_ws(c, std::max(1, max_rows)));
   return n;
 }
 
@@ -457,6 +506,7 @@ dflash_status dflash_fuse_ctx(const dflash_model* m, const void* taps, int32_t n
   if (n_rows < 0) return DFLASH_ERR_SHAPE;
   if (n_rows == 0) return DFLASH_OK;
   if (!taps || !ctx || !ws) return DFLASH_ERR_NULL;
+  if (m->target) return DFLASH_ERR_UNSUPPORTED;
   const dflash_config& c = m->cfg;
   if (ws_bytes < fuse_ws(c, n_rows)) return DFLASH_ERR_WORKSPACE;
   const hipStream_t st = as_stream(stream);
@@ -505,6 +555,7 @@ dflash_status dflash_inject_kv(const dflash_model* m, const void* ctx, int32_t n
   if (max_commit == 0) return DFLASH_OK;
   if (!ctx || !commit_rows || !n_commit || !ws) return DFLASH_ERR_NULL;
   if (n_ctx_rows == 0) return DFLASH_ERR_SHAPE;
+  if (m->target) return DFLASH_ERR_UNSUPPORTED;
   dflash_status ks = check_kv(m, kv);
   if (ks != DFLASH_OK) return ks;
   const dflash_config& c = m->cfg;
@@ -567,20 +618,35 @@ dflash_status dflash_inject_kv(const dflash_model* m, const void* ctx, int32_t n
   return DFLASH_OK;
 }
 
-dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
-                                 int32_t* draft, float* dbg_logits, float* dbg_hidden, void* ws,
-                                 size_t ws_bytes, void* stream) {
-  if (!m || !anchor || !draft || !ws) return DFLASH_ERR_NULL;
-  dflash_status ks = check_kv(m, kv);
-  if (ks != DFLASH_OK) return ks;
+namespace {
+
+// One pass of the layer stack over B rows per sequence (a draft block or a
+// target pass); see dflash_draft_block and dflash_target_forward.
+struct StackIO {
+  const int32_t* anchor = nullptr;  // draft: row 0's token (rows 1..B-1: mask id)
+  const int32_t* tokens = nullptr;  // target: every row's token [batch, B]
+  int B = 0;                        // rows per sequence
+  int lm_skip = 0;                  // 1: rows j >= 1 reach the LM head (draft), 0: all rows
+  int causal = 0;                   // block attention causal inside the block
+  uint16_t* taps = nullptr;         // target: bf16 [batch*B, n_tap*H] or NULL
+  int32_t* out = nullptr;           // argmax of the LM rows, [batch, B - lm_skip]
+  float* dbg_logits = nullptr;
+  float* dbg_hidden = nullptr;
+};
+
+dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io, void* ws, size_t ws_bytes,
+                        void* stream) {
   const dflash_config& c = m->cfg;
-  const int batch = kv->batch, B = c.block, H = c.hidden, D = c.head_dim;
+  const int batch = kv->batch, B = io.B, H = c.hidden, D = c.head_dim;
   const int Hq = c.n_q_heads, Hkv = c.n_kv_heads, I = c.intermediate, NL = c.n_layers;
-  const int Mb = batch * B, Ml = batch * (B - 1);
+  const int lm_rows = B - io.lm_skip;
+  const int Mb = batch * B, Ml = batch * lm_rows;
   const int qw = Hq * D, qkvw = (Hq + 2 * Hkv) * D;
-  const DraftWs w = draft_ws(c, batch, kv->max_ctx);
+  const StackWs w = stack_ws(c, batch, kv->max_ctx, B, lm_rows);
   if (ws_bytes < w.total) return DFLASH_ERR_WORKSPACE;
-  const AttnPlan ap = plan_attn(c, batch, kv->max_ctx);
+  const AttnPlan ap = plan_attn(c, batch, kv->max_ctx, B);
+  float* dbg_hidden = io.dbg_hidden;
+  float* dbg_logits = io.dbg_logits;
   const hipStream_t st = as_stream(stream);
   char* base = static_cast<char*>(ws);
   float* x = reinterpret_cast<float*>(base + w.x);
@@ -600,7 +666,8 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
 
   dfl::EmbedParams ep;
   std::memset(&ep, 0, sizeof(ep));
-  ep.anchor = anchor;
+  ep.anchor = io.anchor;
+  ep.tokens = io.tokens;
   ep.embed = static_cast<const uint16_t*>(m->w.embed);
   ep.gain = static_cast<const uint16_t*>(m->layers[0].g_in);
   ep.ctx_len = kv->ctx_len;
@@ -674,6 +741,7 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     at.n_chunks = ap.n_chunks;
     at.slice = ap.slice;
     at.gb_pad = ap.gb_pad;
+    at.causal = io.causal;
     at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     at.pm = pm;
     at.pl = pl;
@@ -770,13 +838,20 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     rn.rows = Mb;
     rn.n = H;
     rn.dbg = dbg_hidden ? dbg_hidden + (long long)(l + 1) * hid : nullptr;
+    if (io.taps) {
+      for (size_t t = 0; t < m->taps.size(); ++t)
+        if (m->taps[t] == l) {
+          rn.tap = io.taps + (long long)t * H;
+          rn.tap_ld = (long long)m->taps.size() * H;
+        }
+    }
     if (l + 1 < NL) {
       rn.gain = static_cast<const uint16_t*>(m->layers[l + 1].g_in);
       rn.out = u;
     } else {
       rn.gain = static_cast<const uint16_t*>(m->w.g_final);
       rn.out = ulm;
-      rn.final_mode = 1;
+      rn.final_mode = io.lm_skip;
       rn.B = B;
     }
     if ((e = dfl::launch_row_norm(rn, st)) != hipSuccess) return DFLASH_ERR_HIP;
@@ -801,7 +876,57 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
     e = run_gemm(gl, st, nullptr);
   }
   if (e != hipSuccess) return DFLASH_ERR_HIP;
-  return hip_status(dfl::launch_argmax_finish(keys, lm_tiles(c, Ml), kv->status, batch, B, draft, st));
+  return hip_status(dfl::launch_argmax_finish(keys, lm_tiles(c, Ml), kv->status, batch, lm_rows, io.out, st));
+}
+
+}  // namespace
+
+dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
+                                 int32_t* draft, float* dbg_logits, float* dbg_hidden, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!m || !anchor || !draft || !ws) return DFLASH_ERR_NULL;
+  if (m->target) return DFLASH_ERR_UNSUPPORTED;
+  dflash_status ks = check_kv(m, kv);
+  if (ks != DFLASH_OK) return ks;
+  StackIO io;
+  io.anchor = anchor;
+  io.B = m->cfg.block;
+  io.lm_skip = 1;
+  io.out = draft;
+  io.dbg_logits = dbg_logits;
+  io.dbg_hidden = dbg_hidden;
+  return run_stack(m, kv, io, ws, ws_bytes, stream);
+}
+
+dflash_status dflash_target_forward(const dflash_model* m, dflash_kv* kv, const int32_t* tokens, int32_t n,
+                                    int32_t* argmax, void* taps, float* dbg_logits, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (!m || !tokens || !argmax || !ws) return DFLASH_ERR_NULL;
+  if (!m->target) return DFLASH_ERR_UNSUPPORTED;
+  if (n < 1 || n > m->cfg.block) return DFLASH_ERR_SHAPE;
+  dflash_status ks = check_kv(m, kv);
+  if (ks != DFLASH_OK) return ks;
+  StackIO io;
+  io.tokens = tokens;
+  io.B = n;
+  io.lm_skip = 0;
+  io.causal = 1;
+  io.taps = static_cast<uint16_t*>(taps);
+  io.out = argmax;
+  io.dbg_logits = dbg_logits;
+  return run_stack(m, kv, io, ws, ws_bytes, stream);
+}
+
+dflash_status dflash_kv_commit(const dflash_model* m, dflash_kv* kv, const int32_t* commit_rows,
+                               const int32_t* n_commit, int32_t max_commit, void* stream) {
+  if (!m) return DFLASH_ERR_NULL;
+  if (max_commit < 0) return DFLASH_ERR_SHAPE;
+  if (max_commit == 0) return DFLASH_OK;
+  if (!commit_rows || !n_commit) return DFLASH_ERR_NULL;
+  dflash_status ks = check_kv(m, kv);
+  if (ks != DFLASH_OK) return ks;
+  return hip_status(dfl::launch_kv_commit(commit_rows, n_commit, max_commit, kv->batch, kv->max_ctx, kv->ctx_len,
+                                          as_stream(stream)));
 }
 
 dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,
@@ -811,6 +936,7 @@ dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,
                                    int32_t* n_emit, int32_t* done, int32_t* commit_rows,
                                    int32_t* n_commit, void* stream) {
   if (!m) return DFLASH_ERR_NULL;
+  if (m->target) return DFLASH_ERR_UNSUPPORTED;
   dflash_status ks = check_kv(m, kv);
   if (ks != DFLASH_OK) return ks;
   if (!draft || !target_argmax || !accept_len || !anchor_out || !emitted || !n_emit || !done ||

@@ -1,8 +1,9 @@
 // Block attention of the draft step on gfx950.
 //
 // For sequence b and kv head g, the G = Hq/Hkv query heads times B block rows
-// (G*B query rows, padded to 16) attend with no mask over the cache slots
-// [0, L_b + B): the injected context followed by the block's own K/V. Every
+// (G*B query rows, padded to 16) attend over the cache slots [0, L_b + B): the
+// context followed by the block's own K/V, with no mask (a draft block) or
+// causally inside the block (a target pass: row j sees slots < L_b + j + 1). Every
 // key costs 4*D bytes of K+V and 4*D*G*B flops, so at G*B = 64..128 the kernel
 // is bound by streaming K/V from HBM; MFMA keeps the arithmetic far below that
 // bound.
@@ -144,14 +145,17 @@ void attn_kernel(const AttnParams p) {
   const int GB = G * p.B;
   const int QT = p.gb_pad / 16;
 
-  // queries of this wave, as MFMA B operands (column = query, k = d)
+  // queries of this wave, as MFMA B operands (column = query, k = d); jrow
+  // is the block row of this lane's query column
   u32x4 qreg[QPW][D / 32];
+  int jrow[QPW];
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
     const int qt = wave + 4 * i;
     int rr = qt * 16 + r;
     rr = rr < GB ? rr : GB - 1;
     const int hl = rr / p.B, j = rr % p.B;
+    jrow[i] = j;
     const bf16_t* qrow = p.q + ((long long)(b * p.B + j) * p.Hq + g * G + hl) * D + gq * 8;
     // rows past GB read the last row (valid memory); padded tiles are zeroed
     // by a select, not a guarded load
@@ -199,15 +203,22 @@ void attn_kernel(const AttnParams p) {
         for (int i = 0; i < QPW; ++i) sacc[i][kt] = mfma16x16x32(a, qreg[i][ds], sacc[i][kt]);
       }
     }
-    // keys past the end exist only in the chunk's last slice
-    if (k0 + SL > k_end) {
+    // keys past the end exist only in the chunk's last slice; in a causal
+    // block, row j also drops the block keys after its own position
+    const int lim0 = Lk - p.B + 1;  // key limit of block row 0
+    if (k0 + SL > k_end || (p.causal && k0 + SL > lim0)) {
+      int lim[QPW];
+#pragma unroll
+      for (int i = 0; i < QPW; ++i) lim[i] = p.causal ? min(k_end, lim0 + jrow[i]) : k_end;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (k0 + kt * 16 + 4 * gq + e >= k_end)
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + kt * 16 + 4 * gq + e;
 #pragma unroll
-            for (int i = 0; i < QPW; ++i) sacc[i][kt][e] = -__builtin_inff();
+          for (int i = 0; i < QPW; ++i)
+            if (key >= lim[i]) sacc[i][kt][e] = -__builtin_inff();
+        }
     }
     // online softmax on raw scores: the running max is kept in scaled base-2
     // units, and max(s) * c == max(s * c) for the positive scale c
@@ -222,13 +233,16 @@ void attn_kernel(const AttnParams p) {
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mnew = fmaxf(mrun[i], mx * p.scale_log2);
-      const float alpha = fast_exp2(mrun[i] - mnew);
+      // a causal row may have no visible key yet: weights against 0 are then
+      // exp2(-inf) = 0 instead of NaN
+      const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
+      const float alpha = fast_exp2(mrun[i] - mref);
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pv = fast_exp2(__builtin_fmaf(sacc[i][kt][e], p.scale_log2, -mnew));
+          const float pv = fast_exp2(__builtin_fmaf(sacc[i][kt][e], p.scale_log2, -mref));
           sacc[i][kt][e] = pv;
           rs += pv;
         }

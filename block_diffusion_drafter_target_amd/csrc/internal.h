@@ -78,8 +78,9 @@ struct AttnParams {
   const int32_t* ctx_len;
   const int32_t* status;
   int batch, Hq, Hkv, B, max_ctx;
-  int n_chunks;  // key chunks per (b, g) (grid x, <= 64); chunk length per sequence
-                 // = max(slice, L_b + B split n_chunks ways, rounded up to slice)
+  int n_chunks;  // key chunks per (b, g) (grid x, <= 64); chunk length for the batch
+                 // = max(slice, max_b(L_b) + B split n_chunks ways, rounded up to slice)
+  int causal;    // 0: every block row sees all L_b + B keys; 1: block row j sees keys < L_b + j + 1
   int slice;     // keys per LDS slice: 64 or 128
   int gb_pad;    // query rows per (b, g), padded to 16
   float scale_log2;
@@ -117,13 +118,16 @@ struct RowNormParams {
   int rows, n;
   uint16_t* out;       // bf16 [rows, n] (or [batch*(B-1), n] in final mode)
   float* dbg;          // optional fp32 copy of x after the add, [rows, n]
-  int final_mode, B;
+  uint16_t* tap;       // optional bf16 copy of x after the add, row stride tap_ld
+  long long tap_ld;
+  int final_mode, B;   // final_mode 1: out holds rows j >= 1 of every B-row sequence only
 };
 
 hipError_t launch_row_norm(const RowNormParams& p, hipStream_t st);
 
 struct EmbedParams {
-  const int32_t* anchor;
+  const int32_t* anchor;  // row 0 of every sequence (rows 1..B-1: mask_id), or
+  const int32_t* tokens;  // every row's token [batch, B] when not NULL
   const uint16_t* embed;
   const uint16_t* gain;
   int32_t* ctx_len;
@@ -180,7 +184,12 @@ hipError_t launch_inject_post(const InjectPostParams& p, hipStream_t st);
 // draft[b][j-1] = index of max over tiles of keys[tile * (batch*(B-1)) + row],
 // row = b*(B-1) + j-1; -1 for a sequence whose status is nonzero.
 hipError_t launch_argmax_finish(const unsigned long long* keys, int n_tiles, const int32_t* status,
-                                int batch, int B, int32_t* draft, hipStream_t st);
+                                int batch, int rows_per_seq, int32_t* out, hipStream_t st);
+
+// ctx_len[seq] = max(ctx_len[seq], pos + 1) for the first min(n_commit, max_commit)
+// commit rows (src, seq, pos) with a valid seq and 0 <= pos < max_ctx.
+hipError_t launch_kv_commit(const int32_t* commit_rows, const int32_t* n_commit, int max_commit, int batch,
+                            int max_ctx, int32_t* ctx_len, hipStream_t st);
 
 struct VerifyParams {
   const int32_t* draft;

@@ -1,8 +1,8 @@
 // Row-wise kernels of the draft step (gfx950): embedding + RMSNorm, split-K
 // reduction + residual + RMSNorm, per-head q/k RMSNorm + RoPE + KV-cache
 // append, the inject epilogue (k-norm + RoPE + cache scatter + commit
-// of ctx_len), the final argmax over the LM-head tiles, and the combine pass
-// of a split SwiGLU.
+// of ctx_len), the final argmax over the LM-head tiles, the combine pass of a
+// split SwiGLU, and the commit of rows whose K/V are already cached.
 //
 // All are bound by a few kilobytes per row; they exist to keep every fp32
 // statistic (RMSNorm sums, residual stream, RoPE) on the device between the
@@ -71,15 +71,16 @@ __device__ __forceinline__ f32x4_t bf4_to_f32(u32x2 w) {
 
 // ---------------------------------------------------------------------------
 // block row embedding: x = E[token], u = bf16(RMSNorm(x) * g_in of layer 0)
-// Row j of sequence b holds the anchor (j = 0) or the mask id. The j == 0
-// workgroup also records the sequence's capacity status.
+// Row j of sequence b holds the anchor (j = 0) or the mask id (a draft block),
+// or the given token (a target pass). The j == 0 workgroup also records the
+// sequence's capacity status.
 __global__ __launch_bounds__(kRowThreads) void embed_kernel(const EmbedParams p) {
   __shared__ float red[kRowThreads / 64];
   const int m = blockIdx.x;
   const int b = m / p.B, j = m % p.B;
   const int L = p.ctx_len[b];
   const bool cap_bad = L < 0 || L + p.B > p.max_ctx || L + p.B > p.rope_max;
-  int tok = j == 0 ? p.anchor[b] : p.mask_id;
+  int tok = p.tokens ? p.tokens[(long long)b * p.B + j] : (j == 0 ? p.anchor[b] : p.mask_id);
   const bool tok_bad = tok < 0 || tok >= p.V;
   if (j == 0 && threadIdx.x == 0) p.status[b] = cap_bad ? kErrCapacity : (tok_bad ? kErrShape : 0);
   if (tok_bad) tok = 0;
@@ -154,6 +155,9 @@ __global__ __launch_bounds__(kRowThreads) void row_norm_kernel(const RowNormPara
     if (i4 < n4) {
       if (p.x) *reinterpret_cast<f32x4_t*>(p.x + row_off + 4 * i4) = v[c];
       if (p.dbg) *reinterpret_cast<f32x4_t*>(p.dbg + row_off + 4 * i4) = v[c];
+      if (p.tap)
+        *reinterpret_cast<u32x2*>(p.tap + (long long)m * p.tap_ld + 4 * i4) =
+            u32x2{pack_bf2(v[c][0], v[c][1]), pack_bf2(v[c][2], v[c][3])};
     }
     ss += v[c][0] * v[c][0] + v[c][1] * v[c][1] + v[c][2] * v[c][2] + v[c][3] * v[c][3];
   }
@@ -326,10 +330,10 @@ constexpr int kFinishBatch = 8;
 
 __global__ __launch_bounds__(kFinishThreads) void argmax_finish_kernel(const unsigned long long* keys,
                                                                        int n_tiles, const int32_t* status,
-                                                                       int batch, int B, int32_t* draft) {
+                                                                       int batch, int rows_per_seq, int32_t* out) {
   __shared__ unsigned long long red[kFinishThreads / 64];
   const int row = blockIdx.x;
-  const int rows = batch * (B - 1);
+  const int rows = batch * rows_per_seq;
   unsigned long long best = 0ull;
   for (int t0 = threadIdx.x; t0 < n_tiles; t0 += kFinishThreads * kFinishBatch) {
     unsigned long long k[kFinishBatch];
@@ -353,9 +357,24 @@ __global__ __launch_bounds__(kFinishThreads) void argmax_finish_kernel(const uns
 #pragma unroll
     for (int w = 1; w < kFinishThreads / 64; ++w) best = max(best, red[w]);
     best = max(best, red[0]);
-    const int b = row / (B - 1);
-    draft[row] = status[b] != 0 ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+    const int b = row / rows_per_seq;
+    out[row] = status[b] != 0 ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
   }
+}
+
+// ---------------------------------------------------------------------------
+// commit without K/V writes (the rows' K/V are already in the cache): ctx_len
+// of each committed row's sequence grows to pos + 1.
+__global__ __launch_bounds__(256) void kv_commit_kernel(const int32_t* commit_rows, const int32_t* n_commit,
+                                                        int max_commit, int batch, int max_ctx, int32_t* ctx_len) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= max_commit) return;
+  int nc = *n_commit;
+  nc = nc < 0 ? 0 : (nc > max_commit ? max_commit : nc);
+  if (i >= nc) return;
+  const int seq = commit_rows[3 * i + 1], pos = commit_rows[3 * i + 2];
+  if (seq < 0 || seq >= batch || pos < 0 || pos >= max_ctx) return;
+  atomicMax(ctx_len + seq, pos + 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -425,9 +444,18 @@ hipError_t launch_inject_post(const InjectPostParams& p, hipStream_t st) {
 }
 
 hipError_t launch_argmax_finish(const unsigned long long* keys, int n_tiles, const int32_t* status,
-                                int batch, int B, int32_t* draft, hipStream_t st) {
-  hipLaunchKernelGGL(argmax_finish_kernel, dim3(batch * (B - 1)), dim3(kFinishThreads), 0, st, keys, n_tiles,
-                     status, batch, B, draft);
+                                int batch, int rows_per_seq, int32_t* out, hipStream_t st) {
+  if (rows_per_seq < 1 || batch < 1 || n_tiles < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(argmax_finish_kernel, dim3(batch * rows_per_seq), dim3(kFinishThreads), 0, st, keys, n_tiles,
+                     status, batch, rows_per_seq, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_commit(const int32_t* commit_rows, const int32_t* n_commit, int max_commit, int batch,
+                            int max_ctx, int32_t* ctx_len, hipStream_t st) {
+  if (max_commit <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_commit_kernel, dim3((max_commit + 255) / 256), dim3(256), 0, st, commit_rows, n_commit,
+                     max_commit, batch, max_ctx, ctx_len);
   return hipGetLastError();
 }
 

@@ -2,7 +2,8 @@
 
 ``Drafter`` owns torch device buffers (weights, draft KV cache, workspace,
 per-step outputs) and a model handle; each method marshals pointers to one
-C entry point. ``spec_generate`` drives the greedy loop for one sequence with a
+C entry point. ``DeviceTarget`` does the same for a target model (causal
+passes that emit taps and argmax). ``spec_generate`` drives the greedy loop for one sequence with a
 caller-supplied target, following the pages' ``spec_generate`` call shape
 (input ids, a token budget, temperature 0, a target, stop ids) [P4
 "Ejecutando DFlash"].
@@ -165,15 +166,121 @@ class Drafter:
         self.inject_kv(ctx, n, rows, cnt, n)
 
 
+class DeviceTarget:
+    """A target model on the device: ``n_layers`` decoder layers of the
+    drafter's layer shape sharing its embedding and LM head, its own KV cache,
+    and the layers in ``tap_layers`` tapped. ``pass_tokens`` runs the causal
+    pass over up to ``max_n`` new tokens per sequence (K/V written
+    speculatively) and ``commit`` keeps verified rows; ``forward``/``truncate``
+    /``reset`` are the loop's target protocol for one sequence."""
+
+    def __init__(self, cfg: DraftConfig, weights: dict, n_layers: int, tap_layers: Sequence[int],
+                 batch: int = 1, max_ctx: int = 4096, max_n: int = 16, device="cuda", rope_max: int | None = None):
+        torch = _torch()
+        bd.load()
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.batch, self.max_ctx, self.max_n = batch, max_ctx, max_n
+        self.n_layers, self.tap_layers = n_layers, tuple(int(t) for t in tap_layers)
+        self.rope_max = rope_max or max_ctx
+        self.w = {}
+        for name, arr in weights.items():
+            if name.startswith("layers.") and int(name.split(".")[1]) >= n_layers:
+                continue
+            if name in ("w_fc", "g_fc"):
+                continue
+            t = arr if hasattr(arr, "data_ptr") else to_device_bf16(np.asarray(arr), self.device)
+            self.w[name] = pack_matrix(t) if is_packed(name) else t
+            del t
+        rope = np.empty(self.rope_max * (cfg.head_dim // 2) * 2, np.float32)
+        bd.dflash_rope_table(rope.ctypes.data_as(C.c_void_p), self.rope_max, cfg.head_dim, cfg.rope_theta)
+        self.rope = torch.from_numpy(rope).to(self.device)
+        c = bd.dflash_config(hidden=cfg.hidden, n_layers=n_layers, n_q_heads=cfg.n_q_heads,
+                             n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim,
+                             intermediate=cfg.intermediate, vocab=cfg.vocab, n_tap=len(self.tap_layers),
+                             block=max_n, mask_id=cfg.mask_id, rope_theta=cfg.rope_theta,
+                             rms_eps=cfg.rms_eps)
+        layers = (bd.dflash_layer_weights * n_layers)()
+        for l in range(n_layers):
+            for f in ("g_in", "w_qkv", "g_q", "g_k", "w_o", "g_post", "w_gate", "w_up", "w_down"):
+                setattr(layers[l], f, self.w[f"layers.{l}.{f}"].data_ptr())
+        wst = bd.dflash_weights(embed=self.w["embed"].data_ptr(), lm_head=self.w["lm_head"].data_ptr(),
+                                w_fc=None, g_fc=None, g_final=self.w["g_final"].data_ptr(), layers=layers,
+                                rope=self.rope.data_ptr(), rope_max_pos=self.rope_max)
+        self._c_cfg, self._c_layers, self._c_w = c, layers, wst
+        self.model = bd.dflash_target_create(c, wst, self.tap_layers)
+        Hkv, D = cfg.n_kv_heads, cfg.head_dim
+        self.k = torch.zeros((n_layers, batch, Hkv, max_ctx, D), dtype=torch.bfloat16, device=self.device)
+        self.v = torch.zeros((n_layers, batch, Hkv, max_ctx, D), dtype=torch.bfloat16, device=self.device)
+        self.ctx_len = torch.zeros(batch, dtype=torch.int32, device=self.device)
+        self.status = torch.zeros(batch, dtype=torch.int32, device=self.device)
+        self.kv = bd.dflash_kv(k=self.k.data_ptr(), v=self.v.data_ptr(), batch=batch, max_ctx=max_ctx,
+                               ctx_len=self.ctx_len.data_ptr(), status=self.status.data_ptr())
+        self.ws_bytes = bd.dflash_workspace_bytes(self.model, batch, max_ctx, 0)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.argmax = torch.zeros(batch * max_n, dtype=torch.int32, device=self.device)
+        self.taps = torch.zeros((batch * max_n, len(self.tap_layers) * cfg.hidden), dtype=torch.bfloat16,
+                                device=self.device)
+
+    def __del__(self):
+        m = getattr(self, "model", None)
+        if m:
+            bd.dflash_model_destroy(m)
+            self.model = None
+
+    # -- entry points --------------------------------------------------------
+    def pass_tokens(self, tokens, dbg_logits=None):
+        """tokens: device int32 [batch, n] (contiguous); returns (argmax [batch, n],
+        taps [batch*n, n_tap*H]) as views of the target's output buffers."""
+        n = tokens.shape[1]
+        if tokens.dtype != _torch().int32 or not tokens.is_contiguous() or tokens.shape[0] != self.batch:
+            raise ValueError("tokens must be a contiguous int32 [batch, n] device tensor")
+        bd.dflash_target_forward(self.model, self.kv, bd.ptr(tokens), n, bd.ptr(self.argmax), bd.ptr(self.taps),
+                                 bd.ptr(dbg_logits), bd.ptr(self.ws), self.ws_bytes, Drafter.stream())
+        return self.argmax[:self.batch * n].view(self.batch, n), self.taps[:self.batch * n]
+
+    def commit(self, commit_rows, n_commit, max_commit: int):
+        bd.dflash_kv_commit(self.model, self.kv, bd.ptr(commit_rows), bd.ptr(n_commit), max_commit,
+                            Drafter.stream())
+
+    # -- loop protocol (batch 1) ---------------------------------------------
+    def reset(self) -> None:
+        self.ctx_len.zero_()
+        self.status.zero_()
+
+    def forward(self, tokens: Sequence[int]):
+        """Append tokens (in passes of up to max_n); returns (argmax as numpy
+        [n], taps as a device bf16 tensor [n, n_tap*H])."""
+        torch = _torch()
+        toks = torch.tensor(list(tokens), dtype=torch.int32, device=self.device)
+        outs, taps = [], []
+        for i in range(0, len(toks), self.max_n):
+            part = toks[i:i + self.max_n][None, :]
+            a, t = self.pass_tokens(part)
+            outs.append(a[0].clone())
+            taps.append(t.clone())
+            self.ctx_len += part.shape[1]
+        return torch.cat(outs).cpu().numpy(), torch.cat(taps)
+
+    def truncate(self, length: int) -> None:
+        self.ctx_len.fill_(length)
+
+
 class Target(Protocol):
     """What the loop needs from the target model (batch 1)."""
 
     def reset(self) -> None: ...
 
-    def forward(self, tokens: Sequence[int]) -> tuple[np.ndarray, np.ndarray]:
-        """Append tokens; return (greedy argmax per row, taps [n, n_tap*H])."""
+    def forward(self, tokens: Sequence[int]):
+        """Append tokens; return (greedy argmax per row, taps [n, n_tap*H] as an
+        array or a device bf16 tensor)."""
 
     def truncate(self, length: int) -> None: ...
+
+
+def _taps_dev(taps, dev):
+    """Taps as a device bf16 tensor (a device target's are already there)."""
+    return taps if hasattr(taps, "data_ptr") else to_device_bf16(np.asarray(taps, np.float32), dev)
 
 
 def spec_generate(drafter: Drafter, target: Target, prompt: Sequence[int], max_new_tokens: int,
@@ -194,7 +301,7 @@ def spec_generate(drafter: Drafter, target: Target, prompt: Sequence[int], max_n
     anchor = int(a[-1])
     out = [anchor]
     P = len(prompt)
-    drafter.ingest(0, to_device_bf16(np.asarray(taps, np.float32), dev))
+    drafter.ingest(0, _taps_dev(taps, dev))
     stops = torch.tensor(list(stop_token_ids), dtype=torch.int32, device=dev) if stop_token_ids else None
     budget = torch.tensor([max_new_tokens - 1], dtype=torch.int32, device=dev)
     L = P
@@ -208,7 +315,7 @@ def spec_generate(drafter: Drafter, target: Target, prompt: Sequence[int], max_n
         drafter.verify_accept(tgt, stops, budget)
         m = int(drafter.accept_len.item())
         target.truncate(L + m + 1)
-        ctx = drafter.fuse_ctx(to_device_bf16(np.asarray(taps, np.float32), dev), B)
+        ctx = drafter.fuse_ctx(_taps_dev(taps, dev), B)
         drafter.inject_kv(ctx, B, drafter.commit_rows, drafter.n_commit, B)
         n = int(drafter.n_emit.item())
         out += [int(t) for t in drafter.emitted[0, :n].cpu().numpy()]

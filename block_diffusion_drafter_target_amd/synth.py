@@ -56,7 +56,8 @@ class DraftConfig:
     # workload
     batch: int = 1
     ctx_len: int | tuple[int, int] = 1024  # fixed length, or (lo, hi) uniform
-    # tiny-target case only
+    # target model paired with the drafter (tiny case: the CPU-checkable
+    # target; Qwen3-8B shape: the device target of the verify pass)
     target_layers: int = 0
     tap_layers: tuple[int, ...] = ()
     n_new: int = 0
@@ -96,15 +97,15 @@ CONFIGS: dict[str, DraftConfig] = {
     "c2": DraftConfig(
         name="qwen3-8b-shaped-5L", hidden=4096, n_layers=5, n_q_heads=32,
         n_kv_heads=8, head_dim=128, intermediate=12288, vocab=151936, n_tap=5,
-        block=16, batch=1, ctx_len=1024),
+        block=16, batch=1, ctx_len=1024, target_layers=36, tap_layers=(1, 9, 17, 25, 33)),
     "c3": DraftConfig(
         name="qwen3-8b-shaped-5L", hidden=4096, n_layers=5, n_q_heads=32,
         n_kv_heads=8, head_dim=128, intermediate=12288, vocab=151936, n_tap=5,
-        block=16, batch=32, ctx_len=(512, 4096)),
+        block=16, batch=32, ctx_len=(512, 4096), target_layers=36, tap_layers=(1, 9, 17, 25, 33)),
     "c4": DraftConfig(
         name="qwen3-8b-shaped-5L", hidden=4096, n_layers=5, n_q_heads=32,
         n_kv_heads=8, head_dim=128, intermediate=12288, vocab=151936, n_tap=5,
-        block=16, batch=8, ctx_len=8192),
+        block=16, batch=8, ctx_len=8192, target_layers=36, tap_layers=(1, 9, 17, 25, 33)),
     "c5": DraftConfig(
         name="gpt-oss-120b-shaped-8L", hidden=2880, n_layers=8, n_q_heads=64,
         n_kv_heads=8, head_dim=64, intermediate=2880, vocab=201088, n_tap=5,
@@ -250,7 +251,7 @@ def weight_rows(cfg: DraftConfig, name: str, r0: int, r1: int, seed: int = SEED_
 
 
 def target_weight_shapes(cfg: DraftConfig) -> list[tuple[str, int, int]]:
-    """Tiny target: same layer shapes as the drafter, ``cfg.target_layers`` deep.
+    """Target: same layer shapes as the drafter, ``cfg.target_layers`` deep.
 
     Its embedding and LM head are the drafter's (shared)."""
     H = cfg.hidden

@@ -144,7 +144,8 @@ dflash_status dflash_pack_matrix(const void* src, void* dst, int32_t rows, int32
 
 /* Workspace (device scratch, caller-allocated) needed by calls that handle up
  * to max_batch sequences, a cache of max_ctx slots and up to max_rows context
- * rows per fuse/inject call. */
+ * rows per fuse/inject call; for a target model, by a dflash_target_forward of
+ * any n <= block (max_rows unused). */
 size_t dflash_workspace_bytes(const dflash_model* m, int32_t max_batch, int32_t max_ctx,
                               int32_t max_rows);
 
@@ -216,6 +217,53 @@ dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,
                                    int32_t* accept_len, int32_t* anchor_out, int32_t* emitted,
                                    int32_t* n_emit, int32_t* done, int32_t* commit_rows,
                                    int32_t* n_commit, void* stream);
+
+/* Target side of the step: a causal pass of the target model over n new
+ * tokens per sequence. [P2 introduction and P3 introduction: the target
+ * checks the whole drafted block in one parallel pass and keeps the longest
+ * valid prefix; P3 "L'idea chiave: Il target sa meglio" and P4 "La idea de que
+ * 'el objetivo sabe más'": the drafter is conditioned on hidden states of
+ * several target layers, which this pass emits as taps]
+ *
+ * dflash_target_create builds a target model from the same config and weight
+ * structs as the drafter: n_layers decoder layers of the drafter's layer shape
+ * (up to 256), the shared embedding and LM head and g_final; w_fc and g_fc are
+ * not used (may be NULL); block = the largest n per call (1..64, and
+ * Hq/Hkv * block <= 256); n_tap tapped layers tap_layers[n_tap] (host array,
+ * strictly increasing, in [0, n_layers)). Host only: no HIP call. The model
+ * works with dflash_target_forward, dflash_kv_commit and
+ * dflash_workspace_bytes only (the drafter entry points return
+ * DFLASH_ERR_UNSUPPORTED for it), and is released with dflash_model_destroy. */
+dflash_status dflash_target_create(const dflash_config* cfg, const dflash_weights* w,
+                                   const int32_t* tap_layers, dflash_model** out);
+
+/* One target pass over tokens[b][0..n) at positions L_b .. L_b+n-1 (L_b =
+ * ctx_len[b]): token j attends to the cached slots [0, L_b) and to tokens
+ * 0..j of the pass (causal), and its K/V are written to cache slots L_b + j of
+ * every layer. ctx_len is not advanced: dflash_kv_commit keeps the accepted
+ * prefix; the rest is rolled back by construction.
+ *   tokens      device int32 [batch, n], 1 <= n <= block
+ *   argmax      device int32 [batch, n]: greedy next token after each input
+ *               token (lowest index on ties); -1 for a sequence whose status
+ *               is nonzero
+ *   taps        device bf16 [batch*n, n_tap*H] or NULL: the residual stream
+ *               after each tapped layer, layer-major within a row (the layout
+ *               dflash_fuse_ctx reads)
+ *   dbg_logits  device fp32 [batch*n, V] or NULL
+ * kv is the target's own cache ([NL][batch][Hkv][max_ctx][D] per dflash_kv).
+ * Capacity (L_b + n > max_ctx) is reported per sequence in kv->status.
+ * Workspace as in dflash_workspace_bytes of this model. */
+dflash_status dflash_target_forward(const dflash_model* m, dflash_kv* kv, const int32_t* tokens,
+                                    int32_t n, int32_t* argmax, void* taps, float* dbg_logits,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/* Commit rows whose K/V are already in the cache (a target pass wrote them):
+ * for the first min(n_commit, max_commit) rows (src, seq, pos) of commit_rows
+ * (device int32 [max_commit, 3], the layout dflash_verify_accept writes) with
+ * 0 <= seq < batch and 0 <= pos < max_ctx, ctx_len[seq] grows to pos + 1.
+ * [P2 introduction: the longest valid prefix is kept] */
+dflash_status dflash_kv_commit(const dflash_model* m, dflash_kv* kv, const int32_t* commit_rows,
+                               const int32_t* n_commit, int32_t max_commit, void* stream);
 
 /* Kernel timing for benchmarks. dflash_profile_enable(mask) times the phases
  * whose bit (1 << phase) is set in mask (0 switches timing off): every launch

@@ -132,6 +132,62 @@ def test_calls_reject_bad_arguments_without_a_gpu():
         bd.dflash_model_destroy(h)
 
 
+def _create_target(cfg, w, taps):
+    h = C.c_void_p()
+    arr = (C.c_int32 * len(taps))(*taps)
+    rc = bd.load().dflash_target_create(C.byref(cfg), C.byref(w), arr, C.byref(h))
+    return rc, h.value
+
+
+def test_target_create_and_calls_without_a_gpu():
+    lib = bd.load()
+    # a 36-layer Qwen3-8B-shaped target tapping 5 layers, passes of up to 16 tokens;
+    # the drafter's fusion weights are not needed
+    w, keep = _fake_weights(36)
+    w.w_fc = None
+    w.g_fc = None
+    taps = [1, 9, 17, 25, 33]
+    rc, h = _create_target(_cfg(n_layers=36), w, taps)
+    assert rc == bd.DFLASH_OK and h
+    try:
+        need16 = bd.dflash_workspace_bytes(h, 1, 2048, 0)
+        assert need16 > 0
+        kv = bd.dflash_kv(k=0x1000, v=0x1000, batch=1, max_ctx=2048, ctx_len=0x1000, status=0x1000)
+        f = lib.dflash_target_forward
+        assert f(h, C.byref(kv), 0x1000, 0, 0x1000, None, None, 0x1000, need16, None) == bd.DFLASH_ERR_SHAPE
+        assert f(h, C.byref(kv), 0x1000, 17, 0x1000, None, None, 0x1000, need16, None) == bd.DFLASH_ERR_SHAPE
+        assert f(h, C.byref(kv), None, 4, 0x1000, None, None, 0x1000, need16, None) == bd.DFLASH_ERR_NULL
+        assert f(h, C.byref(kv), 0x1000, 16, 0x1000, None, None, 0x1000, 64, None) == bd.DFLASH_ERR_WORKSPACE
+        # the drafter entry points refuse a target model
+        assert lib.dflash_draft_block(h, C.byref(kv), 0x1000, 0x1000, None, None, 0x1000, need16,
+                                      None) == bd.DFLASH_ERR_UNSUPPORTED
+        assert lib.dflash_fuse_ctx(h, 0x1000, 16, 0x1000, 0x1000, 1 << 30, None) == bd.DFLASH_ERR_UNSUPPORTED
+        assert lib.dflash_verify_accept(h, C.byref(kv), 0x1000, 0x1000, None, 0, None,
+                                        *([0x1000] * 7), None) == bd.DFLASH_ERR_UNSUPPORTED
+        # commit: nothing to commit is a no-op, missing count rejected
+        assert lib.dflash_kv_commit(h, C.byref(kv), None, None, 0, None) == bd.DFLASH_OK
+        assert lib.dflash_kv_commit(h, C.byref(kv), 0x1000, None, 4, None) == bd.DFLASH_ERR_NULL
+        assert lib.dflash_kv_commit(h, C.byref(kv), 0x1000, 0x1000, -1, None) == bd.DFLASH_ERR_SHAPE
+    finally:
+        bd.dflash_model_destroy(h)
+    # a drafter cannot be asked for a target pass
+    wd, keepd = _fake_weights(5)
+    rc, hd = _create(_cfg(), wd)
+    assert rc == 0
+    try:
+        kv = bd.dflash_kv(k=0x1000, v=0x1000, batch=1, max_ctx=2048, ctx_len=0x1000, status=0x1000)
+        assert lib.dflash_target_forward(hd, C.byref(kv), 0x1000, 4, 0x1000, None, None, 0x1000, 1 << 30,
+                                         None) == bd.DFLASH_ERR_UNSUPPORTED
+    finally:
+        bd.dflash_model_destroy(hd)
+    # tap layers must be increasing and inside the stack; passes of at most 64 tokens
+    for t, code in (([1, 9, 9, 25, 33], bd.DFLASH_ERR_SHAPE), ([1, 9, 17, 25, 36], bd.DFLASH_ERR_SHAPE),
+                    ([-1, 9, 17, 25, 33], bd.DFLASH_ERR_SHAPE)):
+        assert _create_target(_cfg(n_layers=36), w, t)[0] == code
+    assert _create_target(_cfg(n_layers=36, block=65), w, taps)[0] == bd.DFLASH_ERR_UNSUPPORTED
+    assert _create_target(_cfg(n_layers=257), _fake_weights(257)[0], taps)[0] == bd.DFLASH_ERR_UNSUPPORTED
+
+
 def test_rope_table_values():
     max_pos, D, theta = 300, 64, 1e6
     out = np.empty(max_pos * D // 2 * 2, np.float32)
