@@ -61,15 +61,17 @@ def synth_target(torch, draft, m, rnd, vocab):
     return torch.where((j == m[:, None]) & (m[:, None] < bm1), (d_ext + 1) % (vocab - 1), t)
 
 
-def target_verify(cfg, W, lens, args):
+def target_verify(cfg, W, lens, args, dr):
     """The target side of a step: one causal pass of the target model over the
     B block tokens of every sequence (argmax + taps), timed over repeated
     passes at the workload's context (each pass rewrites the same speculative
-    slots; nothing is committed)."""
+    slots; nothing is committed); a one-token pass (greedy decoding's cost per
+    token); and a whole speculative step on the device (draft, target pass,
+    verify, both commits) replayed from a captured graph."""
     import torch
 
     from block_diffusion_drafter_target_amd import DeviceTarget, synth
-    from block_diffusion_drafter_target_amd import binding as bd
+    from block_diffusion_drafter_target_amd.drafter import _LoopState, device_step
 
     if not cfg.target_layers:
         raise SystemExit(f"config {cfg.name} has no target model")
@@ -78,7 +80,9 @@ def target_verify(cfg, W, lens, args):
     TW = synth.make_target_weights(cfg, W)
     log(f"target weights ({cfg.target_layers} layers) generated in {time.time() - t0:.1f} s")
     L = int(lens.max())
-    tgt = DeviceTarget(cfg, TW, cfg.target_layers, cfg.tap_layers, batch=batch, max_ctx=L + 2 * B + 64, max_n=B)
+    loop_steps = 16
+    tgt = DeviceTarget(cfg, TW, cfg.target_layers, cfg.tap_layers, batch=batch,
+                       max_ctx=L + (2 * loop_steps + 4) * B + 64, max_n=B)
     del TW
     # prefill every sequence's context in passes of B tokens (ragged contexts:
     # a sequence keeps only its own length through the commit of all rows
@@ -106,13 +110,53 @@ def target_verify(cfg, W, lens, args):
     torch.cuda.synchronize()
     us = 1e3 * start.elapsed_time(stop) / reps
     assert int(tgt.status.abs().max()) == 0
+    # one token per sequence: greedy decoding's cost per token
+    one = toks[:, :1].contiguous()
+    tgt.pass_tokens(one)
+    start.record()
+    for _ in range(reps):
+        tgt.pass_tokens(one)
+    stop.record()
+    torch.cuda.synchronize()
+    us_one = 1e3 * start.elapsed_time(stop) / reps
+    # whole steps on the device, captured in a graph (the drafter keeps its
+    # own context from the timed draft steps; both caches grow by the
+    # accepted rows of every step)
+    st = _LoopState(torch, batch, B, 2 * loop_steps + 2, dev, None)
+    st.budget.fill_(1 << 30)
+    dr.status.zero_()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(loop_steps):
+                device_step(dr, tgt, st)
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    acc0 = int(st.cursor.sum())
+    start.record()
+    g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    us_step = 1e3 * start.elapsed_time(stop) / loop_steps
+    emitted = (int(st.cursor.sum()) - acc0) / (loop_steps * batch)
+    assert int(tgt.status.abs().max()) == 0 and int(dr.status.abs().max()) == 0
+    del g
     V, I, NLt = cfg.vocab, cfg.intermediate, cfg.target_layers
     layer_bytes = 2 * H * (cfg.qkv_width + cfg.q_width + 2 * I) + 2 * I * H
     wbytes = NLt * layer_bytes + V * H * 2
     res = {"layers": NLt, "taps": list(cfg.tap_layers), "tokens_per_pass": batch * B, "context": L,
            "us_per_pass": round(us, 1), "weight_bytes": wbytes,
            "weight_stream_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
-           "weight_stream_frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+           "weight_stream_frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "us_per_one_token_pass": round(us_one, 1),
+           "device_step_us": round(us_step, 1),
+           "device_step_tokens_per_seq": round(emitted, 3),
+           "device_step_note": ("draft + target pass + verify + both commits, graph-replayed; "
+                                "tokens per step measured with untrained synthetic weights")}
     del tgt
     torch.cuda.empty_cache()
     return res
@@ -348,9 +392,8 @@ def main():
         "phases": phases,
     }
     if args.target_verify:
-        del dr
-        torch.cuda.empty_cache()
-        out["target_verify"] = target_verify(cfg, W, lens, args)
+        out["target_verify"] = target_verify(cfg, W, lens, args, dr)
+    del dr
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(cfg, W, int(lens.max()), args.cpu_repeats)

@@ -7,6 +7,6 @@ device buffers into its entry points (``binding``) and drives the greedy
 speculative loop (``drafter``). torch is imported only when a Drafter is used.
 """
 from . import binding, synth  # noqa: F401
-from .drafter import DeviceTarget, Drafter, spec_generate  # noqa: F401
+from .drafter import DeviceTarget, Drafter, spec_generate, spec_generate_device  # noqa: F401
 
-__all__ = ["synth", "binding", "Drafter", "DeviceTarget", "spec_generate"]
+__all__ = ["synth", "binding", "Drafter", "DeviceTarget", "spec_generate", "spec_generate_device"]

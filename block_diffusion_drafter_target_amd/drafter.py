@@ -325,3 +325,136 @@ def spec_generate(drafter: Drafter, target: Target, prompt: Sequence[int], max_n
         if int(drafter.done.item()):
             break
     return out[:max_new_tokens], ms
+
+
+# ---------------------------------------------------------------------------
+# the whole greedy loop on the device
+# ---------------------------------------------------------------------------
+
+class _LoopState:
+    """Device buffers of spec_generate_device (fixed shapes, so a step can be
+    captured in a graph)."""
+
+    def __init__(self, torch, batch, B, max_new, dev, stops):
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.tokens = torch.zeros((batch, B), **i32)       # target input [anchor, d_1..d_{B-1}]
+        self.out = torch.full((batch, max_new + 1), -1, **i32)  # last column: sink of unused lanes
+        self.cursor = torch.zeros(batch, **i32)
+        self.alive = torch.ones(batch, **i32)
+        self.budget = torch.zeros(batch, **i32)
+        self.lane = torch.arange(B, **i32)[None, :]
+        self.row = (torch.arange(batch, **i32) * (max_new + 1))[:, None]
+        self.stops = stops
+        self.max_new = max_new
+
+
+def _prefill_device(drafter: Drafter, target: DeviceTarget, prompts, st: _LoopState):
+    """Target passes over the prompts (passes of up to max_n tokens, ragged
+    prompts committed row by row), the drafter's fuse + inject of the same
+    rows, and the first anchor (the target's token after each prompt)."""
+    torch = _torch()
+    dev, batch = target.device, target.batch
+    P = max(len(p) for p in prompts)
+    anchor = np.zeros(batch, np.int32)
+    for i0 in range(0, P, target.max_n):
+        n = min(target.max_n, P - i0)
+        toks = np.zeros((batch, n), np.int32)
+        rows = []
+        for b, p in enumerate(prompts):
+            for j in range(n):
+                if i0 + j < len(p):
+                    toks[b, j] = p[i0 + j]
+                    rows.append((b * n + j, b, i0 + j))
+        a, taps = target.pass_tokens(torch.from_numpy(toks).to(dev))
+        crow = torch.zeros((batch * n, 3), dtype=torch.int32, device=dev)
+        if rows:
+            crow[:len(rows)] = torch.tensor(rows, dtype=torch.int32, device=dev)
+        cnt = torch.tensor([len(rows)], dtype=torch.int32, device=dev)
+        target.commit(crow, cnt, batch * n)
+        drafter.fuse_ctx(taps, batch * n, drafter.ctx)
+        drafter.inject_kv(drafter.ctx, batch * n, crow, cnt, batch * n)
+        a = a.cpu().numpy()
+        for b, p in enumerate(prompts):
+            if i0 <= len(p) - 1 < i0 + n:
+                anchor[b] = a[b, len(p) - 1 - i0]
+    drafter.anchor.copy_(torch.from_numpy(anchor))
+    return anchor
+
+
+def device_step(drafter: Drafter, target: DeviceTarget, st: _LoopState) -> None:
+    """One speculative step with no host synchronisation: draft, target pass
+    over [anchor, draft], verify, commit in both caches, next anchor, and the
+    emitted tokens of sequences still running appended to the output."""
+    torch = _torch()
+    B = drafter.cfg.block
+    batch = drafter.batch
+    drafter.draft_block(anchor=drafter.anchor)
+    st.tokens[:, 0].copy_(drafter.anchor)
+    st.tokens[:, 1:].copy_(drafter.draft)
+    a, taps = target.pass_tokens(st.tokens)
+    drafter.verify_accept(a, st.stops, st.budget)
+    target.commit(drafter.commit_rows, drafter.n_commit, batch * B)
+    drafter.fuse_ctx(taps, batch * B, drafter.ctx)
+    drafter.inject_kv(drafter.ctx, batch * B, drafter.commit_rows, drafter.n_commit, batch * B)
+    drafter.anchor.copy_(drafter.anchor_out)
+    n = drafter.n_emit * st.alive
+    pos = st.cursor[:, None] + st.lane
+    keep = (st.lane < n[:, None]) & (pos < st.max_new)
+    # kept lanes write distinct slots; every other lane writes the sink column
+    idx = (st.row + torch.where(keep, pos, st.max_new)).reshape(-1)
+    st.out.view(-1).scatter_(0, idx, drafter.emitted.reshape(-1))
+    st.cursor += n
+    st.alive *= 1 - drafter.done
+
+
+def spec_generate_device(drafter: Drafter, target: DeviceTarget, prompts, max_new_tokens: int,
+                         stop_token_ids: Sequence[int] = (), steps_per_sync: int = 8, graph: bool = True):
+    """Greedy speculative decoding of a batch with the drafter and the target on
+    the device: steps run without host synchronisation (``steps_per_sync`` of
+    them captured in one graph when ``graph``), stop ids and the token budget
+    are applied on the device, and the host only checks between groups of
+    steps whether every sequence has finished. Returns the tokens of each
+    sequence (as spec_generate does for one)."""
+    torch = _torch()
+    if drafter.batch != target.batch or len(prompts) != drafter.batch:
+        raise ValueError("one prompt per sequence of the drafter and the target")
+    if target.max_n < drafter.cfg.block:
+        raise ValueError("the target's passes must hold a whole block")
+    dev = drafter.device
+    B = drafter.cfg.block
+    stops = torch.tensor(list(stop_token_ids), dtype=torch.int32, device=dev) if stop_token_ids else None
+    st = _LoopState(torch, drafter.batch, B, max_new_tokens, dev, stops)
+    target.reset()
+    drafter.ctx_len.zero_()
+    drafter.status.zero_()
+    anchor = _prefill_device(drafter, target, [list(p) for p in prompts], st)
+    st.out[:, 0] = torch.from_numpy(anchor).to(dev)
+    st.cursor.fill_(1)
+    stop_set = set(int(x) for x in stop_token_ids)
+    st.alive.copy_(torch.tensor([0 if int(a) in stop_set or max_new_tokens <= 1 else 1 for a in anchor],
+                                dtype=torch.int32))
+    st.budget.fill_(max_new_tokens - 1)
+    g = None
+    if graph:
+        # capture records the steps without running them; every replay then
+        # advances the state in place
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(steps_per_sync):
+                    device_step(drafter, target, st)
+        torch.cuda.current_stream().wait_stream(s)
+    for _ in range(0, max_new_tokens + steps_per_sync, steps_per_sync):
+        if g is not None:
+            g.replay()
+        else:
+            for _ in range(steps_per_sync):
+                device_step(drafter, target, st)
+        if int(st.alive.max()) == 0 or int(st.cursor.min()) >= max_new_tokens:
+            break
+    out = st.out.cpu().numpy()
+    cur = st.cursor.cpu().numpy()
+    return [list(int(t) for t in out[b, :min(int(cur[b]), max_new_tokens)]) for b in range(drafter.batch)]

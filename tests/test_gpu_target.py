@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import gpu_helpers as gh
-from block_diffusion_drafter_target_amd import DeviceTarget, Drafter, spec_generate, synth
+from block_diffusion_drafter_target_amd import DeviceTarget, Drafter, spec_generate, spec_generate_device, synth
 from oracle import ref
 
 pytestmark = pytest.mark.gpu
@@ -141,3 +141,36 @@ def test_loop_lossless_with_device_target(gpu_lib):
     oracle = ref.greedy_generate(_oracle_target(cfg, ref.OracleConfig.from_any(cfg), TW), prompt, cfg.n_new)
     same = next((i for i, (x, y) in enumerate(zip(greedy, oracle)) if x != y), len(oracle))
     gh.log(f"    device greedy equals the fp64 oracle's greedy decoding for the first {same}/{len(oracle)} tokens")
+
+
+def test_device_loop_matches_host_loop(gpu_lib):
+    """The loop with no per-step host synchronisation (steps captured in a
+    graph, and run eagerly), over a batch of two prompts of different lengths
+    with a stop id, emits per sequence exactly what the host-driven loop does
+    for that prompt alone."""
+    cfg = synth.CONFIGS["c1"]
+    W = synth.make_weights(cfg)
+    TW = synth.make_target_weights(cfg, W)
+    prompts = [list(synth.make_prompt(cfg, 64)), list(synth.make_prompt(cfg, 37, seed=11))]
+    n_new, S = cfg.n_new, 4
+    max_ctx = 64 + n_new + (S + 2) * cfg.block + 16
+    ref_out = []
+    for p in prompts:
+        tgt1 = DeviceTarget(cfg, TW, cfg.target_layers, cfg.tap_layers, max_ctx=max_ctx, max_n=16)
+        dr1 = Drafter(cfg, W, batch=1, max_ctx=max_ctx, max_rows=64)
+        ref_out.append(spec_generate(dr1, tgt1, p, n_new)[0])
+        del tgt1, dr1
+    tgt = DeviceTarget(cfg, TW, cfg.target_layers, cfg.tap_layers, batch=2, max_ctx=max_ctx, max_n=16)
+    dr = Drafter(cfg, W, batch=2, max_ctx=max_ctx, max_rows=2 * 16)
+    for graph in (True, False):
+        out = spec_generate_device(dr, tgt, prompts, n_new, steps_per_sync=S, graph=graph)
+        assert out == ref_out, f"graph={graph}"
+    # a stop id (the 21st token of the first sequence) ends that sequence there
+    stop = ref_out[0][20]
+    want = []
+    for r in ref_out:
+        cut = r.index(stop) + 1 if stop in r else len(r)
+        want.append(r[:cut])
+    out = spec_generate_device(dr, tgt, prompts, n_new, stop_token_ids=[stop], steps_per_sync=S, graph=True)
+    assert out == want
+    gh.log(f"[device loop] lengths {[len(o) for o in out]}")
