@@ -66,6 +66,7 @@ inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct GemmPlan {
+  bool big;    // large-tile kernel (256 x 256 tiles) over all rows
   bool tiled;  // LDS-tiled kernel over all rows, or the streaming kernel per kGemmRows rows
   int mt, nf;  // streaming: activation tiles and weight fragments per workgroup
   int ng;      // tiled: weight row groups per wave (64*ng columns per workgroup); mt: 16-row tiles
@@ -74,15 +75,19 @@ struct GemmPlan {
 };
 
 constexpr int kStreamMaxRows = 32;   // more rows take the tiled kernel
+constexpr int kBigMinRows = 256;     // this many rows take the large-tile kernel
+constexpr int kBigSlots = 256;       // large-tile workgroups resident at once (one per CU)
 constexpr int kSwigluMinWGs = 256;   // fewer single-pass SwiGLU workgroups: split-K path
 
 // Kernel, tile shape and split-K for Y = A W^T.
+// From kBigMinRows rows: the large-tile kernel (256 x 256 tiles, both
+// operands staged through LDS; the product is bound by the matrix cores).
 // Up to kStreamMaxRows rows (or K < 128): the weight-streaming kernel with
 // NF = 2 weight fragments per workgroup (measured best on MI355X with cold
 // caches: more waves in flight beat wider tiles); split-K only in partial
 // mode, to bring the grid to about kTargetWGs workgroups (1024 when there are
 // at most 128 column tiles: longer splits per workgroup measured slower
-// there). More rows: the
+// there). Up to kBigMinRows rows: the
 // tiled kernel (activations shared through LDS) with 64 or 128 activation
 // rows per tile. Its split-K partials cost 2*splits*M/K bytes per weight
 // byte: with one row tile (HBM-bound) splits aim for 256 workgroups at 128
@@ -95,6 +100,28 @@ constexpr int kSwigluMinWGs = 256;   // fewer single-pass SwiGLU workgroups: spl
 GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
   GemmPlan g;
   g.swiglu_split = false;
+  g.big = false;
+  if (M >= kBigMinRows && K >= 32) {
+    // Large tiles (one 512-thread workgroup per CU). Split-K only in partial
+    // mode and only while the grid still fits one round of kBigSlots
+    // workgroups: a second, partly filled round costs more than the split
+    // saves (c3, 512 rows: qkv 240 workgroups at 5 splits, o and down 256 at
+    // 8; 6 splits of qkv, 288 workgroups, measured 47% slower than 4).
+    g.big = true;
+    g.tiled = false;
+    g.mt = g.nf = g.ng = 0;
+    const long long base = cdiv(M, dfl::gemm_big_rows()) * cdiv(N, dfl::gemm_big_cols(mode)) * nz;
+    const int chunks = K / 32;
+    int s = 1;
+    if (mode == dfl::kGemmPartial && base < kBigSlots) {
+      s = (int)(kBigSlots / base);
+      s = std::min(s, std::max(1, chunks / 8));  // at least 256 k per split
+    }
+    const int per = (int)cdiv(chunks, s);
+    g.splits = (int)cdiv(chunks, per);
+    g.k_per_split = per * 32;
+    return g;
+  }
   if (M > kStreamMaxRows && K >= 128) {
     g.tiled = true;
     g.nf = 0;
@@ -148,6 +175,7 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
 // tile and row).
 int lm_tiles(const dflash_config& c, int M) {
   const GemmPlan g = plan_gemm(M, c.vocab, c.hidden, 1, dfl::kGemmArgmax);
+  if (g.big) return (int)cdiv(c.vocab, dfl::gemm_big_cols(dfl::kGemmArgmax));
   return (int)(g.tiled ? cdiv(c.vocab, 64 * g.ng) : cdiv(c.vocab, 16 * g.nf));
 }
 
@@ -204,7 +232,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     sc.ld_out = c.ld_out;
     return dfl::launch_swiglu_combine(sc, st);
   }
-  if (g.tiled) {
+  if (g.tiled || g.big) {
     GemmParams p;
     std::memset(&p, 0, sizeof(p));
     p.A = c.A;
@@ -233,7 +261,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     p.P = c.P;
     p.p_s_stride = (long long)c.M * c.N;
     p.p_z_stride = (long long)g.splits * c.M * c.N;
-    return dfl::launch_gemm_tile(p, g.ng, g.mt, c.mode, c.nz, st);
+    return g.big ? dfl::launch_gemm_big(p, c.mode, c.nz, st) : dfl::launch_gemm_tile(p, g.ng, g.mt, c.mode, c.nz, st);
   }
   for (int m0 = 0; m0 < c.M; m0 += kGemmRows) {
     GemmParams p;
