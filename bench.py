@@ -29,6 +29,7 @@ import numpy as np
 
 METRIC = "draft-step latency (µs) + drafted tokens/s, 5-layer drafter, block 16; %roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 
 
 def log(*a):
@@ -242,11 +243,15 @@ def main():
     dev = torch.device("cuda")
     dr = Drafter(cfg, W, batch=batch, max_ctx=max_ctx, max_rows=max(int(lens.max()), batch * B), device=dev)
 
-    # context ingest (fuse + inject of the whole prompt), timed on its own
+    # context ingest (fuse + inject of the whole prompt), timed on its own:
+    # every sequence is ingested twice (the same rows into the same slots) and
+    # the second pass is timed, so that first-launch costs stay out of it
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ingest_ms = 0.0
     for b in range(batch):
         taps = torch.from_numpy(synth.make_taps(cfg, int(lens[b]), tid=b).view(np.int16)).view(torch.bfloat16).to(dev)
+        dr.ingest(b, taps)
+        torch.cuda.synchronize()
         ev0.record()
         dr.ingest(b, taps)
         ev1.record()
@@ -254,6 +259,8 @@ def main():
         ingest_ms += ev0.elapsed_time(ev1)
         del taps
     assert dr.ctx_len.cpu().numpy().tolist() == lens.tolist()
+    ingest_rows = int(lens.sum())
+    ingest_flop = 2.0 * ingest_rows * H * (cfg.tap_width + cfg.n_layers * cfg.kv_width * 2)
 
     # per-step synthetic inputs, resident before timing
     taps_step = torch.from_numpy(synth.make_taps(cfg, batch * B, tid=999).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -388,6 +395,10 @@ def main():
         "step_weight_bytes": step_weight_bytes,
         "step_weight_stream_frac": round(step_weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "ingest_ms": round(ingest_ms, 3),
+        "ingest": {"rows": ingest_rows, "gflop": round(ingest_flop * 1e-9, 1),
+                   "tflops": round(ingest_flop / (ingest_ms * 1e-3) * 1e-12, 1),
+                   "mfma_frac": round(ingest_flop / (ingest_ms * 1e-3) * 1e-12 / MFMA_PEAK_TFLOPS, 4),
+                   "note": "fuse + inject of every context row (GEMM flops), second pass timed"},
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "phases": phases,
     }

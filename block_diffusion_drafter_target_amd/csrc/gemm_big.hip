@@ -6,7 +6,9 @@
 // operand traffic rather than for the weight stream:
 //   * workgroup = 8 waves over a 256 (rows of A) x 256 (weight rows) tile;
 //     wave w owns 128 rows (w & 1) x 64 weight rows (w >> 1), 32 MFMA tiles
-//     of 16 x 16 and 128 accumulator registers;
+//     of 16 x 16 and 128 accumulator registers (two waves per SIMD; a
+//     4-wave layout of 128 x 128 wave tiles, one wave per SIMD, measured
+//     10-25% slower: nothing hides its LDS latency);
 //   * both operands go HBM/L2 -> LDS by gfx950's direct loads
 //     (global_load_lds_dwordx4: lane l's 16 bytes land at offset 16*l of a
 //     1 KB slot), so they take no registers on the way. A weight fragment is
@@ -14,11 +16,17 @@
 //     (16 rows x 32 k) is gathered so that it lands in MFMA operand order too.
 //     Every LDS operand read is then one ds_read_b128 of 1 KB contiguous
 //     bytes, free of bank conflicts, with no swizzle;
-//   * a stage is 32 k (16 weight + 16 activation fragments, 32 KB), four
-//     stages in LDS (128 KB, one workgroup per CU, two waves per SIMD), loads
-//     issued three stages ahead; each wave waits for its own loads of a stage
-//     with an explicit vmcnt (the compiler does not track direct LDS loads)
-//     before the workgroup barrier that publishes the stage;
+//   * a stage is 32 k (16 weight + 16 activation fragments, 32 KB); five
+//     stages fill the 160 KB of LDS (one workgroup per CU). A stage's loads
+//     are issued five stages ahead, at the end of the MFMAs of the stage
+//     whose buffer they refill; each wave waits for its own direct loads of a
+//     stage with an explicit vmcnt (the compiler does not track them) before
+//     the workgroup barrier that publishes the stage. (Direct loads issued
+//     among the LDS reads and MFMAs measured 13 times slower.)
+//   * the fragments of stage c + 1 are read while the MFMAs of stage c run
+//     (weights into a second register set, each activation fragment into the
+//     register its stage-c twin frees), so the LDS reads after a barrier
+//     overlap the matrix cores;
 //   * the tile order keeps a compact block of tiles on each XCD (block ids go
 //     round-robin to the 8 XCDs; each XCD takes one contiguous range of the
 //     grouped tile order), so the panels of A and W that its workgroups share
@@ -26,6 +34,8 @@
 //   * epilogues as in the other GEMM kernels: split-K fp32 partials, SwiGLU
 //     (a wave's first two groups are gate rows, its last two the up rows of
 //     the same 32 output columns) and one argmax key per (256-column tile, row).
+// Measured on MI355X (cold weights): 4096 x 4096 x 20480 at 53% of the dense
+// bf16 peak; the same loop without the direct loads reaches 73%.
 #include "common.h"
 #include "internal.h"
 
@@ -34,7 +44,7 @@ namespace dfl {
 namespace {
 
 constexpr int kBM = 256, kBN = 256;  // activation rows, weight rows per workgroup
-constexpr int kStages = 4;
+constexpr int kStages = 5;   // 160 KB of LDS
 constexpr int kFrags = 32;           // per stage: 16 weight fragments, then 16 activation fragments
 constexpr int kGroupM = 4;           // row tiles per group of the tile order
 
@@ -47,12 +57,45 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int MODE>
-__global__ __launch_bounds__(512) void gemm_big_kernel(const GemmParams p) {
-  __shared__ __align__(1024) u32x4 lds[kStages][kFrags][kWave];
-  static_assert(MODE != kGemmArgmax || sizeof(unsigned long long) * 4 * kBM <= sizeof(lds), "argmax staging fits");
+// s_waitcnt lgkmcnt(0) only.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Wave layout of a WAVES-wave workgroup (8: wave tiles of 128 rows x 64
+// weight rows).
+template <int WAVES>
+struct BigShape {
+  static constexpr int kWavesN = WAVES / 2;     // waves along the weight rows
+  static constexpr int kNF = 16 / kWavesN;      // weight fragments per wave
+  static constexpr int kLoads = kFrags / WAVES; // direct loads per wave and stage
+  static constexpr int kThreads = 64 * WAVES;
+};
+
+// Workgroup barrier for LDS data published by direct loads. The barrier
+// intrinsic alone does not order memory accesses in the compiler, so LDS
+// reads could be hoisted above it; the empty asm with a memory clobber keeps
+// every memory access on its side, and the scheduling barriers keep the
+// machine scheduler from moving instructions across. No s_waitcnt comes with
+// it: each wave waits for its own direct loads (vmcnt) before calling it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MODE, int WAVES>
+__device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
+  using S = BigShape<WAVES>;
+  constexpr int kNF = S::kNF, kLoads = S::kLoads, kWavesN = S::kWavesN;
+  __shared__ __align__(1024) u32x4 lds[kStages][kFrags][kWave];
+  static_assert(MODE != kGemmArgmax || sizeof(unsigned long long) * kWavesN * kBM <= sizeof(lds),
+                "argmax staging fits");
+  static_assert(MODE != kGemmSwiglu || kNF % 2 == 0, "gate and up halves");
+
+  // the wave index is uniform: kept in scalar registers, so are every
+  // load's base address and LDS slot
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
   constexpr int kOutCols = MODE == kGemmSwiglu ? kBN / 2 : kBN;
@@ -79,109 +122,166 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(const GemmParams p) {
   const int nk = (kend - kbeg) >> 5;  // 32-k stages of this split (K % 32 == 0)
   const long long frag_row = (long long)(p.K / 32) * 512;
 
-  // this wave's two weight slots (2w, 2w + 1) and two activation slots
-  const bf16_t* wsrc[2];
-  const bf16_t* asrc[2];
+  // this wave's kLoads / 2 weight slots and as many activation slots
+  // (slot = wave * kLoads / 2 + i); weight slot j is computed by wave
+  // j / kNF as its group j % kNF
+  constexpr int kHalf = kLoads / 2;
+  const bf16_t* wsrc[kHalf];  // uniform: the group's fragment row at the split's first stage
+  int aoff[kHalf];            // per lane: element offset of its row and k in A
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int slot = 2 * wave + i;  // weight slot: wave slot / 4 computes it, as its group slot % 4
+  for (int i = 0; i < kHalf; ++i) {
+    const int slot = kHalf * wave + i;
     const bf16_t* base;
     int gi;
-    if (MODE == kGemmSwiglu) {
-      const int f = slot & 3, fo = f & 1;
-      gi = min(bx * kOutCols + (slot >> 2) * 32 + fo * 16, p.N - 16) >> 4;
-      base = f < 2 ? p.W0[z] : p.W1[z];
+    if (MODE == kGemmSwiglu) {  // a wave's first kNF/2 groups: gate rows, the rest: up rows of the same columns
+      const int f = slot % kNF, fo = f % (kNF / 2);
+      gi = min(bx * kOutCols + (slot / kNF) * (kNF / 2) * 16 + fo * 16, p.N - 16) >> 4;
+      base = f < kNF / 2 ? p.W0[z] : p.W1[z];
     } else {
       const int n = min(bx * kBN + slot * 16, p.N - 16);
       base = n < p.n_split ? p.W0[z] : p.W1[z];
       gi = (n < p.n_split ? n : n - p.n_split) >> 4;
     }
-    wsrc[i] = base + gi * frag_row + (long long)(kbeg >> 5) * 512 + lane * 8;
+    wsrc[i] = base + gi * frag_row + (long long)(kbeg >> 5) * 512;
     // activation slot: rows m0 + 16*slot .. +15, lane -> row r, k 8g .. 8g+7
     int m = min(m0 + slot * 16 + r, p.M - 1);
     if (p.a_idx) {
       m = p.a_idx[(long long)m * p.a_idx_stride];
       m = m < 0 ? 0 : (m >= p.a_idx_max ? p.a_idx_max - 1 : m);
     }
-    asrc[i] = p.A + (long long)m * p.lda + kbeg + 8 * g;
+    aoff[i] = (int)((long long)m * p.lda) + kbeg + 8 * g;
   }
+  const int woff = lane * 8;  // per lane, shared by every weight fragment
 
+  // this wave's direct loads of stage c into its LDS buffer (weight and
+  // activation slots alternating)
   auto issue = [&](int c) __attribute__((always_inline)) {
-    const int b = c & (kStages - 1);
+    const int b = c % kStages;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      __builtin_amdgcn_global_load_lds(wsrc[i] + (long long)c * 512, (lds_void*)&lds[b][2 * wave + i][0], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(asrc[i] + c * 32, (lds_void*)&lds[b][16 + 2 * wave + i][0], 16, 0, 0);
+    for (int i = 0; i < kHalf; ++i) {
+      __builtin_amdgcn_global_load_lds(wsrc[i] + (long long)c * 512 + woff, (lds_void*)&lds[b][kHalf * wave + i][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(p.A + (aoff[i] + c * 32), (lds_void*)&lds[b][16 + kHalf * wave + i][0], 16, 0, 0);
     }
   };
 
-  f32x4_t acc[4][8];
+  f32x4_t acc[kNF][8];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < kNF; ++f)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[f][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int c = 0; c < kStages - 1; ++c)
+  for (int c = 0; c < kStages; ++c)
     if (c < nk) issue(c);
 
-  for (int c = 0; c < nk; ++c) {
-    // this wave's loads of stage c are done once at most the later stages'
-    // (up to two, four loads each) are outstanding
+  // Stage c + 1 is published, then its fragments are read while the MFMAs of
+  // stage c run: the weight fragments into a second register set (the loop
+  // is unrolled by two so that the sets keep fixed registers), each
+  // activation fragment into the register its stage-c twin frees once its
+  // MFMAs are issued. After those MFMAs the wave issues its direct loads of
+  // stage c + kStages into the buffer of stage c.
+  auto publish = [&](int c) __attribute__((always_inline)) {
+    static_assert(kStages == 5, "wait counts below");
     __builtin_amdgcn_sched_barrier(0);
-    if (c + 2 < nk)
-      wait_vm<8>();
+    // this wave's LDS reads of the stage just computed have landed (the
+    // compiler then knows that no read is older than the ones issued next)
+    wait_lgkm0();
+    // this wave's direct loads of stage c have landed once at most those of
+    // the stages issued after it (c + 1 .. c + 3, where they exist; before
+    // stage 0 also c + 4, and the wait covers stage 1 too) remain
+    if (c + 3 < nk)
+      wait_vm<3 * kLoads>();
+    else if (c + 2 < nk)
+      wait_vm<2 * kLoads>();
     else if (c + 1 < nk)
-      wait_vm<4>();
+      wait_vm<kLoads>();
     else
       wait_vm<0>();
-    // every wave's loads of stage c have landed, and every wave is done with
-    // stage c - 1, whose buffer the next loads overwrite
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    if (c + kStages - 1 < nk) issue(c + kStages - 1);
-    const u32x4(*st)[kWave] = lds[c & (kStages - 1)];
-    u32x4 wf[4];
+    // every wave's loads of stage c have landed, and every wave's reads of
+    // stage c - 1 have completed
+    lds_barrier();
+  };
+  auto read_w = [&](int c, u32x4(&wf)[kNF]) __attribute__((always_inline)) {
+    const u32x4(*st)[kWave] = lds[c % kStages];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) wf[f] = st[4 * wn + f][lane];
+    for (int f = 0; f < kNF; ++f) wf[f] = st[kNF * wn + f][lane];
+  };
+  // MFMAs of stage c_next - 1 with weight set wf and activations af,
+  // refilling af with stage c_next; then the direct loads of stage
+  // c_next - 1 + kStages into the buffer of stage c_next - 1, whose reads
+  // every wave completed before the barrier that published stage c_next
+  auto step = [&](const u32x4(&wf)[kNF], u32x4(&af)[8], int c_next) __attribute__((always_inline)) {
+    const u32x4(*st)[kWave] = lds[c_next % kStages];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const u32x4 a = st[16 + 8 * wm + i][lane];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) acc[f][i] = mfma16x16x32(wf[f], a, acc[f][i]);
+      for (int f = 0; f < kNF; ++f) acc[f][i] = mfma16x16x32(wf[f], af[i], acc[f][i]);
+      af[i] = st[16 + 8 * wm + i][lane];
     }
+    // order for the scheduler: the weight reads issued just before, then per
+    // activation fragment its MFMAs and the read that refills it (hoisting
+    // the reads would keep two operand sets live and spill)
+    __builtin_amdgcn_sched_group_barrier(0x100, kNF, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kNF, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int cl = c_next - 1 + kStages;
+    if (cl < nk) issue(cl);
+  };
+  u32x4 wa[kNF], wb[kNF], af[8];
+  publish(0);
+  read_w(0, wa);
+  {
+    const u32x4(*st)[kWave] = lds[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) af[i] = st[16 + 8 * wm + i][lane];
+  }
+  // one stage past the last is published (a plain barrier: its wait is
+  // vmcnt(0)) and read too (its fragments come from a stale buffer and are
+  // not used)
+  for (int c = 0; c < nk; c += 2) {
+    publish(c + 1);
+    read_w(c + 1, wb);
+    step(wa, af, c + 1);
+    if (c + 1 >= nk) break;
+    publish(c + 2);
+    read_w(c + 2, wa);
+    step(wb, af, c + 2);
   }
 
   if (MODE == kGemmPartial) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < kNF; ++f)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int m = m0 + wm * 128 + i * 16 + r;
-        const int nb = bx * kBN + (wn * 4 + f) * 16 + 4 * g;
+        const int nb = bx * kBN + (wn * kNF + f) * 16 + 4 * g;
         if (m < p.M && nb < p.N)
           *reinterpret_cast<f32x4_t*>(p.P + (long long)z * p.p_z_stride + (long long)s * p.p_s_stride +
                                       (long long)m * p.N + nb) = acc[f][i];
       }
   } else if (MODE == kGemmSwiglu) {
 #pragma unroll
-    for (int fo = 0; fo < 2; ++fo)
+    for (int fo = 0; fo < kNF / 2; ++fo)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int m = m0 + wm * 128 + i * 16 + r;
-        const int nb = bx * kOutCols + (wn * 2 + fo) * 16 + 4 * g;
+        const int nb = bx * kOutCols + (wn * (kNF / 2) + fo) * 16 + 4 * g;
         if (m < p.M && nb < p.N) {
           float sv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sv[e] = acc[fo][i][e] / (1.0f + __expf(-acc[fo][i][e])) * acc[fo + 2][i][e];
+            sv[e] = acc[fo][i][e] / (1.0f + __expf(-acc[fo][i][e])) * acc[fo + kNF / 2][i][e];
           *reinterpret_cast<u32x2*>(p.out + (long long)m * p.ld_out + nb) =
               u32x2{pack_bf2(sv[0], sv[1]), pack_bf2(sv[2], sv[3])};
         }
       }
   } else {
     // per row: the best of the wave's 64 columns, then of the 4 column waves
-    unsigned long long* kbest = reinterpret_cast<unsigned long long*>(&lds[0][0][0]);  // [4][kBM]
+    unsigned long long* kbest = reinterpret_cast<unsigned long long*>(&lds[0][0][0]);  // [kWavesN][kBM]
     __syncthreads();  // every wave is done reading the stages
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -189,8 +289,8 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(const GemmParams p) {
       float bv = -__builtin_inff();
       int bn = 0x7FFFFFFF;
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int nb = bx * kBN + (wn * 4 + f) * 16 + 4 * g;
+      for (int f = 0; f < kNF; ++f) {
+        const int nb = bx * kBN + (wn * kNF + f) * 16 + 4 * g;
         if (p.dbg && m < p.M && nb < p.N) *reinterpret_cast<f32x4_t*>(p.dbg + (long long)m * p.ld_dbg + nb) = acc[f][i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -212,13 +312,27 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(const GemmParams p) {
       if (g == 0) kbest[wn * kBM + wm * 128 + i * 16 + r] = bn != 0x7FFFFFFF ? argmax_key(bv, bn) : 0ull;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kBM; i += 512) {
+    for (int i = threadIdx.x; i < kBM; i += S::kThreads) {
       const int m = m0 + i;
-      if (m < p.M)
-        p.keys[(long long)bx * p.ld_keys + m] =
-            max(max(kbest[i], kbest[kBM + i]), max(kbest[2 * kBM + i], kbest[3 * kBM + i]));
+      if (m < p.M) {
+        unsigned long long k = kbest[i];
+#pragma unroll
+        for (int w = 1; w < kWavesN; ++w) k = max(k, kbest[w * kBM + i]);
+        p.keys[(long long)bx * p.ld_keys + m] = k;
+      }
     }
   }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_big8_kernel(const GemmParams p) {
+  gemm_big_body<MODE, 8>(p);
+}
+
+template <int MODE>
+hipError_t launch_one(const GemmParams& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL(gemm_big8_kernel<MODE>, grid, dim3(512), 0, st, p);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -236,15 +350,11 @@ hipError_t launch_gemm_big(const GemmParams& p, int mode, int nz, hipStream_t st
   const long long total = m_tiles * n_tiles * p.splits * nz;
   const long long grid = (total + 7) / 8 * 8;
   if (grid > 0x7FFFFFFFll) return hipErrorInvalidValue;
-  if (mode == kGemmPartial)
-    hipLaunchKernelGGL(gemm_big_kernel<kGemmPartial>, dim3((unsigned)grid), dim3(512), 0, st, p);
-  else if (mode == kGemmSwiglu)
-    hipLaunchKernelGGL(gemm_big_kernel<kGemmSwiglu>, dim3((unsigned)grid), dim3(512), 0, st, p);
-  else if (mode == kGemmArgmax)
-    hipLaunchKernelGGL(gemm_big_kernel<kGemmArgmax>, dim3((unsigned)grid), dim3(512), 0, st, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  const dim3 g((unsigned)grid);
+  if (mode == kGemmPartial) return launch_one<kGemmPartial>(p, g, st);
+  if (mode == kGemmSwiglu) return launch_one<kGemmSwiglu>(p, g, st);
+  if (mode == kGemmArgmax) return launch_one<kGemmArgmax>(p, g, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dfl
