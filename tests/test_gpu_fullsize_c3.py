@@ -2,9 +2,10 @@
 drafter, batch 32, block 16, context lengths uniform in 512..4096 per
 sequence (seeded), then two draft / verify / commit steps.
 
-At 512 block rows every GEMM runs on four 128-row tiles that share each weight
-tile (the shared-weight loads and the XCD-aware tile order), the LM head runs
-on 480 rows, and the attention chunks follow the batch's longest sequence.
+At 512 block rows every GEMM runs on the large-tile kernel: two 256-row tiles
+share each weight tile (direct global-to-LDS loads, the XCD-grouped tile
+order), o and down with 8-way split-K, the LM head on 480 rows (the second row
+tile ragged), and the attention chunks follow the batch's longest sequence.
 The checks are sampled or replayed stage by stage from the device's state:
   * every layer of sequences 0 and 31 (block rows in the first and last row
     tile) from the device's own input and cache, with their block K/V;
