@@ -24,7 +24,8 @@ EXPORTED = ("dflash_model_create", "dflash_model_destroy", "dflash_rope_table",
             "dflash_workspace_bytes", "dflash_fuse_ctx", "dflash_inject_kv",
             "dflash_draft_block", "dflash_verify_accept", "dflash_status_string",
             "dflash_profile_enable", "dflash_profile_read", "dflash_pack_matrix",
-            "dflash_target_create", "dflash_target_forward", "dflash_kv_commit")
+            "dflash_target_create", "dflash_target_forward", "dflash_kv_commit",
+            "dflash_draft_block_sample", "dflash_verify_sample", "dflash_sample_logits")
 
 PHASES = {"lm_head": 0, "attention": 1, "qkv": 2, "o": 3, "gate_up": 4, "down": 5, "fuse": 6,
           "inject": 7, "verify": 8}
@@ -86,6 +87,11 @@ def load() -> C.CDLL:
     lib.dflash_kv_commit.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, i32, vp]
     lib.dflash_verify_accept.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, i32, vp, vp, vp, vp,
                                          vp, vp, vp, vp, vp]
+    u64, f32 = C.c_uint64, C.c_float
+    lib.dflash_draft_block_sample.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, f32, u64, i32, vp, sz, vp]
+    lib.dflash_verify_sample.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, f32, u64, i32, vp, i32, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dflash_sample_logits.argtypes = [vp, vp, i32, f32, u64, i32, i32, vp, vp, sz, vp]
     lib.dflash_pack_matrix.argtypes = [vp, vp, i32, i32, vp]
     lib.dflash_pack_matrix.restype = i32
     lib.dflash_profile_enable.argtypes = [C.c_uint32]
@@ -96,7 +102,8 @@ def load() -> C.CDLL:
     lib.dflash_status_string.restype = C.c_char_p
     for fn in ("dflash_model_create", "dflash_rope_table", "dflash_fuse_ctx", "dflash_inject_kv",
                "dflash_draft_block", "dflash_verify_accept", "dflash_target_create",
-               "dflash_target_forward", "dflash_kv_commit"):
+               "dflash_target_forward", "dflash_kv_commit", "dflash_draft_block_sample",
+               "dflash_verify_sample", "dflash_sample_logits"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -178,6 +185,26 @@ def dflash_verify_accept(model, kv, draft, target_argmax, stop_ids, n_stop, budg
     _check("dflash_verify_accept", load().dflash_verify_accept(
         model, C.byref(kv), draft, target_argmax, stop_ids, n_stop, budget, accept_len, anchor_out,
         emitted, n_emit, done, commit_rows, n_commit, stream))
+
+
+def dflash_draft_block_sample(model, kv, anchor, draft, logits, temperature: float, seed: int, step: int, ws,
+                              ws_bytes, stream) -> None:
+    _check("dflash_draft_block_sample", load().dflash_draft_block_sample(
+        model, C.byref(kv), anchor, draft, logits, temperature, seed, step, ws, ws_bytes, stream))
+
+
+def dflash_verify_sample(model, kv, draft, draft_logits, target_logits, temperature: float, seed: int, step: int,
+                         stop_ids, n_stop, budget, accept_len, anchor_out, emitted, n_emit, done, commit_rows,
+                         n_commit, ws, ws_bytes, stream) -> None:
+    _check("dflash_verify_sample", load().dflash_verify_sample(
+        model, C.byref(kv), draft, draft_logits, target_logits, temperature, seed, step, stop_ids, n_stop,
+        budget, accept_len, anchor_out, emitted, n_emit, done, commit_rows, n_commit, ws, ws_bytes, stream))
+
+
+def dflash_sample_logits(model, logits, rows: int, temperature: float, seed: int, step: int, row0: int, tokens,
+                         ws, ws_bytes, stream) -> None:
+    _check("dflash_sample_logits", load().dflash_sample_logits(model, logits, rows, temperature, seed, step, row0,
+                                                               tokens, ws, ws_bytes, stream))
 
 
 def dflash_pack_matrix(src, dst, rows: int, cols: int, stream) -> None:

@@ -511,6 +511,38 @@ dflash_status dflash_rope_table(float* out, int32_t max_pos, int32_t head_dim, f
   return DFLASH_OK;
 }
 
+namespace {
+
+// Workspace of sampling-mode verification (and of the Gumbel pass of a
+// sampled draft block): log-sum-exps, the target-token row, per-sequence
+// state and the chunk keys.
+struct SampleWs {
+  size_t lse, a, m, rej, keys, total;
+};
+
+SampleWs sample_ws(const dflash_config& c, int batch) {
+  SampleWs w;
+  const int B = c.block;
+  const long long items = std::max<long long>(batch, (long long)batch * (B - 1));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  w.lse = take((size_t)batch * (2 * B - 1) * 4);
+  w.a = take((size_t)batch * B * 4);
+  w.m = take((size_t)batch * 4);
+  w.rej = take((size_t)batch * 4);
+  w.keys = take((size_t)dfl::sample_chunks(c.vocab) * items * 8);
+  w.total = off;
+  return w;
+}
+
+bool sample_temperature_ok(float t) { return t > 0.f && t < 3.0e38f; }
+
+}  // namespace
+
 size_t dflash_workspace_bytes(const dflash_model* m, int32_t max_batch, int32_t max_ctx,
                               int32_t max_rows) {
   if (!m || max_batch < 1 || max_ctx < 1 || max_rows < 0) return 0;
@@ -523,6 +555,7 @@ size_t dflash_workspace_bytes(const dflash_model* m, int32_t max_batch, int32_t 
     return n;
   }
   size_t n = stack_ws(c, max_batch, max_ctx, c.block, c.block - 1).total;
+  n = std::max(n, sample_ws(c, max_batch).total);
   n = std::max(n, fuse_ws(c, std::max(1, max_rows)));
   n = std::max(n, inject_ws(c, std::max(1, max_rows)));
   return n;
@@ -926,6 +959,44 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
   return run_stack(m, kv, io, ws, ws_bytes, stream);
 }
 
+dflash_status dflash_draft_block_sample(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
+                                        int32_t* draft, float* logits, float temperature, uint64_t seed,
+                                        int32_t step, void* ws, size_t ws_bytes, void* stream) {
+  if (!m || !anchor || !draft || !logits || !ws) return DFLASH_ERR_NULL;
+  if (m->target) return DFLASH_ERR_UNSUPPORTED;
+  if (!sample_temperature_ok(temperature)) return DFLASH_ERR_SHAPE;
+  dflash_status ks = check_kv(m, kv);
+  if (ks != DFLASH_OK) return ks;
+  const dflash_config& c = m->cfg;
+  const SampleWs sw = sample_ws(c, kv->batch);
+  if (ws_bytes < sw.total) return DFLASH_ERR_WORKSPACE;
+  // the greedy pass writes the raw logits; its argmax is then replaced by the
+  // Gumbel-max samples (the stack's workspace is dead by then)
+  StackIO io;
+  io.anchor = anchor;
+  io.B = c.block;
+  io.lm_skip = 1;
+  io.out = draft;
+  io.dbg_logits = logits;
+  const dflash_status s = run_stack(m, kv, io, ws, ws_bytes, stream);
+  if (s != DFLASH_OK) return s;
+  dfl::GumbelParams g;
+  std::memset(&g, 0, sizeof(g));
+  g.z = logits;
+  g.B = c.block;
+  g.V = c.vocab;
+  g.items = kv->batch * (c.block - 1);
+  g.chunks = dfl::sample_chunks(c.vocab);
+  g.inv_t = 1.0f / temperature;
+  g.seed_lo = (uint32_t)seed;
+  g.seed_hi = (uint32_t)(seed >> 32);
+  g.step = (uint32_t)step;
+  g.keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + sw.keys);
+  g.out = draft;
+  g.status = kv->status;
+  return hip_status(dfl::launch_gumbel(g, 0, as_stream(stream)));
+}
+
 dflash_status dflash_target_forward(const dflash_model* m, dflash_kv* kv, const int32_t* tokens, int32_t n,
                                     int32_t* argmax, void* taps, float* dbg_logits, void* ws, size_t ws_bytes,
                                     void* stream) {
@@ -991,6 +1062,130 @@ dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,
   p.n_commit = n_commit;
   prof::Scope ps(DFLASH_PHASE_VERIFY, as_stream(stream));
   return hip_status(dfl::launch_verify(p, as_stream(stream)));
+}
+
+dflash_status dflash_sample_logits(const dflash_model* m, const float* logits, int32_t rows, float temperature,
+                                   uint64_t seed, int32_t step, int32_t row0, int32_t* tokens, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!m) return DFLASH_ERR_NULL;
+  if (rows < 0 || row0 < 0) return DFLASH_ERR_SHAPE;
+  if (rows == 0) return DFLASH_OK;
+  if (!logits || !tokens || !ws) return DFLASH_ERR_NULL;
+  if (!sample_temperature_ok(temperature)) return DFLASH_ERR_SHAPE;
+  const dflash_config& c = m->cfg;
+  const size_t need = align256((size_t)dfl::sample_chunks(c.vocab) * rows * 8);
+  if (ws_bytes < need) return DFLASH_ERR_WORKSPACE;
+  dfl::GumbelParams g;
+  std::memset(&g, 0, sizeof(g));
+  g.z = logits;
+  g.row0 = row0;
+  g.B = 2;
+  g.V = c.vocab;
+  g.items = rows;
+  g.chunks = dfl::sample_chunks(c.vocab);
+  g.inv_t = 1.0f / temperature;
+  g.seed_lo = (uint32_t)seed;
+  g.seed_hi = (uint32_t)(seed >> 32);
+  g.step = (uint32_t)step;
+  g.keys = static_cast<unsigned long long*>(ws);
+  g.out = tokens;
+  return hip_status(dfl::launch_gumbel(g, 0, as_stream(stream)));
+}
+
+dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, const int32_t* draft,
+                                   const float* draft_logits, const float* target_logits, float temperature,
+                                   uint64_t seed, int32_t step, const int32_t* stop_ids, int32_t n_stop,
+                                   int32_t* budget, int32_t* accept_len, int32_t* anchor_out, int32_t* emitted,
+                                   int32_t* n_emit, int32_t* done, int32_t* commit_rows, int32_t* n_commit,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (!m) return DFLASH_ERR_NULL;
+  if (m->target) return DFLASH_ERR_UNSUPPORTED;
+  dflash_status ks = check_kv(m, kv);
+  if (ks != DFLASH_OK) return ks;
+  if (!draft || !draft_logits || !target_logits || !accept_len || !anchor_out || !emitted || !n_emit || !done ||
+      !commit_rows || !n_commit || !ws)
+    return DFLASH_ERR_NULL;
+  if (n_stop < 0) return DFLASH_ERR_SHAPE;
+  if (n_stop > 0 && !stop_ids) return DFLASH_ERR_NULL;
+  if (!sample_temperature_ok(temperature)) return DFLASH_ERR_SHAPE;
+  const dflash_config& c = m->cfg;
+  const int batch = kv->batch, B = c.block;
+  const SampleWs sw = sample_ws(c, batch);
+  if (ws_bytes < sw.total) return DFLASH_ERR_WORKSPACE;
+  const hipStream_t st = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  float* lse = reinterpret_cast<float*>(base + sw.lse);
+  int32_t* a = reinterpret_cast<int32_t*>(base + sw.a);
+  int32_t* mm = reinterpret_cast<int32_t*>(base + sw.m);
+  int32_t* rej = reinterpret_cast<int32_t*>(base + sw.rej);
+  prof::Scope ps(DFLASH_PHASE_VERIFY, st);
+  dfl::LseParams lp;
+  lp.z0 = draft_logits;
+  lp.z1 = target_logits;
+  lp.rows0 = batch * (B - 1);
+  lp.rows1 = batch * B;
+  lp.V = c.vocab;
+  lp.inv_t = 1.0f / temperature;
+  lp.lse = lse;
+  hipError_t e = dfl::launch_lse(lp, st);
+  if (e != hipSuccess) return DFLASH_ERR_HIP;
+  dfl::AcceptParams ap;
+  ap.draft = draft;
+  ap.zd = draft_logits;
+  ap.zt = target_logits;
+  ap.lse_d = lse;
+  ap.lse_t = lse + batch * (B - 1);
+  ap.batch = batch;
+  ap.B = B;
+  ap.V = c.vocab;
+  ap.inv_t = lp.inv_t;
+  ap.seed_lo = (uint32_t)seed;
+  ap.seed_hi = (uint32_t)(seed >> 32);
+  ap.step = (uint32_t)step;
+  ap.a = a;
+  ap.m = mm;
+  ap.rejected = rej;
+  if ((e = dfl::launch_accept(ap, st)) != hipSuccess) return DFLASH_ERR_HIP;
+  dfl::GumbelParams g;
+  std::memset(&g, 0, sizeof(g));
+  g.zd = draft_logits;
+  g.zt = target_logits;
+  g.lse_d = ap.lse_d;
+  g.lse_t = ap.lse_t;
+  g.m = mm;
+  g.rejected = rej;
+  g.B = B;
+  g.V = c.vocab;
+  g.items = batch;
+  g.chunks = dfl::sample_chunks(c.vocab);
+  g.inv_t = lp.inv_t;
+  g.seed_lo = ap.seed_lo;
+  g.seed_hi = ap.seed_hi;
+  g.step = ap.step;
+  g.keys = reinterpret_cast<unsigned long long*>(base + sw.keys);
+  g.a = a;
+  if ((e = dfl::launch_gumbel(g, 1, st)) != hipSuccess) return DFLASH_ERR_HIP;
+  // the greedy rule on (draft, a) yields the sampled outcome: a holds the
+  // accepted drafts and then the new token, which never equals the rejected
+  // draft (the residual is zero there)
+  dfl::VerifyParams p;
+  p.draft = draft;
+  p.target = a;
+  p.stop_ids = stop_ids;
+  p.n_stop = n_stop;
+  p.budget = budget;
+  p.ctx_len = kv->ctx_len;
+  p.status = kv->status;
+  p.batch = batch;
+  p.B = B;
+  p.accept_len = accept_len;
+  p.anchor_out = anchor_out;
+  p.emitted = emitted;
+  p.n_emit = n_emit;
+  p.done = done;
+  p.commit_rows = commit_rows;
+  p.n_commit = n_commit;
+  return hip_status(dfl::launch_verify(p, st));
 }
 
 dflash_status dflash_pack_matrix(const void* src, void* dst, int32_t rows, int32_t cols, void* stream) {

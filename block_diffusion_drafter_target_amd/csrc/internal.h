@@ -219,4 +219,57 @@ struct VerifyParams {
 
 hipError_t launch_verify(const VerifyParams& p, hipStream_t st);
 
+// Sampling mode (sample.hip). lse[r] = log sum_v exp(z_r[v] * inv_t) for the
+// rows0 rows of z0 followed by the rows1 rows of z1 (each row V floats).
+struct LseParams {
+  const float* z0;
+  const float* z1;
+  int rows0, rows1, V;
+  float inv_t;
+  float* lse;
+};
+hipError_t launch_lse(const LseParams& p, hipStream_t st);
+
+// Acceptance walk per sequence: accepted drafts into a[b][j-1], the count m[b]
+// and rejected[b] (0: every draft passed).
+struct AcceptParams {
+  const int32_t* draft;  // [batch, B-1]
+  const float* zd;       // draft logits [batch*(B-1), V]
+  const float* zt;       // target logits [batch*B, V]
+  const float* lse_d;
+  const float* lse_t;
+  int batch, B, V;
+  float inv_t;
+  uint32_t seed_lo, seed_hi, step;
+  int32_t* a;  // [batch, B]
+  int32_t* m;
+  int32_t* rejected;
+};
+hipError_t launch_accept(const AcceptParams& p, hipStream_t st);
+
+// Gumbel-max sampling over the vocabulary in sample_chunks(V) chunks per item.
+// mode 0: items = LM rows of z, RNG rows row0 + item, out[item] = token (-1
+// where status of the item's sequence, item / (B-1), is nonzero);
+// mode 1: items = sequences, the residual (rejected) or bonus sample written to
+// a[item][m[item]].
+struct GumbelParams {
+  const float* z;
+  int row0;
+  const float* zd;
+  const float* zt;
+  const float* lse_d;
+  const float* lse_t;
+  const int32_t* m;
+  const int32_t* rejected;
+  int B, V, items, chunks;
+  float inv_t;
+  uint32_t seed_lo, seed_hi, step;
+  unsigned long long* keys;  // [chunks, items]
+  int32_t* out;
+  const int32_t* status;
+  int32_t* a;
+};
+int sample_chunks(int V);
+hipError_t launch_gumbel(const GumbelParams& p, int mode, hipStream_t st);
+
 }  // namespace dfl

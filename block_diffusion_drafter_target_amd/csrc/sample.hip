@@ -1,0 +1,244 @@
+// Sampling mode (temperature > 0): Gumbel-max draft sampling and
+// speculative-sampling verification, gfx950.
+//
+// The acceptance rule is the standard speculative-sampling one: draft token
+// d_j (sampled from the drafter's q_j = softmax(z^d_j / T)) is accepted when
+// u_j <= p_{j-1}(d_j) / q_j(d_j), p_i = softmax(z^t_i / T) the target's
+// distribution after block row i; the first rejected position takes a token
+// sampled from the normalised max(0, p_{j-1} - q_j), and when every draft
+// passes a bonus token is sampled from p_{B-1}. Sampling from a distribution
+// is the argmax of its log-probabilities plus Gumbel noise -log(-log u).
+//
+// Uniforms come from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11: ten
+// rounds of two 32x32-bit multiplications by 0xD2511F53 and 0xCD9E8D57, Weyl
+// key increments 0x9E3779B9 and 0xBB67AE85). A draw (seed, tag, step, row, v)
+// uses key (seed low word, seed high word), counter (v / 4, row, step, tag) and
+// output word v % 4, mapped to ((word >> 9) + 0.5) * 2^-23 (exact in fp32).
+// Tags: 0 draft sampling (row = LM row), 1 acceptance (row = b*B + j, v = 0),
+// 2 residual or bonus sample (row = b).
+//
+// Work layout: log-sum-exp one workgroup per logits row; the Gumbel argmax
+// over the vocabulary in chunks of kChunk values per workgroup (each thread
+// four consecutive values per Philox call, float4 loads), one packed
+// (score, index) key per chunk, reduced by a finishing kernel (no atomics).
+#include "common.h"
+#include "internal.h"
+
+namespace dfl {
+
+namespace {
+
+constexpr int kChunk = 8192;  // vocabulary values per Gumbel-argmax workgroup
+constexpr int kTagDraft = 0, kTagAccept = 1, kTagResidual = 2;
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+  constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u, kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kW0;
+      k1 += kW1;
+    }
+    const uint32_t hi0 = __umulhi(kM0, c0), lo0 = kM0 * c0;
+    const uint32_t hi1 = __umulhi(kM1, c2), lo1 = kM1 * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+__device__ __forceinline__ float u01(uint32_t w) { return ((float)(w >> 9) + 0.5f) * 0x1p-23f; }
+
+__device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
+
+// log-sum-exp of z * inv_t over one row per workgroup (256 threads)
+__global__ __launch_bounds__(256) void lse_kernel(const LseParams p) {
+  __shared__ float red[2][4];
+  const int row = blockIdx.x;
+  const float* z = row < p.rows0 ? p.z0 + (long long)row * p.V : p.z1 + (long long)(row - p.rows0) * p.V;
+  float mx = -__builtin_inff(), sum = 0.f;
+  for (int v = threadIdx.x * 4; v < p.V; v += 1024) {  // V % 4 == 0
+    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(z + v) * p.inv_t;
+    const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (m4 > mx) {
+      sum *= __expf(mx - m4);
+      mx = m4;
+    }
+    sum += __expf(x[0] - mx) + __expf(x[1] - mx) + __expf(x[2] - mx) + __expf(x[3] - mx);
+  }
+  // wave, then workgroup: combine (max, sum) pairs
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(mx, o), os = __shfl_xor(sum, o);
+    const float nm = fmaxf(mx, om);
+    sum = (mx == -__builtin_inff() ? 0.f : sum * __expf(mx - nm)) + (om == -__builtin_inff() ? 0.f : os * __expf(om - nm));
+    mx = nm;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    red[0][wave] = mx;
+    red[1][wave] = sum;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = red[0][0];
+    for (int w = 1; w < 4; ++w) m = fmaxf(m, red[0][w]);
+    float s = 0.f;
+    for (int w = 0; w < 4; ++w) s += red[1][w] * __expf(red[0][w] - m);
+    p.lse[row] = m + logf(s);
+  }
+}
+
+// The acceptance walk of one sequence (one thread each): writes the accepted
+// drafts into the target-token row a, the first rejected position (or B - 1)
+// into state[b].m and whether it was a rejection into state[b].rejected.
+__global__ __launch_bounds__(64) void accept_kernel(const AcceptParams p) {
+  const int b = blockIdx.x * 64 + threadIdx.x;
+  if (b >= p.batch) return;
+  const int B = p.B;
+  int m = 0, rejected = 0;
+  for (int j = 1; j < B; ++j) {
+    const int d = p.draft[b * (B - 1) + j - 1];
+    const int dc = d < 0 ? 0 : (d >= p.V ? p.V - 1 : d);
+    const float lp = p.zt[(long long)(b * B + j - 1) * p.V + dc] * p.inv_t - p.lse_t[b * B + j - 1];
+    const float lq = p.zd[(long long)(b * (B - 1) + j - 1) * p.V + dc] * p.inv_t - p.lse_d[b * (B - 1) + j - 1];
+    const u32x4 w = philox4x32_10(0u, (uint32_t)(b * B + j), p.step, kTagAccept, p.seed_lo, p.seed_hi);
+    if (d == dc && logf(u01(w[0])) <= lp - lq) {
+      p.a[b * B + j - 1] = d;
+      m = j;
+    } else {
+      rejected = 1;
+      break;
+    }
+  }
+  p.m[b] = m;
+  p.rejected[b] = rejected;
+}
+
+// One chunk of the Gumbel argmax of one item: MODE 0 draft sampling (item =
+// LM row; score z * inv_t + g), MODE 1 the new token of sequence `item`
+// (score log(max(0, p - q)) + g after a rejection, log p + g for the bonus).
+template <int MODE>
+__global__ __launch_bounds__(256) void gumbel_argmax_kernel(const GumbelParams p) {
+  __shared__ unsigned long long red[4];
+  const int item = blockIdx.y, chunk = blockIdx.x;
+  const int v0 = chunk * kChunk;
+  const float* zp;  // MODE 0: the row's logits; MODE 1: the target row p is taken from
+  const float* zq = nullptr;
+  float lse_p = 0.f, lse_q = 0.f;
+  uint32_t row_id, tag;
+  if (MODE == 0) {
+    zp = p.z + (long long)item * p.V;
+    row_id = (uint32_t)(p.row0 + item);
+    tag = kTagDraft;
+  } else {
+    const int B = p.B, m = p.m[item];
+    const int tr = item * B + m;
+    zp = p.zt + (long long)tr * p.V;
+    lse_p = p.lse_t[tr];
+    if (p.rejected[item]) {
+      const int dr = item * (B - 1) + m;
+      zq = p.zd + (long long)dr * p.V;
+      lse_q = p.lse_d[dr];
+    }
+    row_id = (uint32_t)item;
+    tag = kTagResidual;
+  }
+  float bv = -__builtin_inff();
+  int bn = 0x7FFFFFFF;
+  const int vend = min(p.V, v0 + kChunk);
+  for (int v = v0 + threadIdx.x * 4; v < vend; v += 1024) {
+    const u32x4 w = philox4x32_10((uint32_t)(v >> 2), row_id, p.step, tag, p.seed_lo, p.seed_hi);
+    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(zp + v);
+    f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+    if (MODE == 1 && zq) y = *reinterpret_cast<const f32x4_t*>(zq + v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float s;
+      if (MODE == 0) {
+        s = x[i] * p.inv_t;
+      } else if (zq) {
+        const float r = __expf(x[i] * p.inv_t - lse_p) - __expf(y[i] * p.inv_t - lse_q);
+        s = r > 0.f ? logf(r) : -__builtin_inff();
+      } else {
+        s = x[i] * p.inv_t - lse_p;
+      }
+      if (s != -__builtin_inff()) {
+        s += gumbel(u01(w[i]));
+        if (s > bv) {  // ascending v within the thread: lowest index on ties
+          bv = s;
+          bn = v + i;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int on = __shfl_xor(bn, o);
+    if (ov > bv || (ov == bv && on < bn)) {
+      bv = ov;
+      bn = on;
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = bn != 0x7FFFFFFF ? argmax_key(bv, bn) : 0ull;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    p.keys[(long long)chunk * p.items + item] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// Best key over the chunks of every item: MODE 0 writes the sampled draft
+// token (-1 for a sequence whose status is nonzero, as the greedy path does),
+// MODE 1 writes the new token into the target-token row at position m.
+template <int MODE>
+__global__ __launch_bounds__(256) void gumbel_finish_kernel(const GumbelParams p) {
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  if (item >= p.items) return;
+  unsigned long long best = 0ull;
+  for (int c = 0; c < p.chunks; ++c) best = max(best, p.keys[(long long)c * p.items + item]);
+  const int tok = best ? (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull)) : 0;
+  if (MODE == 0) {
+    const int seq = item / (p.B - 1);
+    p.out[item] = (p.status && p.status[seq] != 0) ? -1 : tok;
+  } else {
+    p.a[item * p.B + p.m[item]] = tok;
+  }
+}
+
+}  // namespace
+
+int sample_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+
+hipError_t launch_lse(const LseParams& p, hipStream_t st) {
+  if (p.V % 4 || p.rows0 < 0 || p.rows0 + p.rows1 < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lse_kernel, dim3(p.rows0 + p.rows1), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(const AcceptParams& p, hipStream_t st) {
+  if (p.batch < 1 || p.B < 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(accept_kernel, dim3((p.batch + 63) / 64), dim3(64), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gumbel(const GumbelParams& p, int mode, hipStream_t st) {
+  if (p.V % 4 || p.items < 1 || p.chunks != sample_chunks(p.V)) return hipErrorInvalidValue;
+  const dim3 grid(p.chunks, p.items);
+  if (mode == 0) {
+    hipLaunchKernelGGL(gumbel_argmax_kernel<0>, grid, dim3(256), 0, st, p);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(gumbel_finish_kernel<0>, dim3((p.items + 255) / 256), dim3(256), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(gumbel_argmax_kernel<1>, grid, dim3(256), 0, st, p);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(gumbel_finish_kernel<1>, dim3((p.items + 255) / 256), dim3(256), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dfl

@@ -143,6 +143,42 @@ class Drafter:
                               bd.ptr(dbg_hidden), bd.ptr(self.ws), self.ws_bytes, self.stream())
         return self.draft
 
+    def draft_block_sample(self, temperature: float, seed: int, step: int, anchor=None):
+        """Sampling-mode draft block: tokens sampled from the drafter's own
+        distributions (Gumbel-max, Philox draws of (seed, step)); the raw logits
+        stay in self.draft_logits [batch*(B-1), V] for the verify."""
+        a = self.anchor if anchor is None else anchor
+        if getattr(self, "draft_logits", None) is None:
+            torch = _torch()
+            self.draft_logits = torch.empty((self.batch * (self.cfg.block - 1), self.cfg.vocab),
+                                            dtype=torch.float32, device=self.device)
+        bd.dflash_draft_block_sample(self.model, self.kv, bd.ptr(a), bd.ptr(self.draft), bd.ptr(self.draft_logits),
+                                     float(temperature), int(seed), int(step), bd.ptr(self.ws), self.ws_bytes,
+                                     self.stream())
+        return self.draft
+
+    def verify_sample(self, target_logits, temperature: float, seed: int, step: int, stop_ids=None, budget=None,
+                      draft=None, draft_logits=None):
+        """Speculative-sampling verification against the target's logits
+        [batch*B, V] (fp32) of the block rows; same outputs as verify_accept."""
+        d = self.draft if draft is None else draft
+        zd = self.draft_logits if draft_logits is None else draft_logits
+        n_stop = 0 if stop_ids is None else int(stop_ids.numel())
+        bd.dflash_verify_sample(self.model, self.kv, bd.ptr(d), bd.ptr(zd), bd.ptr(target_logits),
+                                float(temperature), int(seed), int(step), bd.ptr(stop_ids), n_stop, bd.ptr(budget),
+                                bd.ptr(self.accept_len), bd.ptr(self.anchor_out), bd.ptr(self.emitted),
+                                bd.ptr(self.n_emit), bd.ptr(self.done), bd.ptr(self.commit_rows),
+                                bd.ptr(self.n_commit), bd.ptr(self.ws), self.ws_bytes, self.stream())
+
+    def sample_logits(self, logits, temperature: float, seed: int, step: int, row0: int = 0, out=None):
+        """Gumbel-max samples of softmax(logits / T) per row (fp32 [rows, V])."""
+        torch = _torch()
+        rows = logits.shape[0]
+        out = torch.empty(rows, dtype=torch.int32, device=self.device) if out is None else out
+        bd.dflash_sample_logits(self.model, bd.ptr(logits), rows, float(temperature), int(seed), int(step),
+                                int(row0), bd.ptr(out), bd.ptr(self.ws), self.ws_bytes, self.stream())
+        return out
+
     def verify_accept(self, target_argmax, stop_ids=None, budget=None, draft=None):
         d = self.draft if draft is None else draft
         n_stop = 0 if stop_ids is None else int(stop_ids.numel())
@@ -248,18 +284,24 @@ class DeviceTarget:
         self.ctx_len.zero_()
         self.status.zero_()
 
-    def forward(self, tokens: Sequence[int]):
+    def forward(self, tokens: Sequence[int], logits: bool = False):
         """Append tokens (in passes of up to max_n); returns (argmax as numpy
-        [n], taps as a device bf16 tensor [n, n_tap*H])."""
+        [n], taps as a device bf16 tensor [n, n_tap*H]), and with logits=True
+        also the fp32 logits of the last pass's rows (device [rows, V])."""
         torch = _torch()
         toks = torch.tensor(list(tokens), dtype=torch.int32, device=self.device)
         outs, taps = [], []
+        z = None
         for i in range(0, len(toks), self.max_n):
             part = toks[i:i + self.max_n][None, :]
-            a, t = self.pass_tokens(part)
+            if logits:
+                z = torch.empty((part.shape[1], self.cfg.vocab), dtype=torch.float32, device=self.device)
+            a, t = self.pass_tokens(part, dbg_logits=z)
             outs.append(a[0].clone())
             taps.append(t.clone())
             self.ctx_len += part.shape[1]
+        if logits:
+            return torch.cat(outs).cpu().numpy(), torch.cat(taps), z
         return torch.cat(outs).cpu().numpy(), torch.cat(taps)
 
     def truncate(self, length: int) -> None:
@@ -284,14 +326,17 @@ def _taps_dev(taps, dev):
 
 
 def spec_generate(drafter: Drafter, target: Target, prompt: Sequence[int], max_new_tokens: int,
-                  stop_token_ids: Sequence[int] = (), temperature: float = 0.0):
-    """Greedy speculative decoding of one sequence with the device drafter.
+                  stop_token_ids: Sequence[int] = (), temperature: float = 0.0, seed: int = 0):
+    """Speculative decoding of one sequence with the device drafter: greedy
+    at temperature 0, speculative sampling above (seed keys the draws).
 
     Returns (tokens, accepted lengths per step)."""
-    if temperature != 0.0:
-        raise NotImplementedError("only greedy (temperature 0) verification is implemented")
+    if temperature < 0.0:
+        raise ValueError("temperature must be >= 0")
     if drafter.batch != 1:
         raise ValueError("spec_generate drives one sequence")
+    if temperature > 0.0:
+        return _spec_sample(drafter, target, prompt, max_new_tokens, stop_token_ids, temperature, seed)
     torch = _torch()
     dev = drafter.device
     B = drafter.cfg.block
@@ -319,6 +364,58 @@ def spec_generate(drafter: Drafter, target: Target, prompt: Sequence[int], max_n
         drafter.inject_kv(ctx, B, drafter.commit_rows, drafter.n_commit, B)
         n = int(drafter.n_emit.item())
         out += [int(t) for t in drafter.emitted[0, :n].cpu().numpy()]
+        ms.append(m)
+        anchor = int(drafter.anchor_out.item())
+        L += m + 1
+        if int(drafter.done.item()):
+            break
+    return out[:max_new_tokens], ms
+
+
+def _spec_sample(drafter: Drafter, target: "DeviceTarget", prompt, max_new_tokens: int, stop_token_ids,
+                 temperature: float, seed: int, trace: list | None = None):
+    """The sampling loop: the first token is sampled from the target's last
+    prompt row (draws of step 0); step s >= 1 samples the block (draft
+    block, draws of step s), runs the target pass with logits and verifies by
+    speculative sampling (draws of step s). ``trace`` collects per step
+    (draft, draft logits, target logits, accept_len, emitted) copies."""
+    torch = _torch()
+    dev = drafter.device
+    B = drafter.cfg.block
+    target.reset()
+    drafter.ctx_len.zero_()
+    _, taps, z = target.forward(list(prompt), logits=True)
+    first = drafter.sample_logits(z[-1:].contiguous(), temperature, seed, 0)
+    anchor = int(first.item())
+    out = [anchor]
+    drafter.ingest(0, _taps_dev(taps, dev))
+    stops = torch.tensor(list(stop_token_ids), dtype=torch.int32, device=dev) if stop_token_ids else None
+    budget = torch.tensor([max_new_tokens - 1], dtype=torch.int32, device=dev)
+    L = len(prompt)
+    ms = []
+    stop_set = set(int(s) for s in stop_token_ids)
+    step = 0
+    zt = torch.empty((B, drafter.cfg.vocab), dtype=torch.float32, device=dev)
+    while len(out) < max_new_tokens and out[-1] not in stop_set:
+        step += 1
+        drafter.anchor.fill_(anchor)
+        drafter.draft_block_sample(temperature, seed, step)
+        toks = torch.cat([drafter.anchor[:, None], drafter.draft], dim=1).contiguous()
+        _, taps_b = target.pass_tokens(toks, dbg_logits=zt)
+        taps_b = taps_b.clone()
+        drafter.verify_sample(zt, temperature, seed, step, stops, budget)
+        m = int(drafter.accept_len.item())
+        target.commit(drafter.commit_rows, drafter.n_commit, B)
+        ctx = drafter.fuse_ctx(taps_b, B)
+        drafter.inject_kv(ctx, B, drafter.commit_rows, drafter.n_commit, B)
+        n = int(drafter.n_emit.item())
+        em = [int(t) for t in drafter.emitted[0, :n].cpu().numpy()]
+        if trace is not None:
+            trace.append({"draft": drafter.draft.cpu().numpy().copy(),
+                          "draft_logits": drafter.draft_logits.cpu().numpy().copy(),
+                          "target_logits": zt.cpu().numpy().copy(), "accept_len": m, "emitted": em,
+                          "step": step})
+        out += em
         ms.append(m)
         anchor = int(drafter.anchor_out.item())
         L += m + 1

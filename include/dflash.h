@@ -195,6 +195,63 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
                                  int32_t* draft, float* dbg_logits, float* dbg_hidden, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/* Sampling mode, draft side (temperature > 0). [P4 "Ejecutando DFlash": the
+ * user call takes a temperature; P2 results: speed-ups are quoted under
+ * sampling too] The pages give no sampling rule; the plain reading is standard
+ * speculative sampling, whose draft side samples every block token from the
+ * drafter's own distribution at its position, q_j = softmax(z_j / T).
+ * Runs the pass of dflash_draft_block (same inputs, cache effects and status
+ * rules), writes the raw logits of rows 1..B-1 and replaces each greedy token
+ * by a Gumbel-max sample: draft[b][j-1] = argmax_v z_v / T + g_v with
+ * g_v = -log(-log u_v), u_v the Philox4x32-10 uniform of the draw
+ * (seed, tag 0, step, row b*(B-1)+j-1, v) (see dflash_verify_sample).
+ *   logits      device fp32 [batch*(B-1), V] out, required (the verify reads
+ *               them)
+ *   temperature > 0, finite (else DFLASH_ERR_SHAPE)
+ *   seed, step  the draws' key and step counter (a new step per block keeps
+ *               the draws of different steps independent)
+ * ws: dflash_workspace_bytes covers it. */
+dflash_status dflash_draft_block_sample(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
+                                        int32_t* draft, float* logits, float temperature, uint64_t seed,
+                                        int32_t step, void* ws, size_t ws_bytes, void* stream);
+
+/* Sampling mode: Gumbel-max samples of softmax(logits / T) for `rows` rows of
+ * the model's vocabulary width, the draw of row r being (seed, tag 0, step,
+ * row0 + r) (see dflash_verify_sample), e.g. the first token after a prompt,
+ * which comes from the target's last prompt row. [P4 "Ejecutando DFlash":
+ * the call's temperature]
+ *   logits  device fp32 [rows, V]; tokens device int32 [rows] out
+ *   ws      at least 8 * ceil(V / 8192) * rows bytes (dflash_workspace_bytes
+ *           covers rows <= batch * (block - 1)) */
+dflash_status dflash_sample_logits(const dflash_model* m, const float* logits, int32_t rows, float temperature,
+                                   uint64_t seed, int32_t step, int32_t row0, int32_t* tokens, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/* Sampling mode, verify side: standard speculative-sampling acceptance (the
+ * plain reading; see dflash_draft_block_sample). With p_i = softmax(zt_i / T)
+ * the target's distribution after block row i and q_j = softmax(zd_j / T):
+ * draft d_j is accepted when u_j <= p_{j-1}(d_j) / q_j(d_j), for j = 1, 2, ...
+ * until the first rejection; the first rejected position takes a token
+ * sampled from the normalised max(0, p_{j-1} - q_j), and when all B-1 drafts
+ * pass a bonus token is sampled from p_{B-1}. The emitted tokens are the
+ * accepted drafts and the new token, cut by stop ids and budget, and rows
+ * 0..m are committed, exactly as in dflash_verify_accept (same outputs).
+ * Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11), key =
+ * (seed low word, high word), counter = (v / 4, row, step, tag), output word
+ * v % 4, uniform ((word >> 9) + 0.5) * 2^-23. u_j: tag 1, row b*B + j, v 0;
+ * the residual or bonus sample: Gumbel-max with tag 2, row b.
+ *   draft_logits  device fp32 [batch*(B-1), V]: the drafter's rows 1..B-1
+ *   target_logits device fp32 [batch*B, V]: the target's logits after rows
+ *                 0..B-1 of [anchor, d_1..d_{B-1}]
+ *   temperature   > 0, finite (else DFLASH_ERR_SHAPE)
+ * ws: dflash_workspace_bytes covers it. ctx_len is read, never written. */
+dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, const int32_t* draft,
+                                   const float* draft_logits, const float* target_logits, float temperature,
+                                   uint64_t seed, int32_t step, const int32_t* stop_ids, int32_t n_stop,
+                                   int32_t* budget, int32_t* accept_len, int32_t* anchor_out, int32_t* emitted,
+                                   int32_t* n_emit, int32_t* done, int32_t* commit_rows, int32_t* n_commit,
+                                   void* ws, size_t ws_bytes, void* stream);
+
 /* S11 — greedy acceptance of the longest valid prefix. [P2 introduction: the
  * target checks the block in parallel and keeps the longest valid prefix;
  * P4 "Ejecutando DFlash" for stop tokens and the token budget]

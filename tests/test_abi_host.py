@@ -205,3 +205,46 @@ def test_rope_table_values():
 def test_status_strings():
     assert bd.status_string(0) == "ok"
     assert "workspace" in bd.status_string(bd.DFLASH_ERR_WORKSPACE)
+
+
+def test_sampling_entry_points_check_arguments_without_a_gpu():
+    """Argument checks of the sampling-mode entry points run on the host and
+    return before any HIP call."""
+    lib = bd.load()
+    w, keep = _fake_weights(5)
+    rc, h = _create(_cfg(), w)
+    assert rc == bd.DFLASH_OK
+    try:
+        kv = bd.dflash_kv(k=0x1000, v=0x1000, batch=2, max_ctx=2048, ctx_len=0x1000, status=0x1000)
+        ws = bd.dflash_workspace_bytes(h, 2, 2048, 32)
+        P = 0x1000
+        ds = lib.dflash_draft_block_sample
+        assert ds(h, C.byref(kv), P, P, None, 1.0, 7, 1, P, ws, None) == bd.DFLASH_ERR_NULL  # logits required
+        for t in (0.0, -1.0, float("nan"), float("inf")):
+            assert ds(h, C.byref(kv), P, P, P, t, 7, 1, P, ws, None) == bd.DFLASH_ERR_SHAPE
+        assert ds(h, C.byref(kv), P, P, P, 1.0, 7, 1, P, 16, None) == bd.DFLASH_ERR_WORKSPACE
+        vs = lib.dflash_verify_sample
+        args = [P, P, P, 1.0, 7, 1, None, 0, None] + [P] * 7 + [P, ws, None]
+        bad = list(args)
+        bad[1] = None  # draft logits
+        assert vs(h, C.byref(kv), *bad) == bd.DFLASH_ERR_NULL
+        bad = list(args)
+        bad[3] = 0.0
+        assert vs(h, C.byref(kv), *bad) == bd.DFLASH_ERR_SHAPE
+        bad = list(args)
+        bad[7] = -1  # n_stop
+        assert vs(h, C.byref(kv), *bad) == bd.DFLASH_ERR_SHAPE
+        bad = list(args)
+        bad[7] = 2  # stop ids missing
+        assert vs(h, C.byref(kv), *bad) == bd.DFLASH_ERR_NULL
+        bad = list(args)
+        bad[-2] = 64
+        assert vs(h, C.byref(kv), *bad) == bd.DFLASH_ERR_WORKSPACE
+        sl = lib.dflash_sample_logits
+        assert sl(h, P, 0, 1.0, 7, 0, 0, P, P, ws, None) == bd.DFLASH_OK  # nothing to sample
+        assert sl(h, P, -1, 1.0, 7, 0, 0, P, P, ws, None) == bd.DFLASH_ERR_SHAPE
+        assert sl(h, None, 3, 1.0, 7, 0, 0, P, P, ws, None) == bd.DFLASH_ERR_NULL
+        assert sl(h, P, 3, 0.0, 7, 0, 0, P, P, ws, None) == bd.DFLASH_ERR_SHAPE
+        assert sl(h, P, 3, 1.0, 7, 0, 0, P, P, 8, None) == bd.DFLASH_ERR_WORKSPACE
+    finally:
+        bd.dflash_model_destroy(h)
