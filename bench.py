@@ -62,6 +62,47 @@ def synth_target(torch, draft, m, rnd, vocab):
     return torch.where((j == m[:, None]) & (m[:, None] < bm1), (d_ext + 1) % (vocab - 1), t)
 
 
+def sampling_steps(torch, dr, cfg, args, taps_step, state):
+    """The step in sampling mode at temperature args.temperature: fuse + inject
+    of the committed rows, the sampled draft block (its logits written), and
+    speculative-sampling verification against synthetic target logits of the
+    block rows (seeded N(0, 2), resident before timing). Timed like the greedy
+    steps, from the state after the greedy warmup."""
+    from block_diffusion_drafter_target_amd import binding as bd
+    B, V, batch = cfg.block, cfg.vocab, cfg.batch
+    for k, v in state.items():
+        getattr(dr, k).copy_(v)
+    g = torch.Generator(device="cuda").manual_seed(4)
+    zt = torch.randn((batch * B, V), generator=g, device="cuda") * 2.0
+    T, seed = args.temperature, 2024
+
+    def step(i):
+        dr.fuse_ctx(taps_step, batch * B, dr.ctx)
+        dr.inject_kv(dr.ctx, batch * B, dr.commit_rows, dr.n_commit, batch * B)
+        dr.draft_block_sample(T, seed, i, anchor=dr.anchor_out)
+        dr.verify_sample(zt, T, seed, i)
+
+    for i in range(args.warmup):
+        step(1 + i)
+    torch.cuda.synchronize()
+    bd.dflash_profile_enable(["lm_head", "verify"])
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(1 + args.warmup + i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    v_ms, v_n = bd.dflash_profile_read("verify")
+    bd.dflash_profile_enable([])
+    assert int(dr.status.abs().max()) == 0, "a sequence ran out of cache"
+    return {"temperature": T, "us_per_step": round(ms * 1e3, 1),
+            "drafted_tokens_per_s": round(batch * (B - 1) / (ms * 1e-3), 1),
+            "us_verify_sample": round(1e3 * v_ms / max(1, v_n), 1),
+            "note": ("fuse + inject + sampled draft block (logits written, Gumbel-max tokens) + "
+                     "speculative-sampling verify against synthetic target logits")}
+
+
 def target_verify(cfg, W, lens, args, dr):
     """The target side of a step: one causal pass of the target model over the
     B block tokens of every sequence (argmax + taps), timed over repeated
@@ -214,6 +255,8 @@ def main():
                     help="also time the target's causal verify pass (Qwen3-8B-shaped 36-layer target)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="also time the step in sampling mode at this temperature")
     ap.add_argument("--graph", action="store_true",
                     help="also time the same steps captured in one HIP graph")
     args = ap.parse_args()
@@ -235,7 +278,7 @@ def main():
     B, V, H, batch = cfg.block, cfg.vocab, cfg.hidden, cfg.batch
     lens = synth.make_ctx_lens(cfg)
     n_break = min(args.steps, 20)  # steps of the per-phase breakdown pass
-    n_steps = 1 + args.warmup + args.steps + n_break
+    n_steps = 1 + args.warmup + args.steps + n_break + (args.warmup if args.temperature > 0 else 0)
     max_ctx = int(lens.max()) + (n_steps + 2) * B + 64
     t0 = time.time()
     W = synth.make_weights(cfg)
@@ -337,6 +380,10 @@ def main():
             assert torch.equal(getattr(dr, k), v), f"graph replay diverged from the eager steps ({k})"
         del graph
 
+    sampling = None
+    if args.temperature > 0:
+        sampling = sampling_steps(torch, dr, cfg, args, taps_step, after_warmup)
+
     bd.dflash_profile_enable(list(bd.PHASES))
     for i in range(n_break):
         step(targets[1 + args.warmup + args.steps + i])
@@ -400,6 +447,7 @@ def main():
                    "mfma_frac": round(ingest_flop / (ingest_ms * 1e-3) * 1e-12 / MFMA_PEAK_TFLOPS, 4),
                    "note": "fuse + inject of every context row (GEMM flops), second pass timed"},
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "sampling": sampling,
         "phases": phases,
     }
     if args.target_verify:

@@ -517,7 +517,7 @@ namespace {
 // sampled draft block): log-sum-exps, the target-token row, per-sequence
 // state and the chunk keys.
 struct SampleWs {
-  size_t lse, a, m, rej, keys, total;
+  size_t pmax, psum, a, m, rej, keys, total;
 };
 
 SampleWs sample_ws(const dflash_config& c, int batch) {
@@ -530,7 +530,9 @@ SampleWs sample_ws(const dflash_config& c, int batch) {
     off += align256(bytes);
     return o;
   };
-  w.lse = take((size_t)batch * (2 * B - 1) * 4);
+  const size_t pairs = (size_t)batch * (2 * B - 1) * dfl::sample_chunks(c.vocab);
+  w.pmax = take(pairs * 4);
+  w.psum = take(pairs * 4);
   w.a = take((size_t)batch * B * 4);
   w.m = take((size_t)batch * 4);
   w.rej = take((size_t)batch * 4);
@@ -1114,7 +1116,9 @@ dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, c
   if (ws_bytes < sw.total) return DFLASH_ERR_WORKSPACE;
   const hipStream_t st = as_stream(stream);
   char* base = static_cast<char*>(ws);
-  float* lse = reinterpret_cast<float*>(base + sw.lse);
+  float* pmax = reinterpret_cast<float*>(base + sw.pmax);
+  float* psum = reinterpret_cast<float*>(base + sw.psum);
+  const int chunks = dfl::sample_chunks(c.vocab);
   int32_t* a = reinterpret_cast<int32_t*>(base + sw.a);
   int32_t* mm = reinterpret_cast<int32_t*>(base + sw.m);
   int32_t* rej = reinterpret_cast<int32_t*>(base + sw.rej);
@@ -1125,16 +1129,20 @@ dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, c
   lp.rows0 = batch * (B - 1);
   lp.rows1 = batch * B;
   lp.V = c.vocab;
+  lp.chunks = chunks;
   lp.inv_t = 1.0f / temperature;
-  lp.lse = lse;
+  lp.pmax = pmax;
+  lp.psum = psum;
   hipError_t e = dfl::launch_lse(lp, st);
   if (e != hipSuccess) return DFLASH_ERR_HIP;
   dfl::AcceptParams ap;
   ap.draft = draft;
   ap.zd = draft_logits;
   ap.zt = target_logits;
-  ap.lse_d = lse;
-  ap.lse_t = lse + batch * (B - 1);
+  ap.pmax = pmax;
+  ap.psum = psum;
+  ap.rows_d = batch * (B - 1);
+  ap.chunks = chunks;
   ap.batch = batch;
   ap.B = B;
   ap.V = c.vocab;
@@ -1150,8 +1158,10 @@ dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, c
   std::memset(&g, 0, sizeof(g));
   g.zd = draft_logits;
   g.zt = target_logits;
-  g.lse_d = ap.lse_d;
-  g.lse_t = ap.lse_t;
+  g.pmax = pmax;
+  g.psum = psum;
+  g.rows_d = ap.rows_d;
+  g.lse_chunks = chunks;
   g.m = mm;
   g.rejected = rej;
   g.B = B;

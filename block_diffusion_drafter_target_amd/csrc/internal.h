@@ -219,14 +219,16 @@ struct VerifyParams {
 
 hipError_t launch_verify(const VerifyParams& p, hipStream_t st);
 
-// Sampling mode (sample.hip). lse[r] = log sum_v exp(z_r[v] * inv_t) for the
-// rows0 rows of z0 followed by the rows1 rows of z1 (each row V floats).
+// Sampling mode (sample.hip). Per-chunk log-sum-exp pairs of z * inv_t for the
+// rows0 rows of z0 followed by the rows1 rows of z1 (each row V floats):
+// pmax[row][chunk] and psum[row][chunk] (sample_chunks(V) chunks per row).
 struct LseParams {
   const float* z0;
   const float* z1;
-  int rows0, rows1, V;
+  int rows0, rows1, V, chunks;
   float inv_t;
-  float* lse;
+  float* pmax;
+  float* psum;
 };
 hipError_t launch_lse(const LseParams& p, hipStream_t st);
 
@@ -236,8 +238,9 @@ struct AcceptParams {
   const int32_t* draft;  // [batch, B-1]
   const float* zd;       // draft logits [batch*(B-1), V]
   const float* zt;       // target logits [batch*B, V]
-  const float* lse_d;
-  const float* lse_t;
+  const float* pmax;     // log-sum-exp pairs: draft rows, then target rows from rows_d
+  const float* psum;
+  int rows_d, chunks;
   int batch, B, V;
   float inv_t;
   uint32_t seed_lo, seed_hi, step;
@@ -257,8 +260,9 @@ struct GumbelParams {
   int row0;
   const float* zd;
   const float* zt;
-  const float* lse_d;
-  const float* lse_t;
+  const float* pmax;  // log-sum-exp pairs as in AcceptParams
+  const float* psum;
+  int rows_d, lse_chunks;
   const int32_t* m;
   const int32_t* rejected;
   int B, V, items, chunks;

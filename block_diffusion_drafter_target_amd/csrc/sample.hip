@@ -17,10 +17,13 @@
 // Tags: 0 draft sampling (row = LM row), 1 acceptance (row = b*B + j, v = 0),
 // 2 residual or bonus sample (row = b).
 //
-// Work layout: log-sum-exp one workgroup per logits row; the Gumbel argmax
-// over the vocabulary in chunks of kChunk values per workgroup (each thread
-// four consecutive values per Philox call, float4 loads), one packed
-// (score, index) key per chunk, reduced by a finishing kernel (no atomics).
+// Work layout: every vocabulary pass runs in chunks of kChunk values per
+// 256-thread workgroup, a thread taking eight groups of four consecutive
+// values (one Philox call each) with all eight 16-byte loads issued before any
+// arithmetic. The log-sum-exp of a row is kept as per-chunk (max, sum) pairs
+// that its readers combine (19 pairs at V = 151936); the Gumbel argmax leaves
+// one packed (score, index) key per chunk, reduced by a finishing kernel (no
+// atomics).
 #include "common.h"
 #include "internal.h"
 
@@ -55,22 +58,37 @@ __device__ __forceinline__ float u01(uint32_t w) { return ((float)(w >> 9) + 0.5
 
 __device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
 
-// log-sum-exp of z * inv_t over one row per workgroup (256 threads)
-__global__ __launch_bounds__(256) void lse_kernel(const LseParams p) {
+constexpr int kGroups = kChunk / 1024;  // float4 groups per thread and chunk
+
+// Partial log-sum-exp of z * inv_t over one chunk of one row: pmax[row][chunk]
+// and psum[row][chunk] = sum over the chunk of exp(z * inv_t - pmax).
+__global__ __launch_bounds__(256) void lse_partial_kernel(const LseParams p) {
   __shared__ float red[2][4];
-  const int row = blockIdx.x;
+  const int row = blockIdx.y, chunk = blockIdx.x;
   const float* z = row < p.rows0 ? p.z0 + (long long)row * p.V : p.z1 + (long long)(row - p.rows0) * p.V;
-  float mx = -__builtin_inff(), sum = 0.f;
-  for (int v = threadIdx.x * 4; v < p.V; v += 1024) {  // V % 4 == 0
-    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(z + v) * p.inv_t;
-    const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    if (m4 > mx) {
-      sum *= __expf(mx - m4);
-      mx = m4;
-    }
-    sum += __expf(x[0] - mx) + __expf(x[1] - mx) + __expf(x[2] - mx) + __expf(x[3] - mx);
+  const int v0 = chunk * kChunk;
+  f32x4_t x[kGroups];
+#pragma unroll
+  for (int k = 0; k < kGroups; ++k) {
+    const int v = min(v0 + (k * 256 + (int)threadIdx.x) * 4, p.V - 4);  // clamped: loads stay in the row
+    x[k] = *reinterpret_cast<const f32x4_t*>(z + v);
   }
-  // wave, then workgroup: combine (max, sum) pairs
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int k = 0; k < kGroups; ++k) {
+    const bool in = v0 + (k * 256 + (int)threadIdx.x) * 4 < p.V;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (in) mx = fmaxf(mx, x[k][i] * p.inv_t);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < kGroups; ++k) {
+    const bool in = v0 + (k * 256 + (int)threadIdx.x) * 4 < p.V;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (in) sum += __expf(x[k][i] * p.inv_t - mx);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float om = __shfl_xor(mx, o), os = __shfl_xor(sum, o);
@@ -87,36 +105,51 @@ __global__ __launch_bounds__(256) void lse_kernel(const LseParams p) {
   if (threadIdx.x == 0) {
     float m = red[0][0];
     for (int w = 1; w < 4; ++w) m = fmaxf(m, red[0][w]);
-    float s = 0.f;
-    for (int w = 0; w < 4; ++w) s += red[1][w] * __expf(red[0][w] - m);
-    p.lse[row] = m + logf(s);
+    float t = 0.f;
+    for (int w = 0; w < 4; ++w) t += red[0][w] == -__builtin_inff() ? 0.f : red[1][w] * __expf(red[0][w] - m);
+    p.pmax[(long long)row * p.chunks + chunk] = m;
+    p.psum[(long long)row * p.chunks + chunk] = t;
   }
 }
 
-// The acceptance walk of one sequence (one thread each): writes the accepted
-// drafts into the target-token row a, the first rejected position (or B - 1)
-// into state[b].m and whether it was a rejection into state[b].rejected.
+// log-sum-exp of one row from its per-chunk pairs
+__device__ __forceinline__ float lse_of(const float* pmax, const float* psum, int row, int chunks) {
+  const float* pm = pmax + (long long)row * chunks;
+  const float* ps = psum + (long long)row * chunks;
+  float m = pm[0];
+  for (int c = 1; c < chunks; ++c) m = fmaxf(m, pm[c]);
+  float t = 0.f;
+  for (int c = 0; c < chunks; ++c) t += ps[c] * __expf(pm[c] - m);
+  return m + logf(t);
+}
+
+// Acceptance of one sequence per wave: lane j (1 <= j <= B-1) tests draft j
+// (the tests are independent given the drafts), the first failing lane ends
+// the accepted prefix (ballot). Writes the accepted drafts into the
+// target-token row a, the count m[b] and rejected[b] (0: every draft passed).
 __global__ __launch_bounds__(64) void accept_kernel(const AcceptParams p) {
-  const int b = blockIdx.x * 64 + threadIdx.x;
-  if (b >= p.batch) return;
+  const int b = blockIdx.x, j = threadIdx.x;
   const int B = p.B;
-  int m = 0, rejected = 0;
-  for (int j = 1; j < B; ++j) {
-    const int d = p.draft[b * (B - 1) + j - 1];
+  bool ok = true;
+  int d = 0;
+  if (j >= 1 && j < B) {
+    d = p.draft[b * (B - 1) + j - 1];
     const int dc = d < 0 ? 0 : (d >= p.V ? p.V - 1 : d);
-    const float lp = p.zt[(long long)(b * B + j - 1) * p.V + dc] * p.inv_t - p.lse_t[b * B + j - 1];
-    const float lq = p.zd[(long long)(b * (B - 1) + j - 1) * p.V + dc] * p.inv_t - p.lse_d[b * (B - 1) + j - 1];
+    const float lp = p.zt[(long long)(b * B + j - 1) * p.V + dc] * p.inv_t -
+                     lse_of(p.pmax, p.psum, p.rows_d + b * B + j - 1, p.chunks);
+    const float lq = p.zd[(long long)(b * (B - 1) + j - 1) * p.V + dc] * p.inv_t -
+                     lse_of(p.pmax, p.psum, b * (B - 1) + j - 1, p.chunks);
     const u32x4 w = philox4x32_10(0u, (uint32_t)(b * B + j), p.step, kTagAccept, p.seed_lo, p.seed_hi);
-    if (d == dc && logf(u01(w[0])) <= lp - lq) {
-      p.a[b * B + j - 1] = d;
-      m = j;
-    } else {
-      rejected = 1;
-      break;
-    }
+    ok = d == dc && logf(u01(w[0])) <= lp - lq;
   }
-  p.m[b] = m;
-  p.rejected[b] = rejected;
+  const unsigned long long fail = __ballot(!ok);  // lanes 1..B-1 only can fail
+  const int first = fail ? __ffsll((long long)fail) - 1 : B;  // first rejected position, or B
+  const int m = first - 1;
+  if (j >= 1 && j <= m) p.a[b * B + j - 1] = d;
+  if (j == 0) {
+    p.m[b] = m;
+    p.rejected[b] = first < B ? 1 : 0;
+  }
 }
 
 // One chunk of the Gumbel argmax of one item: MODE 0 draft sampling (item =
@@ -139,37 +172,43 @@ __global__ __launch_bounds__(256) void gumbel_argmax_kernel(const GumbelParams p
     const int B = p.B, m = p.m[item];
     const int tr = item * B + m;
     zp = p.zt + (long long)tr * p.V;
-    lse_p = p.lse_t[tr];
+    lse_p = lse_of(p.pmax, p.psum, p.rows_d + tr, p.lse_chunks);
     if (p.rejected[item]) {
       const int dr = item * (B - 1) + m;
       zq = p.zd + (long long)dr * p.V;
-      lse_q = p.lse_d[dr];
+      lse_q = lse_of(p.pmax, p.psum, dr, p.lse_chunks);
     }
     row_id = (uint32_t)item;
     tag = kTagResidual;
   }
+  f32x4_t x[kGroups], y[kGroups];
+#pragma unroll
+  for (int k = 0; k < kGroups; ++k) {
+    const int v = min(v0 + (k * 256 + (int)threadIdx.x) * 4, p.V - 4);  // clamped: loads stay in the row
+    x[k] = *reinterpret_cast<const f32x4_t*>(zp + v);
+    if (MODE == 1) y[k] = zq ? *reinterpret_cast<const f32x4_t*>(zq + v) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   float bv = -__builtin_inff();
   int bn = 0x7FFFFFFF;
-  const int vend = min(p.V, v0 + kChunk);
-  for (int v = v0 + threadIdx.x * 4; v < vend; v += 1024) {
+#pragma unroll
+  for (int k = 0; k < kGroups; ++k) {  // ascending v within the thread: lowest index on ties
+    const int v = v0 + (k * 256 + (int)threadIdx.x) * 4;
+    if (v >= p.V) continue;
     const u32x4 w = philox4x32_10((uint32_t)(v >> 2), row_id, p.step, tag, p.seed_lo, p.seed_hi);
-    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(zp + v);
-    f32x4_t y = {0.f, 0.f, 0.f, 0.f};
-    if (MODE == 1 && zq) y = *reinterpret_cast<const f32x4_t*>(zq + v);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float s;
       if (MODE == 0) {
-        s = x[i] * p.inv_t;
+        s = x[k][i] * p.inv_t;
       } else if (zq) {
-        const float r = __expf(x[i] * p.inv_t - lse_p) - __expf(y[i] * p.inv_t - lse_q);
+        const float r = __expf(x[k][i] * p.inv_t - lse_p) - __expf(y[k][i] * p.inv_t - lse_q);
         s = r > 0.f ? logf(r) : -__builtin_inff();
       } else {
-        s = x[i] * p.inv_t - lse_p;
+        s = x[k][i] * p.inv_t - lse_p;
       }
       if (s != -__builtin_inff()) {
         s += gumbel(u01(w[i]));
-        if (s > bv) {  // ascending v within the thread: lowest index on ties
+        if (s > bv) {
           bv = s;
           bn = v + i;
         }
@@ -215,19 +254,20 @@ __global__ __launch_bounds__(256) void gumbel_finish_kernel(const GumbelParams p
 int sample_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
 hipError_t launch_lse(const LseParams& p, hipStream_t st) {
-  if (p.V % 4 || p.rows0 < 0 || p.rows0 + p.rows1 < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lse_kernel, dim3(p.rows0 + p.rows1), dim3(256), 0, st, p);
+  if (p.V % 4 || p.V < 4 || p.rows0 < 0 || p.rows0 + p.rows1 < 1 || p.chunks != sample_chunks(p.V))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lse_partial_kernel, dim3(p.chunks, p.rows0 + p.rows1), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_accept(const AcceptParams& p, hipStream_t st) {
-  if (p.batch < 1 || p.B < 2) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(accept_kernel, dim3((p.batch + 63) / 64), dim3(64), 0, st, p);
+  if (p.batch < 1 || p.B < 2 || p.B > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(accept_kernel, dim3(p.batch), dim3(64), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_gumbel(const GumbelParams& p, int mode, hipStream_t st) {
-  if (p.V % 4 || p.items < 1 || p.chunks != sample_chunks(p.V)) return hipErrorInvalidValue;
+  if (p.V % 4 || p.V < 4 || p.items < 1 || p.chunks != sample_chunks(p.V)) return hipErrorInvalidValue;
   const dim3 grid(p.chunks, p.items);
   if (mode == 0) {
     hipLaunchKernelGGL(gumbel_argmax_kernel<0>, grid, dim3(256), 0, st, p);
