@@ -81,4 +81,31 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
   return ((unsigned long long)orderable(v) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
+// --- direct global -> LDS loads (global_load_lds_dwordx4) -------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt with vmcnt(N) only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// s_waitcnt lgkmcnt(0) only.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// Workgroup barrier for LDS data published by direct loads. The barrier
+// intrinsic alone does not order memory accesses in the compiler, so LDS
+// reads could be hoisted above it; the empty asm with a memory clobber keeps
+// every memory access on its side, and the scheduling barriers keep the
+// machine scheduler from moving instructions across. No s_waitcnt comes with
+// it: each wave waits for its own direct loads (vmcnt) before calling it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace dfl

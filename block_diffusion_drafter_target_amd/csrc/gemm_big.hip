@@ -48,18 +48,6 @@ constexpr int kStages = 5;   // 160 KB of LDS
 constexpr int kFrags = 32;           // per stage: 16 weight fragments, then 16 activation fragments
 constexpr int kGroupM = 4;           // row tiles per group of the tile order
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt with vmcnt(N) only (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// s_waitcnt lgkmcnt(0) only.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
-
 // Wave layout of a WAVES-wave workgroup (8: wave tiles of 128 rows x 64
 // weight rows).
 template <int WAVES>
