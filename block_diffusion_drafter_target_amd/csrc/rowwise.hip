@@ -38,8 +38,13 @@ __device__ __forceinline__ float block_sum_512(float v, float* red) {
 // addresses (a guarded load becomes a branch, and the compiler waits for
 // every outstanding load where branches join); out-of-range values are
 // dropped by a select.
-__device__ __forceinline__ void add_splits(f32x4_t (&v)[kMaxC4], const float* P, long long s_stride,
-                                           int splits, long long row_off, int n4, float keep_v) {
+// SB splits per batch; add_splits picks the smallest batch that covers the
+// split count (one split, a whole ingest chunk, would otherwise load eight
+// copies of the same partial).
+template <int SB>
+__device__ __forceinline__ void add_splits_sb(f32x4_t (&v)[kMaxC4], const float* P, long long s_stride,
+                                              int splits, long long row_off, int n4, float keep_v) {
+  constexpr int kSplitBatch = SB;
   for (int s0 = 0; s0 < splits; s0 += kSplitBatch) {
     f32x4_t t[kMaxC4][kSplitBatch];
 #pragma unroll
@@ -61,6 +66,18 @@ __device__ __forceinline__ void add_splits(f32x4_t (&v)[kMaxC4], const float* P,
       for (int j = 0; j < kSplitBatch; ++j)
         if (threadIdx.x + c * kRowThreads < n4 && s0 + j < splits) v[c] += t[c][j];
   }
+}
+
+__device__ __forceinline__ void add_splits(f32x4_t (&v)[kMaxC4], const float* P, long long s_stride,
+                                           int splits, long long row_off, int n4, float keep_v) {
+  if (splits == 1)
+    add_splits_sb<1>(v, P, s_stride, splits, row_off, n4, keep_v);
+  else if (splits <= 2)
+    add_splits_sb<2>(v, P, s_stride, splits, row_off, n4, keep_v);
+  else if (splits <= 4)
+    add_splits_sb<4>(v, P, s_stride, splits, row_off, n4, keep_v);
+  else
+    add_splits_sb<kSplitBatch>(v, P, s_stride, splits, row_off, n4, keep_v);
 }
 
 // Unpacks four bf16 (two 32-bit words) to fp32.
@@ -188,8 +205,10 @@ __global__ __launch_bounds__(kRowThreads) void row_norm_kernel(const RowNormPara
 // is already clamped to a valid lane. Loads are unconditional (see
 // add_splits); lanes that hold no pair (active false) return zeros, so that
 // wave sums over the head see only its D values.
-__device__ __forceinline__ void sum_pair(const float* src, long long s_stride, int splits, int half,
-                                         bool active, float& x1, float& x2) {
+template <int SB>
+__device__ __forceinline__ void sum_pair_sb(const float* src, long long s_stride, int splits, int half,
+                                            bool active, float& x1, float& x2) {
+  constexpr int kSplitBatch = SB;
   x1 = 0.f;
   x2 = 0.f;
   for (int s0 = 0; s0 < splits; s0 += kSplitBatch) {
@@ -212,6 +231,20 @@ __device__ __forceinline__ void sum_pair(const float* src, long long s_stride, i
     x1 = 0.f;
     x2 = 0.f;
   }
+}
+
+// Sum of the split partials of a lane's pair (i, i + half), in batches that
+// match the split count (see add_splits).
+__device__ __forceinline__ void sum_pair(const float* src, long long s_stride, int splits, int half,
+                                         bool active, float& x1, float& x2) {
+  if (splits == 1)
+    sum_pair_sb<1>(src, s_stride, splits, half, active, x1, x2);
+  else if (splits <= 2)
+    sum_pair_sb<2>(src, s_stride, splits, half, active, x1, x2);
+  else if (splits <= 4)
+    sum_pair_sb<4>(src, s_stride, splits, half, active, x1, x2);
+  else
+    sum_pair_sb<kSplitBatch>(src, s_stride, splits, half, active, x1, x2);
 }
 
 // ---------------------------------------------------------------------------
@@ -273,11 +306,15 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
 // ---------------------------------------------------------------------------
 // KV injection epilogue: for commit row i and layer l, k = RoPE(RMSNorm_head(
 // W_k c)), v = W_v c, scattered to (seq, pos); ctx_len[seq] grows to pos + 1.
-// One wave per (commit row, layer, head); the split partials, the commit row
-// and the gains are loaded together, the RoPE row once the position is known.
+// One wave per (block of kInjectRows commit rows, layer, head): the commit
+// rows, split partials and RoPE rows of the whole block are loaded before any
+// arithmetic (a wave per single row left the context ingest bound by workgroup
+// starts: 81,920 workgroups of under 1 KB each for a 4096-row chunk).
+constexpr int kInjectRows = 8;
+
 __global__ __launch_bounds__(256) void inject_post_kernel(const InjectPostParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = p.c0 + blockIdx.x, l = blockIdx.y;
+  const int i0 = p.c0 + blockIdx.x * kInjectRows, l = blockIdx.y;
   const int head = blockIdx.z * 4 + wave;
   if (head >= 2 * p.Hkv) return;
   const int D = p.D, half = D >> 1;
@@ -285,39 +322,55 @@ __global__ __launch_bounds__(256) void inject_post_kernel(const InjectPostParams
   const bool active = lane < half;
   const int li = active ? lane : 0;
   int nc = *p.n_commit;
-  const int src = p.commit_rows[3 * i], seq = p.commit_rows[3 * i + 1], pos = p.commit_rows[3 * i + 2];
-  float x1, x2;
-  sum_pair(p.P + (long long)l * p.p_z_stride + (long long)(i - p.c0) * width + head * D + li, p.p_s_stride,
-           p.splits, half, active, x1, x2);
-  const float g1 = bf2f(p.gk[l][li]), g2 = bf2f(p.gk[l][li + half]);
-  const int rpos = pos < 0 ? 0 : (pos >= p.rope_max ? p.rope_max - 1 : pos);
-  const float2 cs = reinterpret_cast<const float2*>(p.rope)[(long long)rpos * half + li];
   nc = nc < 0 ? 0 : (nc > p.max_commit ? p.max_commit : nc);
-  if (i >= nc || i >= p.c1) return;
-  if (src < 0 || src >= p.n_ctx_rows || seq < 0 || seq >= p.batch) return;
+  const int iend = min(min(nc, p.c1), i0 + kInjectRows);
+  int src[kInjectRows], seq[kInjectRows], pos[kInjectRows];
+  float x1[kInjectRows], x2[kInjectRows];
+  float2 cs[kInjectRows];
+#pragma unroll
+  for (int r = 0; r < kInjectRows; ++r) {  // clamped rows: every load in bounds, results unused
+    const int i = min(i0 + r, p.c1 - 1);
+    src[r] = p.commit_rows[3 * i];
+    seq[r] = p.commit_rows[3 * i + 1];
+    pos[r] = p.commit_rows[3 * i + 2];
+  }
+#pragma unroll
+  for (int r = 0; r < kInjectRows; ++r) {
+    const int i = min(i0 + r, p.c1 - 1);
+    sum_pair(p.P + (long long)l * p.p_z_stride + (long long)(i - p.c0) * width + head * D + li, p.p_s_stride,
+             p.splits, half, active, x1[r], x2[r]);
+    const int rpos = pos[r] < 0 ? 0 : (pos[r] >= p.rope_max ? p.rope_max - 1 : pos[r]);
+    cs[r] = reinterpret_cast<const float2*>(p.rope)[(long long)rpos * half + li];
+  }
+  const float g1 = bf2f(p.gk[l][li]), g2 = bf2f(p.gk[l][li + half]);
   const bool first = l == 0 && blockIdx.z == 0 && threadIdx.x == 0;
-  if (pos < 0 || pos >= p.max_ctx || pos >= p.rope_max) {
-    if (first) p.status[seq] = kErrCapacity;
-    return;
-  }
   const int g = head < p.Hkv ? head : head - p.Hkv;
-  const long long off = ((((long long)l * p.batch + seq) * p.Hkv + g) * p.max_ctx + pos) * D;
-  if (head >= p.Hkv) {
-    if (active) {
-      p.vc[off + lane] = f2bf(x1);
-      p.vc[off + lane + half] = f2bf(x2);
+#pragma unroll
+  for (int r = 0; r < kInjectRows; ++r) {
+    if (i0 + r >= iend) break;
+    if (src[r] < 0 || src[r] >= p.n_ctx_rows || seq[r] < 0 || seq[r] >= p.batch) continue;
+    if (pos[r] < 0 || pos[r] >= p.max_ctx || pos[r] >= p.rope_max) {
+      if (first) p.status[seq[r]] = kErrCapacity;
+      continue;
     }
-  } else {
-    const float ss = wave_sum(x1 * x1 + x2 * x2);
-    const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
-    if (active) {
-      const float y1 = x1 * inv * g1;
-      const float y2 = x2 * inv * g2;
-      p.kc[off + lane] = f2bf(y1 * cs.x - y2 * cs.y);
-      p.kc[off + lane + half] = f2bf(y1 * cs.y + y2 * cs.x);
+    const long long off = ((((long long)l * p.batch + seq[r]) * p.Hkv + g) * p.max_ctx + pos[r]) * D;
+    if (head >= p.Hkv) {
+      if (active) {
+        p.vc[off + lane] = f2bf(x1[r]);
+        p.vc[off + lane + half] = f2bf(x2[r]);
+      }
+    } else {
+      const float ss = wave_sum(x1[r] * x1[r] + x2[r] * x2[r]);
+      const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
+      if (active) {
+        const float y1 = x1[r] * inv * g1;
+        const float y2 = x2[r] * inv * g2;
+        p.kc[off + lane] = f2bf(y1 * cs[r].x - y2 * cs[r].y);
+        p.kc[off + lane + half] = f2bf(y1 * cs[r].y + y2 * cs[r].x);
+      }
     }
+    if (first) atomicMax(p.ctx_len + seq[r], pos[r] + 1);
   }
-  if (first) atomicMax(p.ctx_len + seq, pos + 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -439,7 +492,8 @@ hipError_t launch_qkv_post(const QkvPostParams& p, hipStream_t st) {
 
 hipError_t launch_inject_post(const InjectPostParams& p, hipStream_t st) {
   if (p.c1 <= p.c0) return hipSuccess;
-  hipLaunchKernelGGL(inject_post_kernel, dim3(p.c1 - p.c0, p.n_layers, (2 * p.Hkv + 3) / 4), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(inject_post_kernel, dim3((p.c1 - p.c0 + kInjectRows - 1) / kInjectRows, p.n_layers, (2 * p.Hkv + 3) / 4),
+                     dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

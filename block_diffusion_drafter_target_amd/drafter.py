@@ -196,9 +196,12 @@ class Drafter:
         if n > self.max_rows:
             raise ValueError("ingest rows exceed max_rows of the workspace")
         self.fuse_ctx(taps, n, ctx)
-        rows = torch.stack([torch.arange(n, dtype=torch.int32), torch.full((n,), b, dtype=torch.int32),
-                            start + torch.arange(n, dtype=torch.int32)], dim=1).to(self.device)
-        cnt = torch.tensor([n], dtype=torch.int32, device=self.device)
+        # commit rows (src, seq, pos) built on the device: no host round trip
+        # between the two calls
+        i32 = dict(dtype=torch.int32, device=self.device)
+        ar = torch.arange(n, **i32)
+        rows = torch.stack([ar, torch.full((n,), b, **i32), ar + start], dim=1).contiguous()
+        cnt = torch.full((1,), n, **i32)
         self.inject_kv(ctx, n, rows, cnt, n)
 
 
