@@ -89,6 +89,13 @@ SHAPES = {
     "mlp-wide-b2": synth.DraftConfig(name="mlp-wide-b2", hidden=256, n_layers=1, n_q_heads=4, n_kv_heads=2,
                                      head_dim=64, intermediate=8192, vocab=1024, n_tap=2, block=16,
                                      batch=2, ctx_len=0),
+    # 19 sequences x 16 rows = 304 block rows: every layer GEMM on the
+    # large-tile kernel (two 256-row tiles, the second ragged; split-K qkv/o/down,
+    # single-pass SwiGLU), the LM head over 285 rows with a vocabulary that ends
+    # inside a 256-column tile; ingests of up to 300 rows take it too
+    "big-b19": synth.DraftConfig(name="big-b19", hidden=256, n_layers=2, n_q_heads=4, n_kv_heads=2,
+                                 head_dim=64, intermediate=768, vocab=1040, n_tap=2, block=16,
+                                 batch=19, ctx_len=0),
     # long contexts: 128-key attention slices (chunks of >= 512 keys), G = 8, D = 64
     "long-d64": synth.DraftConfig(name="long-d64", hidden=512, n_layers=1, n_q_heads=64, n_kv_heads=8,
                                   head_dim=64, intermediate=512, vocab=1024, n_tap=2, block=16,
@@ -102,4 +109,5 @@ SHAPES = {
 CTX = {"gqa-d128": [1, 300, 777, 0, 64], "g8-d64": [500, 33], "b12": [129, 0, 64],
        "tiled-b9": [17, 260, 0, 64, 1, 333, 90, 128, 2],
        "long-d64": [8900, 8500, 8193, 100], "long-d128": [16900, 16000, 9000, 3],
-       "mlp-wide": [40, 0, 17, 300, 64, 1, 129, 90, 33, 7], "mlp-wide-b2": [70, 250]}
+       "mlp-wide": [40, 0, 17, 300, 64, 1, 129, 90, 33, 7], "mlp-wide-b2": [70, 250],
+       "big-b19": [0, 1, 17, 64, 129, 260, 300, 33, 90, 5, 200, 150, 75, 12, 280, 45, 100, 3, 64]}
