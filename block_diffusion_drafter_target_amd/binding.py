@@ -88,8 +88,8 @@ def load() -> C.CDLL:
     lib.dflash_verify_accept.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, i32, vp, vp, vp, vp,
                                          vp, vp, vp, vp, vp]
     u64, f32 = C.c_uint64, C.c_float
-    lib.dflash_draft_block_sample.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, f32, u64, i32, vp, sz, vp]
-    lib.dflash_verify_sample.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, f32, u64, i32, vp, i32, vp, vp,
+    lib.dflash_draft_block_sample.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, f32, u64, i32, vp, vp, sz, vp]
+    lib.dflash_verify_sample.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, f32, u64, i32, vp, vp, i32, vp, vp,
                                          vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dflash_sample_logits.argtypes = [vp, vp, i32, f32, u64, i32, i32, vp, vp, sz, vp]
     lib.dflash_pack_matrix.argtypes = [vp, vp, i32, i32, vp]
@@ -187,18 +187,19 @@ def dflash_verify_accept(model, kv, draft, target_argmax, stop_ids, n_stop, budg
         emitted, n_emit, done, commit_rows, n_commit, stream))
 
 
-def dflash_draft_block_sample(model, kv, anchor, draft, logits, temperature: float, seed: int, step: int, ws,
-                              ws_bytes, stream) -> None:
+def dflash_draft_block_sample(model, kv, anchor, draft, logits, temperature: float, seed: int, step: int,
+                              step_dev, ws, ws_bytes, stream) -> None:
     _check("dflash_draft_block_sample", load().dflash_draft_block_sample(
-        model, C.byref(kv), anchor, draft, logits, temperature, seed, step, ws, ws_bytes, stream))
+        model, C.byref(kv), anchor, draft, logits, temperature, seed, step, step_dev, ws, ws_bytes, stream))
 
 
 def dflash_verify_sample(model, kv, draft, draft_logits, target_logits, temperature: float, seed: int, step: int,
-                         stop_ids, n_stop, budget, accept_len, anchor_out, emitted, n_emit, done, commit_rows,
-                         n_commit, ws, ws_bytes, stream) -> None:
+                         step_dev, stop_ids, n_stop, budget, accept_len, anchor_out, emitted, n_emit, done,
+                         commit_rows, n_commit, ws, ws_bytes, stream) -> None:
     _check("dflash_verify_sample", load().dflash_verify_sample(
-        model, C.byref(kv), draft, draft_logits, target_logits, temperature, seed, step, stop_ids, n_stop,
-        budget, accept_len, anchor_out, emitted, n_emit, done, commit_rows, n_commit, ws, ws_bytes, stream))
+        model, C.byref(kv), draft, draft_logits, target_logits, temperature, seed, step, step_dev, stop_ids,
+        n_stop, budget, accept_len, anchor_out, emitted, n_emit, done, commit_rows, n_commit, ws, ws_bytes,
+        stream))
 
 
 def dflash_sample_logits(model, logits, rows: int, temperature: float, seed: int, step: int, row0: int, tokens,

@@ -963,7 +963,8 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
 
 dflash_status dflash_draft_block_sample(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
                                         int32_t* draft, float* logits, float temperature, uint64_t seed,
-                                        int32_t step, void* ws, size_t ws_bytes, void* stream) {
+                                        int32_t step, const int32_t* step_dev, void* ws, size_t ws_bytes,
+                                        void* stream) {
   if (!m || !anchor || !draft || !logits || !ws) return DFLASH_ERR_NULL;
   if (m->target) return DFLASH_ERR_UNSUPPORTED;
   if (!sample_temperature_ok(temperature)) return DFLASH_ERR_SHAPE;
@@ -982,7 +983,7 @@ dflash_status dflash_draft_block_sample(const dflash_model* m, dflash_kv* kv, co
   io.dbg_logits = logits;
   const dflash_status s = run_stack(m, kv, io, ws, ws_bytes, stream);
   if (s != DFLASH_OK) return s;
-  dfl::GumbelParams g;
+  dfl::GumbelParams g{};
   std::memset(&g, 0, sizeof(g));
   g.z = logits;
   g.B = c.block;
@@ -993,6 +994,7 @@ dflash_status dflash_draft_block_sample(const dflash_model* m, dflash_kv* kv, co
   g.seed_lo = (uint32_t)seed;
   g.seed_hi = (uint32_t)(seed >> 32);
   g.step = (uint32_t)step;
+  g.step_dev = step_dev;
   g.keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + sw.keys);
   g.out = draft;
   g.status = kv->status;
@@ -1077,7 +1079,7 @@ dflash_status dflash_sample_logits(const dflash_model* m, const float* logits, i
   const dflash_config& c = m->cfg;
   const size_t need = align256((size_t)dfl::sample_chunks(c.vocab) * rows * 8);
   if (ws_bytes < need) return DFLASH_ERR_WORKSPACE;
-  dfl::GumbelParams g;
+  dfl::GumbelParams g{};
   std::memset(&g, 0, sizeof(g));
   g.z = logits;
   g.row0 = row0;
@@ -1096,7 +1098,8 @@ dflash_status dflash_sample_logits(const dflash_model* m, const float* logits, i
 
 dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, const int32_t* draft,
                                    const float* draft_logits, const float* target_logits, float temperature,
-                                   uint64_t seed, int32_t step, const int32_t* stop_ids, int32_t n_stop,
+                                   uint64_t seed, int32_t step, const int32_t* step_dev, const int32_t* stop_ids,
+                                   int32_t n_stop,
                                    int32_t* budget, int32_t* accept_len, int32_t* anchor_out, int32_t* emitted,
                                    int32_t* n_emit, int32_t* done, int32_t* commit_rows, int32_t* n_commit,
                                    void* ws, size_t ws_bytes, void* stream) {
@@ -1123,7 +1126,7 @@ dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, c
   int32_t* mm = reinterpret_cast<int32_t*>(base + sw.m);
   int32_t* rej = reinterpret_cast<int32_t*>(base + sw.rej);
   prof::Scope ps(DFLASH_PHASE_VERIFY, st);
-  dfl::LseParams lp;
+  dfl::LseParams lp{};
   lp.z0 = draft_logits;
   lp.z1 = target_logits;
   lp.rows0 = batch * (B - 1);
@@ -1135,7 +1138,7 @@ dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, c
   lp.psum = psum;
   hipError_t e = dfl::launch_lse(lp, st);
   if (e != hipSuccess) return DFLASH_ERR_HIP;
-  dfl::AcceptParams ap;
+  dfl::AcceptParams ap{};
   ap.draft = draft;
   ap.zd = draft_logits;
   ap.zt = target_logits;
@@ -1150,11 +1153,12 @@ dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, c
   ap.seed_lo = (uint32_t)seed;
   ap.seed_hi = (uint32_t)(seed >> 32);
   ap.step = (uint32_t)step;
+  ap.step_dev = step_dev;
   ap.a = a;
   ap.m = mm;
   ap.rejected = rej;
   if ((e = dfl::launch_accept(ap, st)) != hipSuccess) return DFLASH_ERR_HIP;
-  dfl::GumbelParams g;
+  dfl::GumbelParams g{};
   std::memset(&g, 0, sizeof(g));
   g.zd = draft_logits;
   g.zt = target_logits;
@@ -1172,6 +1176,7 @@ dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, c
   g.seed_lo = ap.seed_lo;
   g.seed_hi = ap.seed_hi;
   g.step = ap.step;
+  g.step_dev = step_dev;
   g.keys = reinterpret_cast<unsigned long long*>(base + sw.keys);
   g.a = a;
   if ((e = dfl::launch_gumbel(g, 1, st)) != hipSuccess) return DFLASH_ERR_HIP;

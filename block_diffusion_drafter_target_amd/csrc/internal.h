@@ -244,6 +244,7 @@ struct AcceptParams {
   int batch, B, V;
   float inv_t;
   uint32_t seed_lo, seed_hi, step;
+  const int32_t* step_dev;  // or NULL: the draws' step is step + *step_dev
   int32_t* a;  // [batch, B]
   int32_t* m;
   int32_t* rejected;
@@ -268,6 +269,7 @@ struct GumbelParams {
   int B, V, items, chunks;
   float inv_t;
   uint32_t seed_lo, seed_hi, step;
+  const int32_t* step_dev;  // or NULL: the draws' step is step + *step_dev
   unsigned long long* keys;  // [chunks, items]
   int32_t* out;
   const int32_t* status;

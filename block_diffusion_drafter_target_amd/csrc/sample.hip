@@ -139,7 +139,8 @@ __global__ __launch_bounds__(64) void accept_kernel(const AcceptParams p) {
                      lse_of(p.pmax, p.psum, p.rows_d + b * B + j - 1, p.chunks);
     const float lq = p.zd[(long long)(b * (B - 1) + j - 1) * p.V + dc] * p.inv_t -
                      lse_of(p.pmax, p.psum, b * (B - 1) + j - 1, p.chunks);
-    const u32x4 w = philox4x32_10(0u, (uint32_t)(b * B + j), p.step, kTagAccept, p.seed_lo, p.seed_hi);
+    const uint32_t step = p.step + (p.step_dev ? (uint32_t)*p.step_dev : 0u);
+    const u32x4 w = philox4x32_10(0u, (uint32_t)(b * B + j), step, kTagAccept, p.seed_lo, p.seed_hi);
     ok = d == dc && logf(u01(w[0])) <= lp - lq;
   }
   const unsigned long long fail = __ballot(!ok);  // lanes 1..B-1 only can fail
@@ -181,6 +182,7 @@ __global__ __launch_bounds__(256) void gumbel_argmax_kernel(const GumbelParams p
     row_id = (uint32_t)item;
     tag = kTagResidual;
   }
+  const uint32_t step = p.step + (p.step_dev ? (uint32_t)*p.step_dev : 0u);
   f32x4_t x[kGroups], y[kGroups];
 #pragma unroll
   for (int k = 0; k < kGroups; ++k) {
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(256) void gumbel_argmax_kernel(const GumbelParams p
   for (int k = 0; k < kGroups; ++k) {  // ascending v within the thread: lowest index on ties
     const int v = v0 + (k * 256 + (int)threadIdx.x) * 4;
     if (v >= p.V) continue;
-    const u32x4 w = philox4x32_10((uint32_t)(v >> 2), row_id, p.step, tag, p.seed_lo, p.seed_hi);
+    const u32x4 w = philox4x32_10((uint32_t)(v >> 2), row_id, step, tag, p.seed_lo, p.seed_hi);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float s;

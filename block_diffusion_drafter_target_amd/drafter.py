@@ -143,29 +143,34 @@ class Drafter:
                               bd.ptr(dbg_hidden), bd.ptr(self.ws), self.ws_bytes, self.stream())
         return self.draft
 
-    def draft_block_sample(self, temperature: float, seed: int, step: int, anchor=None):
+    def draft_block_sample(self, temperature: float, seed: int, step: int, anchor=None, step_dev=None):
         """Sampling-mode draft block: tokens sampled from the drafter's own
         distributions (Gumbel-max, Philox draws of (seed, step)); the raw logits
         stay in self.draft_logits [batch*(B-1), V] for the verify."""
         a = self.anchor if anchor is None else anchor
+        self._ensure_draft_logits()
+        bd.dflash_draft_block_sample(self.model, self.kv, bd.ptr(a), bd.ptr(self.draft), bd.ptr(self.draft_logits),
+                                     float(temperature), int(seed), int(step), bd.ptr(step_dev), bd.ptr(self.ws),
+                                     self.ws_bytes, self.stream())
+        return self.draft
+
+    def _ensure_draft_logits(self):
         if getattr(self, "draft_logits", None) is None:
             torch = _torch()
             self.draft_logits = torch.empty((self.batch * (self.cfg.block - 1), self.cfg.vocab),
                                             dtype=torch.float32, device=self.device)
-        bd.dflash_draft_block_sample(self.model, self.kv, bd.ptr(a), bd.ptr(self.draft), bd.ptr(self.draft_logits),
-                                     float(temperature), int(seed), int(step), bd.ptr(self.ws), self.ws_bytes,
-                                     self.stream())
-        return self.draft
+        return self.draft_logits
 
     def verify_sample(self, target_logits, temperature: float, seed: int, step: int, stop_ids=None, budget=None,
-                      draft=None, draft_logits=None):
+                      draft=None, draft_logits=None, step_dev=None):
         """Speculative-sampling verification against the target's logits
         [batch*B, V] (fp32) of the block rows; same outputs as verify_accept."""
         d = self.draft if draft is None else draft
         zd = self.draft_logits if draft_logits is None else draft_logits
         n_stop = 0 if stop_ids is None else int(stop_ids.numel())
         bd.dflash_verify_sample(self.model, self.kv, bd.ptr(d), bd.ptr(zd), bd.ptr(target_logits),
-                                float(temperature), int(seed), int(step), bd.ptr(stop_ids), n_stop, bd.ptr(budget),
+                                float(temperature), int(seed), int(step), bd.ptr(step_dev), bd.ptr(stop_ids), n_stop,
+                                bd.ptr(budget),
                                 bd.ptr(self.accept_len), bd.ptr(self.anchor_out), bd.ptr(self.emitted),
                                 bd.ptr(self.n_emit), bd.ptr(self.done), bd.ptr(self.commit_rows),
                                 bd.ptr(self.n_commit), bd.ptr(self.ws), self.ws_bytes, self.stream())
@@ -428,14 +433,16 @@ def _spec_sample(drafter: Drafter, target: "DeviceTarget", prompt, max_new_token
 
 
 # ---------------------------------------------------------------------------
-# the whole greedy loop on the device
+# the whole loop on the device
 # ---------------------------------------------------------------------------
 
 class _LoopState:
     """Device buffers of spec_generate_device (fixed shapes, so a step can be
-    captured in a graph)."""
+    captured in a graph). In sampling mode (temperature > 0) the step counter
+    keying the draws lives on the device too, so every replay of a captured
+    step draws afresh."""
 
-    def __init__(self, torch, batch, B, max_new, dev, stops):
+    def __init__(self, torch, batch, B, max_new, dev, stops, temperature=0.0, seed=0, vocab=0):
         i32 = dict(dtype=torch.int32, device=dev)
         self.tokens = torch.zeros((batch, B), **i32)       # target input [anchor, d_1..d_{B-1}]
         self.out = torch.full((batch, max_new + 1), -1, **i32)  # last column: sink of unused lanes
@@ -446,16 +453,23 @@ class _LoopState:
         self.row = (torch.arange(batch, **i32) * (max_new + 1))[:, None]
         self.stops = stops
         self.max_new = max_new
+        self.temperature, self.seed = float(temperature), int(seed)
+        if self.temperature > 0.0:
+            self.step = torch.ones(1, **i32)  # step 0 drew the first token after the prompt
+            self.zt = torch.empty((batch * B, vocab), dtype=torch.float32, device=dev)
 
 
 def _prefill_device(drafter: Drafter, target: DeviceTarget, prompts, st: _LoopState):
     """Target passes over the prompts (passes of up to max_n tokens, ragged
     prompts committed row by row), the drafter's fuse + inject of the same
-    rows, and the first anchor (the target's token after each prompt)."""
+    rows, and the first anchor: the target's token after each prompt, greedy
+    or, in sampling mode, drawn from the target's distribution after the
+    prompt with the draws of step 0 (RNG row = sequence index)."""
     torch = _torch()
     dev, batch = target.device, target.batch
     P = max(len(p) for p in prompts)
     anchor = np.zeros(batch, np.int32)
+    sampling = st.temperature > 0.0
     for i0 in range(0, P, target.max_n):
         n = min(target.max_n, P - i0)
         toks = np.zeros((batch, n), np.int32)
@@ -465,7 +479,8 @@ def _prefill_device(drafter: Drafter, target: DeviceTarget, prompts, st: _LoopSt
                 if i0 + j < len(p):
                     toks[b, j] = p[i0 + j]
                     rows.append((b * n + j, b, i0 + j))
-        a, taps = target.pass_tokens(torch.from_numpy(toks).to(dev))
+        z = torch.empty((batch * n, drafter.cfg.vocab), dtype=torch.float32, device=dev) if sampling else None
+        a, taps = target.pass_tokens(torch.from_numpy(toks).to(dev), dbg_logits=z)
         crow = torch.zeros((batch * n, 3), dtype=torch.int32, device=dev)
         if rows:
             crow[:len(rows)] = torch.tensor(rows, dtype=torch.int32, device=dev)
@@ -476,7 +491,12 @@ def _prefill_device(drafter: Drafter, target: DeviceTarget, prompts, st: _LoopSt
         a = a.cpu().numpy()
         for b, p in enumerate(prompts):
             if i0 <= len(p) - 1 < i0 + n:
-                anchor[b] = a[b, len(p) - 1 - i0]
+                if sampling:
+                    r = b * n + len(p) - 1 - i0
+                    tok = drafter.sample_logits(z[r:r + 1], st.temperature, st.seed, 0, row0=b)
+                    anchor[b] = int(tok.item())
+                else:
+                    anchor[b] = a[b, len(p) - 1 - i0]
     drafter.anchor.copy_(torch.from_numpy(anchor))
     return anchor
 
@@ -484,15 +504,25 @@ def _prefill_device(drafter: Drafter, target: DeviceTarget, prompts, st: _LoopSt
 def device_step(drafter: Drafter, target: DeviceTarget, st: _LoopState) -> None:
     """One speculative step with no host synchronisation: draft, target pass
     over [anchor, draft], verify, commit in both caches, next anchor, and the
-    emitted tokens of sequences still running appended to the output."""
+    emitted tokens of sequences still running appended to the output. In
+    sampling mode the block is sampled, the target pass keeps its logits, the
+    verify is speculative sampling, and the device step counter advances."""
     torch = _torch()
     B = drafter.cfg.block
     batch = drafter.batch
-    drafter.draft_block(anchor=drafter.anchor)
+    sampling = st.temperature > 0.0
+    if sampling:
+        drafter.draft_block_sample(st.temperature, st.seed, 0, anchor=drafter.anchor, step_dev=st.step)
+    else:
+        drafter.draft_block(anchor=drafter.anchor)
     st.tokens[:, 0].copy_(drafter.anchor)
     st.tokens[:, 1:].copy_(drafter.draft)
-    a, taps = target.pass_tokens(st.tokens)
-    drafter.verify_accept(a, st.stops, st.budget)
+    a, taps = target.pass_tokens(st.tokens, dbg_logits=st.zt if sampling else None)
+    if sampling:
+        drafter.verify_sample(st.zt, st.temperature, st.seed, 0, st.stops, st.budget, step_dev=st.step)
+        st.step += 1
+    else:
+        drafter.verify_accept(a, st.stops, st.budget)
     target.commit(drafter.commit_rows, drafter.n_commit, batch * B)
     drafter.fuse_ctx(taps, batch * B, drafter.ctx)
     drafter.inject_kv(drafter.ctx, batch * B, drafter.commit_rows, drafter.n_commit, batch * B)
@@ -508,22 +538,29 @@ def device_step(drafter: Drafter, target: DeviceTarget, st: _LoopState) -> None:
 
 
 def spec_generate_device(drafter: Drafter, target: DeviceTarget, prompts, max_new_tokens: int,
-                         stop_token_ids: Sequence[int] = (), steps_per_sync: int = 8, graph: bool = True):
-    """Greedy speculative decoding of a batch with the drafter and the target on
-    the device: steps run without host synchronisation (``steps_per_sync`` of
-    them captured in one graph when ``graph``), stop ids and the token budget
-    are applied on the device, and the host only checks between groups of
-    steps whether every sequence has finished. Returns the tokens of each
+                         stop_token_ids: Sequence[int] = (), steps_per_sync: int = 8, graph: bool = True,
+                         temperature: float = 0.0, seed: int = 0):
+    """Speculative decoding of a batch with the drafter and the target on the
+    device, greedy at temperature 0 and speculative sampling above (seed keys
+    the draws; step s of the loop draws with step s, as spec_generate does for
+    one sequence): steps run without host synchronisation (``steps_per_sync``
+    of them captured in one graph when ``graph``), stop ids and the token
+    budget are applied on the device, and the host only checks between groups
+    of steps whether every sequence has finished. Returns the tokens of each
     sequence (as spec_generate does for one)."""
     torch = _torch()
     if drafter.batch != target.batch or len(prompts) != drafter.batch:
         raise ValueError("one prompt per sequence of the drafter and the target")
     if target.max_n < drafter.cfg.block:
         raise ValueError("the target's passes must hold a whole block")
+    if not temperature >= 0.0:
+        raise ValueError("temperature must be >= 0")
     dev = drafter.device
     B = drafter.cfg.block
     stops = torch.tensor(list(stop_token_ids), dtype=torch.int32, device=dev) if stop_token_ids else None
-    st = _LoopState(torch, drafter.batch, B, max_new_tokens, dev, stops)
+    st = _LoopState(torch, drafter.batch, B, max_new_tokens, dev, stops, temperature, seed, drafter.cfg.vocab)
+    if st.temperature > 0.0:
+        drafter._ensure_draft_logits()  # allocated before any capture: a graph must not own it
     target.reset()
     drafter.ctx_len.zero_()
     drafter.status.zero_()

@@ -210,10 +210,13 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
  *   temperature > 0, finite (else DFLASH_ERR_SHAPE)
  *   seed, step  the draws' key and step counter (a new step per block keeps
  *               the draws of different steps independent)
+ *   step_dev    device int32 [1] or NULL: the draws' step is step + *step_dev
+ *               (a loop captured in a graph advances it on the device)
  * ws: dflash_workspace_bytes covers it. */
 dflash_status dflash_draft_block_sample(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
                                         int32_t* draft, float* logits, float temperature, uint64_t seed,
-                                        int32_t step, void* ws, size_t ws_bytes, void* stream);
+                                        int32_t step, const int32_t* step_dev, void* ws, size_t ws_bytes,
+                                        void* stream);
 
 /* Sampling mode: Gumbel-max samples of softmax(logits / T) for `rows` rows of
  * the model's vocabulary width, the draw of row r being (seed, tag 0, step,
@@ -244,10 +247,12 @@ dflash_status dflash_sample_logits(const dflash_model* m, const float* logits, i
  *   target_logits device fp32 [batch*B, V]: the target's logits after rows
  *                 0..B-1 of [anchor, d_1..d_{B-1}]
  *   temperature   > 0, finite (else DFLASH_ERR_SHAPE)
+ *   step_dev      device int32 [1] or NULL: the draws' step is step + *step_dev
  * ws: dflash_workspace_bytes covers it. ctx_len is read, never written. */
 dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, const int32_t* draft,
                                    const float* draft_logits, const float* target_logits, float temperature,
-                                   uint64_t seed, int32_t step, const int32_t* stop_ids, int32_t n_stop,
+                                   uint64_t seed, int32_t step, const int32_t* step_dev, const int32_t* stop_ids,
+                                   int32_t n_stop,
                                    int32_t* budget, int32_t* accept_len, int32_t* anchor_out, int32_t* emitted,
                                    int32_t* n_emit, int32_t* done, int32_t* commit_rows, int32_t* n_commit,
                                    void* ws, size_t ws_bytes, void* stream);

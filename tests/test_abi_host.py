@@ -219,12 +219,12 @@ def test_sampling_entry_points_check_arguments_without_a_gpu():
         ws = bd.dflash_workspace_bytes(h, 2, 2048, 32)
         P = 0x1000
         ds = lib.dflash_draft_block_sample
-        assert ds(h, C.byref(kv), P, P, None, 1.0, 7, 1, P, ws, None) == bd.DFLASH_ERR_NULL  # logits required
+        assert ds(h, C.byref(kv), P, P, None, 1.0, 7, 1, None, P, ws, None) == bd.DFLASH_ERR_NULL  # logits
         for t in (0.0, -1.0, float("nan"), float("inf")):
-            assert ds(h, C.byref(kv), P, P, P, t, 7, 1, P, ws, None) == bd.DFLASH_ERR_SHAPE
-        assert ds(h, C.byref(kv), P, P, P, 1.0, 7, 1, P, 16, None) == bd.DFLASH_ERR_WORKSPACE
+            assert ds(h, C.byref(kv), P, P, P, t, 7, 1, None, P, ws, None) == bd.DFLASH_ERR_SHAPE
+        assert ds(h, C.byref(kv), P, P, P, 1.0, 7, 1, None, P, 16, None) == bd.DFLASH_ERR_WORKSPACE
         vs = lib.dflash_verify_sample
-        args = [P, P, P, 1.0, 7, 1, None, 0, None] + [P] * 7 + [P, ws, None]
+        args = [P, P, P, 1.0, 7, 1, None, None, 0, None] + [P] * 7 + [P, ws, None]
         bad = list(args)
         bad[1] = None  # draft logits
         assert vs(h, C.byref(kv), *bad) == bd.DFLASH_ERR_NULL
@@ -232,10 +232,10 @@ def test_sampling_entry_points_check_arguments_without_a_gpu():
         bad[3] = 0.0
         assert vs(h, C.byref(kv), *bad) == bd.DFLASH_ERR_SHAPE
         bad = list(args)
-        bad[7] = -1  # n_stop
+        bad[8] = -1  # n_stop
         assert vs(h, C.byref(kv), *bad) == bd.DFLASH_ERR_SHAPE
         bad = list(args)
-        bad[7] = 2  # stop ids missing
+        bad[8] = 2  # stop ids missing
         assert vs(h, C.byref(kv), *bad) == bd.DFLASH_ERR_NULL
         bad = list(args)
         bad[-2] = 64

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import gpu_helpers as gh
-from block_diffusion_drafter_target_amd import DeviceTarget, Drafter, synth
+from block_diffusion_drafter_target_amd import DeviceTarget, Drafter, spec_generate_device, synth
 from block_diffusion_drafter_target_amd.drafter import _spec_sample
 from oracle import ref
 from oracle import sampling as S
@@ -204,3 +204,38 @@ def test_sampling_loop_step_by_step(gpu_lib):
     assert again == out
     other, _ = _spec_sample(dr, tgt, prompt, cfg.n_new, (), T, SEED + 1)
     assert other != out
+
+
+def test_device_loop_sampling_matches_host_loop(gpu_lib):
+    """Sampling in the loop with no per-step host synchronisation (steps
+    captured in a graph, with the draws' step counter advanced on the device,
+    and run eagerly): one sequence emits exactly what the host-driven sampling
+    loop emits; in a batch of two, the first sequence (whose RNG rows are
+    those of a batch of one) emits the same again, and graph and eager runs
+    agree. A replayed graph that froze the step would repeat its draws and
+    diverge from the host loop."""
+    import torch
+    cfg = synth.CONFIGS["c1"]
+    W = synth.make_weights(cfg)
+    TW = synth.make_target_weights(cfg, W)
+    prompts = [list(synth.make_prompt(cfg, 64)), list(synth.make_prompt(cfg, 37, seed=11))]
+    n_new, S, T = cfg.n_new, 4, 0.9
+    max_ctx = 64 + n_new + (S + 2) * cfg.block + 16
+    tgt1 = DeviceTarget(cfg, TW, cfg.target_layers, cfg.tap_layers, max_ctx=max_ctx, max_n=16)
+    dr1 = Drafter(cfg, W, batch=1, max_ctx=max_ctx, max_rows=64)
+    host, ms = _spec_sample(dr1, tgt1, prompts[0], n_new, (), T, SEED)
+    assert len(ms) > S  # more steps than one graph holds: replays must draw afresh
+    for graph in (True, False):
+        one = spec_generate_device(dr1, tgt1, prompts[:1], n_new, steps_per_sync=S, graph=graph,
+                                   temperature=T, seed=SEED)
+        assert one[0] == host, f"batch 1, graph={graph}"
+    del tgt1, dr1
+    tgt = DeviceTarget(cfg, TW, cfg.target_layers, cfg.tap_layers, batch=2, max_ctx=max_ctx, max_n=16)
+    dr = Drafter(cfg, W, batch=2, max_ctx=max_ctx, max_rows=2 * 16)
+    outs = [spec_generate_device(dr, tgt, prompts, n_new, steps_per_sync=S, graph=graph, temperature=T, seed=SEED)
+            for graph in (True, False)]
+    assert outs[0] == outs[1]
+    assert outs[0][0] == host
+    assert len(outs[0][1]) == n_new and all(0 <= t < cfg.vocab for t in outs[0][1])
+    torch.cuda.synchronize()
+    gh.log(f"[device sampling loop] {len(ms)} host steps, mean accepted {np.mean(ms):.2f}")
