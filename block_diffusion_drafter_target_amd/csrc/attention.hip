@@ -12,7 +12,7 @@
 // one for the batch, sized on the device from the longest sequence's
 // L_b + B keys, so the work follows the real context rather than the cache
 // capacity and a ragged batch stays balanced; chunks past a sequence's end
-// exit at once. The chunk is walked in 64- or 128-key slices
+// exit at once. The chunk is walked in 64-key slices
 // staged through LDS (K row-major with a 16-byte XOR swizzle over the row's
 // chunks, V transposed),
 // the next slice's global loads issued before the current slice's math.
@@ -45,8 +45,7 @@ __device__ __forceinline__ int chunk_len(const int32_t* ctx_len, int batch, int 
   return max(slice, (c + slice - 1) / slice * slice);
 }
 
-// SL keys per LDS slice (64 for short chunks, 128 to keep more bytes in
-// flight on long ones).
+// SL keys per LDS slice (64: the only length the launcher takes).
 template <int D, int SL>
 struct Slice {
   static constexpr int DC = D / 8;  // 16-byte chunks per key row
@@ -134,10 +133,12 @@ void attn_kernel(const AttnParams p) {
   const int b = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
   if (p.status[b] != 0) return;
   const int Lk = p.ctx_len[b] + p.B;
-  const int chunk = chunk_len(p.ctx_len, p.batch, p.B, p.n_chunks, SL);
+  // the chunk bounds are the same in every lane: held in scalar registers,
+  // the slice loop below branches uniformly
+  const int chunk = __builtin_amdgcn_readfirstlane(chunk_len(p.ctx_len, p.batch, p.B, p.n_chunks, SL));
   const int k_start = c * chunk;
   if (k_start >= Lk) return;
-  const int k_end = (int)min((long long)Lk, (long long)k_start + chunk);
+  const int k_end = __builtin_amdgcn_readfirstlane((int)min((long long)Lk, (long long)k_start + chunk));
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, gq = lane >> 4;
@@ -374,9 +375,7 @@ hipError_t launch_ds(const AttnParams& p, hipStream_t st) {
   else if (qt <= 8)
     hipLaunchKernelGGL((attn_kernel<D, 2, SL>), grid, dim3(256), 0, st, p);
   else if (qt <= 16) {
-    // four query tiles per wave at D = 128 fit the registers with 64-key slices only
-    if constexpr (D == 128 && SL == 128) return hipErrorInvalidValue;
-    else hipLaunchKernelGGL((attn_kernel<D, 4, SL>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((attn_kernel<D, 4, SL>), grid, dim3(256), 0, st, p);
   } else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -384,7 +383,6 @@ hipError_t launch_ds(const AttnParams& p, hipStream_t st) {
 
 template <int D>
 hipError_t launch_d(const AttnParams& p, hipStream_t st) {
-  if (p.slice == 128) return launch_ds<D, 128>(p, st);
   if (p.slice == 64) return launch_ds<D, 64>(p, st);
   return hipErrorInvalidValue;
 }

@@ -89,7 +89,7 @@ struct AttnParams {
   int n_chunks;  // key chunks per (b, g) (grid x, <= 64); chunk length for the batch
                  // = max(slice, max_b(L_b) + B split n_chunks ways, rounded up to slice)
   int causal;    // 0: every block row sees all L_b + B keys; 1: block row j sees keys < L_b + j + 1
-  int slice;     // keys per LDS slice: 64 or 128
+  int slice;     // keys per LDS slice (64)
   int gb_pad;    // query rows per (b, g), padded to 16
   float scale_log2;
   float* pm;   // [batch][Hkv][n_chunks][gb_pad]

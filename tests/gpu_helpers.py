@@ -96,7 +96,7 @@ SHAPES = {
     "big-b19": synth.DraftConfig(name="big-b19", hidden=256, n_layers=2, n_q_heads=4, n_kv_heads=2,
                                  head_dim=64, intermediate=768, vocab=1040, n_tap=2, block=16,
                                  batch=19, ctx_len=0),
-    # long contexts: 128-key attention slices (chunks of >= 512 keys), G = 8, D = 64
+    # long contexts: chunks of many 64-key attention slices, G = 8, D = 64
     "long-d64": synth.DraftConfig(name="long-d64", hidden=512, n_layers=1, n_q_heads=64, n_kv_heads=8,
                                   head_dim=64, intermediate=512, vocab=1024, n_tap=2, block=16,
                                   batch=4, ctx_len=0),
