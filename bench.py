@@ -36,16 +36,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The sources the LM-head kernel compiles from; the PMC summary records their
+# hash, and a change to any of them voids its traffic figure.
+TRAFFIC_SOURCES = ("gemm_stream.hip", "internal.h", "common.h")
+
+
+def kernel_source_hash(root):
+    import hashlib
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(root, "block_diffusion_drafter_target_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes of the LM-head kernel from the committed rocprofv3 PMC summary,
-    or None when the kernel source changed since the counters were taken."""
-    import hashlib
+    or None when the kernel's sources changed since the counters were taken."""
     root = os.path.dirname(os.path.abspath(__file__))
-    src = os.path.join(root, "block_diffusion_drafter_target_amd", "csrc", "gemm_stream.hip")
     summary = os.path.join(root, "profiles", "lm_head_argmax_c2_pmc.txt")
     try:
         kv = dict(line.split(": ", 1) for line in open(summary).read().splitlines() if ": " in line)
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = kernel_source_hash(root)
     except OSError:
         return None
     if kv.get("kernel_source_sha256", "").strip() != sha:
