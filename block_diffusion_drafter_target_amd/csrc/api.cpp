@@ -11,6 +11,7 @@
 #include <new>
 #include <vector>
 
+#include "attn_split.h"
 #include "internal.h"
 
 struct dflash_model {
@@ -306,17 +307,24 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
 }
 
 struct AttnPlan {
-  int n_chunks, slice, gb_pad;
+  int n_chunks;  // key ranges per sequence at full length
+  int n_ranges;  // attention workgroups (chunks at most) per kv head
+  int slots;     // partial slots per kv head
+  int slice, gb_pad;
 };
 
 constexpr int kAttnTargetWGs = 512;  // attention workgroups when every sequence is at full length
 constexpr int kAttnMaxChunks = 32;   // per (sequence, kv head): 64 measured slower at batch 1
 
-// Key chunks per (sequence, kv head): about kAttnTargetWGs workgroups (one per
-// CU slot at two per CU) if every sequence were as long as the longest, without
-// chunks shorter than 64 keys of the cache. Measured on MI355X: 1024 and 2048
-// were slower at every configuration (more fp32 partials and workgroup starts
-// than the finer balance of a ragged batch wins back).
+// Attention chunks: about kAttnTargetWGs workgroups (one per CU slot at two
+// per CU) over the batch, n_chunks per sequence and kv head at full length,
+// without chunks shorter than 64 keys of the cache. The device picks one
+// chunk length for the batch from the real lengths so that all chunks fit the
+// n_chunks * batch workgroups per kv head: in a ragged batch the long
+// sequences take more chunks than the short ones and no workgroup holds more
+// keys than the chunk length (with equal lengths this is the per-sequence
+// split). Measured on MI355X: 768, 1024 and 2048 workgroups were slower at
+// every configuration.
 AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx, int B) {
   AttnPlan a;
   const int G = c.n_q_heads / c.n_kv_heads;
@@ -325,6 +333,8 @@ AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx, int B) {
   long long n = cdiv(kAttnTargetWGs, units);
   n = std::min<long long>(n, cdiv(max_ctx, 64));
   a.n_chunks = (int)std::max<long long>(1, std::min<long long>(n, kAttnMaxChunks));
+  a.n_ranges = a.n_chunks * batch;
+  a.slots = a.n_ranges;
   // 64-key slices at every shape: measured on MI355X against 128-key slices,
   // equal or faster everywhere (c4 303 -> 274 us, c3 466 -> 444, c5 538 ->
   // 530 per step), mostly because a chunk rounds up to whole slices and the
@@ -337,7 +347,7 @@ AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx, int B) {
 // of which reach the LM head (bytes, 256-aligned pieces): a draft block
 // (B = block, lm_rows = B - 1) or a target pass (B = n, lm_rows = n).
 struct StackWs {
-  size_t x, u, q, ao, s, ulm, keys, pm, pl, po, P, total;
+  size_t x, u, q, ao, s, ulm, keys, pm, pl, po, plan, P, total;
 };
 
 StackWs stack_ws(const dflash_config& c, int batch, int max_ctx, int B, int lm_rows) {
@@ -359,10 +369,11 @@ StackWs stack_ws(const dflash_config& c, int batch, int max_ctx, int B, int lm_r
   w.s = take(Mb * c.intermediate * 2);
   w.ulm = take(Ml * H * 2);
   w.keys = take((size_t)lm_tiles(c, (int)Ml) * Ml * 8);
-  const long long att_rows = (long long)batch * c.n_kv_heads * a.n_chunks * a.gb_pad;
+  const long long att_rows = (long long)c.n_kv_heads * a.slots * a.gb_pad;
   w.pm = take(att_rows * 4);
   w.pl = take(att_rows * 4);
   w.po = take(att_rows * c.head_dim * 4);
+  w.plan = take((size_t)dfl::attn_plan_ints(a.n_ranges, batch) * 4);
   size_t pf = 0;
   pf = std::max(pf, gemm_partial_floats((int)Mb, qkvw, H, 1));
   pf = std::max(pf, gemm_partial_floats((int)Mb, H, qw, 1));
@@ -723,6 +734,7 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
   float* pm = reinterpret_cast<float*>(base + w.pm);
   float* pl = reinterpret_cast<float*>(base + w.pl);
   float* po = reinterpret_cast<float*>(base + w.po);
+  int32_t* plan = reinterpret_cast<int32_t*>(base + w.plan);
   float* P = reinterpret_cast<float*>(base + w.P);
   const long long layer_kv = (long long)batch * Hkv * kv->max_ctx * D;
   const long long hid = (long long)Mb * H;
@@ -788,6 +800,11 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
     qp.q = q;
     qp.kc = static_cast<uint16_t*>(kv->k) + l * layer_kv;
     qp.vc = static_cast<uint16_t*>(kv->v) + l * layer_kv;
+    // the attention chunk split holds for the whole pass (lengths and statuses
+    // do not change in it): written once, by the first layer
+    qp.plan = l == 0 ? plan : nullptr;
+    qp.n_ranges = ap.n_ranges;
+    qp.slice = ap.slice;
     if ((e = dfl::launch_qkv_post(qp, st)) != hipSuccess) return DFLASH_ERR_HIP;
     // attention over [context ; block]
     dfl::AttnParams at;
@@ -802,7 +819,9 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
     at.Hkv = Hkv;
     at.B = B;
     at.max_ctx = kv->max_ctx;
-    at.n_chunks = ap.n_chunks;
+    at.n_ranges = ap.n_ranges;
+    at.slots = ap.slots;
+    at.plan = plan;
     at.slice = ap.slice;
     at.gb_pad = ap.gb_pad;
     at.causal = io.causal;
@@ -827,8 +846,10 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
     mp.Hkv = Hkv;
     mp.B = B;
     mp.D = D;
-    mp.n_chunks = ap.n_chunks;
-    mp.slice = ap.slice;
+    mp.n_ranges = ap.n_ranges;
+    mp.slots = ap.slots;
+    mp.seg_hint = ap.n_chunks;
+    mp.plan = plan;
     mp.gb_pad = ap.gb_pad;
     mp.out = ao;
     if ((e = dfl::launch_attn_merge(mp, st)) != hipSuccess) return DFLASH_ERR_HIP;

@@ -8,11 +8,14 @@
 // is bound by streaming K/V from HBM; MFMA keeps the arithmetic far below that
 // bound.
 //
-// Decomposition: workgroup (4 waves) = (b, g, key chunk). The chunk length is
-// one for the batch, sized on the device from the longest sequence's
-// L_b + B keys, so the work follows the real context rather than the cache
-// capacity and a ragged batch stays balanced; chunks past a sequence's end
-// exit at once. The chunk is walked in 64-key slices
+// Decomposition: workgroup (4 waves) = (chunk u, kv head g). Every sequence
+// is cut into chunks of one batch-wide length from its own first key, and
+// the chunks of all sequences are numbered in order (attn_split.h: the length
+// is picked from the real lengths so that a ragged batch gives its long
+// sequences more chunks and no workgroup more keys than the others); the
+// first layer's q/k/v pass writes that split once per pass and every layer
+// reads it. Workgroups past the last chunk exit at once. A chunk is walked
+// in 64-key slices
 // staged through LDS (K row-major with a 16-byte XOR swizzle over the row's
 // chunks, V transposed),
 // the next slice's global loads issued before the current slice's math.
@@ -22,28 +25,15 @@
 //                  accumulators, so each lane keeps one query's softmax state
 // Online softmax in base 2 (scale * log2 e folded in); row max and row sum
 // combine the four lanes that share a query with two xor shuffles. Each
-// workgroup writes (max, sum, unnormalised O) for its chunk; the merge kernel
-// combines chunks with the log-sum-exp rule.
+// workgroup writes (max, sum, unnormalised O) to its chunk's slot; the merge
+// kernel combines the chunks of a sequence with the log-sum-exp rule.
+#include "attn_split.h"
 #include "common.h"
 #include "internal.h"
 
 namespace dfl {
 
 namespace {
-
-// Keys per chunk: one length for the whole batch, the longest sequence's keys
-// split n_chunks ways and rounded up to whole slices. A shorter sequence uses
-// fewer chunks, so no workgroup holds more than one chunk of keys however
-// ragged the batch is.
-__device__ __forceinline__ int chunk_len(const int32_t* ctx_len, int batch, int B, int n_chunks, int slice) {
-  if (n_chunks == 1) return 0x7FFFFFFF;
-  int lmax = 0;
-  for (int i = threadIdx.x & 63; i < batch; i += 64) lmax = max(lmax, ctx_len[i]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lmax = max(lmax, __shfl_xor(lmax, o));
-  const int c = (max(lmax, 0) + B + n_chunks - 1) / n_chunks;
-  return max(slice, (c + slice - 1) / slice * slice);
-}
 
 // SL keys per LDS slice (64: the only length the launcher takes).
 template <int D, int SL>
@@ -130,176 +120,179 @@ void attn_kernel(const AttnParams p) {
   __shared__ __align__(16) u32x4 ks[SL * DC];
   __shared__ __align__(16) bf16_t vt[D * VT];
 
-  const int b = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
-  if (p.status[b] != 0) return;
-  const int Lk = p.ctx_len[b] + p.B;
-  // the chunk bounds are the same in every lane: held in scalar registers,
-  // the slice loop below branches uniformly
-  const int chunk = __builtin_amdgcn_readfirstlane(chunk_len(p.ctx_len, p.batch, p.B, p.n_chunks, SL));
-  const int k_start = c * chunk;
-  if (k_start >= Lk) return;
-  const int k_end = __builtin_amdgcn_readfirstlane((int)min((long long)Lk, (long long)k_start + chunk));
-
+  const int u = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, gq = lane >> 4;
   const int G = p.Hq / p.Hkv;
   const int GB = G * p.B;
   const int QT = p.gb_pad / 16;
+  // chunk u of the batch's split (read from the plan; uniform, so scalar)
+  const int b_u = p.plan[1 + u];
+  if (b_u < 0) return;
+  const int C = p.plan[0];
+  const int k0_u = p.plan[1 + p.n_ranges + u] * C;
+  const int Lk_u = p.ctx_len[b_u] + p.B;
 
-  // queries of this wave, as MFMA B operands (column = query, k = d); jrow
-  // is the block row of this lane's query column
-  u32x4 qreg[QPW][D / 32];
-  int jrow[QPW];
-#pragma unroll
-  for (int i = 0; i < QPW; ++i) {
-    const int qt = wave + 4 * i;
-    int rr = qt * 16 + r;
-    rr = rr < GB ? rr : GB - 1;
-    const int hl = rr / p.B, j = rr % p.B;
-    jrow[i] = j;
-    const bf16_t* qrow = p.q + ((long long)(b * p.B + j) * p.Hq + g * G + hl) * D + gq * 8;
-    // rows past GB read the last row (valid memory); padded tiles are zeroed
-    // by a select, not a guarded load
-    const uint32_t keep = qt < QT ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) qreg[i][ds] = *reinterpret_cast<const u32x4*>(qrow + ds * 32) & keep;
-  }
-
-  float mrun[QPW], lrun[QPW];
-  f32x4_t o[QPW][D / 16];
-#pragma unroll
-  for (int i = 0; i < QPW; ++i) {
-    mrun[i] = -__builtin_inff();
-    lrun[i] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[i][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const long long head_off = ((long long)b * p.Hkv + g) * p.max_ctx * D;
-  const bf16_t* kc = p.k + head_off;
-  const bf16_t* vc = p.v + head_off;
-
-  u32x4 kreg[KL], va[VL], vb[VL];
-
-  load_slice<D, SL>(kreg, va, vb, kc, vc, k_start, k_end);
-  for (int k0 = k_start; k0 < k_end; k0 += SL) {
-    store_slice<D, SL>(ks, vt, kreg, va, vb);
-    __syncthreads();
-    // prefetch the next slice (past the end it re-reads the last key: valid
-    // memory, never used)
-    load_slice<D, SL>(kreg, va, vb, kc, vc, k0 + SL, k_end);
-    constexpr int KT = SL / 16;  // 16-key tiles per slice
-    // S^T tiles of every query tile of the wave; each K fragment is read from
-    // LDS once and feeds all of them
-    f32x4_t sacc[QPW][KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int i = 0; i < QPW; ++i) sacc[i][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int key = kt * 16 + r;
-#pragma unroll
-      for (int ds = 0; ds < D / 32; ++ds) {
-        const u32x4 a = ks[key * DC + ((ds * 4 + gq) ^ (key & (DC - 1)))];
-#pragma unroll
-        for (int i = 0; i < QPW; ++i) sacc[i][kt] = mfma16x16x32(a, qreg[i][ds], sacc[i][kt]);
-      }
-    }
-    // keys past the end exist only in the chunk's last slice; in a causal
-    // block, row j also drops the block keys after its own position
-    const int lim0 = Lk - p.B + 1;  // key limit of block row 0
-    if (k0 + SL > k_end || (p.causal && k0 + SL > lim0)) {
-      int lim[QPW];
-#pragma unroll
-      for (int i = 0; i < QPW; ++i) lim[i] = p.causal ? min(k_end, lim0 + jrow[i]) : k_end;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = k0 + kt * 16 + 4 * gq + e;
-#pragma unroll
-          for (int i = 0; i < QPW; ++i)
-            if (key >= lim[i]) sacc[i][kt][e] = -__builtin_inff();
-        }
-    }
-    // online softmax on raw scores: the running max is kept in scaled base-2
-    // units, and max(s) * c == max(s * c) for the positive scale c
-    u32x4 pb[QPW][KT / 2];
+  // Chunk u: keys [k_start, k_end) of sequence b (Lk keys in all), its
+  // (max, sum, O) partials to slot u.
+  auto run_chunk = [&](int b, int Lk, int k_start, int k_end, int slot) __attribute__((always_inline)) {
+    // queries of this wave, as MFMA B operands (column = query, k = d); jrow
+    // is the block row of this lane's query column
+    u32x4 qreg[QPW][D / 32];
+    int jrow[QPW];
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
-      float mx = -__builtin_inff();
+      const int qt = wave + 4 * i;
+      int rr = qt * 16 + r;
+      rr = rr < GB ? rr : GB - 1;
+      const int hl = rr / p.B, j = rr % p.B;
+      jrow[i] = j;
+      const bf16_t* qrow = p.q + ((long long)(b * p.B + j) * p.Hq + g * G + hl) * D + gq * 8;
+      // rows past GB read the last row (valid memory); padded tiles are zeroed
+      // by a select, not a guarded load
+      const uint32_t keep = qt < QT ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[i][kt][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[i], mx * p.scale_log2);
-      // a causal row may have no visible key yet: weights against 0 are then
-      // exp2(-inf) = 0 instead of NaN
-      const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
-      const float alpha = fast_exp2(mrun[i] - mref);
-      float rs = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = fast_exp2(__builtin_fmaf(sacc[i][kt][e], p.scale_log2, -mref));
-          sacc[i][kt][e] = pv;
-          rs += pv;
-        }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      lrun[i] = lrun[i] * alpha + rs;
-      mrun[i] = mnew;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o[i][dt] *= alpha;
-      // P^T as the B operand: keys 32h + 4gq.. and 32h + 16 + 4gq.. of lane
-      // group gq, the same key order as the V^T operand below
-#pragma unroll
-      for (int h = 0; h < KT / 2; ++h)
-        pb[i][h] = u32x4{pack_bf2(sacc[i][2 * h][0], sacc[i][2 * h][1]),
-                         pack_bf2(sacc[i][2 * h][2], sacc[i][2 * h][3]),
-                         pack_bf2(sacc[i][2 * h + 1][0], sacc[i][2 * h + 1][1]),
-                         pack_bf2(sacc[i][2 * h + 1][2], sacc[i][2 * h + 1][3])};
+      for (int ds = 0; ds < D / 32; ++ds) qreg[i][ds] = *reinterpret_cast<const u32x4*>(qrow + ds * 32) & keep;
     }
-    // O^T += V^T P^T; each V^T fragment is read once for all query tiles
-#pragma unroll
-    for (int h = 0; h < KT / 2; ++h) {
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const bf16_t* row = vt + (dt * 16 + r) * VT + 32 * h + 4 * gq;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
-        const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-        for (int i = 0; i < QPW; ++i) o[i][dt] = mfma16x16x32(a, pb[i][h], o[i][dt]);
-      }
-    }
-    __syncthreads();
-  }
 
-  const long long base = (((long long)b * p.Hkv + g) * p.n_chunks + c) * p.gb_pad;
+    float mrun[QPW], lrun[QPW];
+    f32x4_t o[QPW][D / 16];
 #pragma unroll
-  for (int i = 0; i < QPW; ++i) {
-    const int qt = wave + 4 * i;
-    if (qt >= QT) continue;
-    const int rr = qt * 16 + r;
-    if (gq == 0) {
-      p.pm[base + rr] = mrun[i];
-      p.pl[base + rr] = lrun[i];
+    for (int i = 0; i < QPW; ++i) {
+      mrun[i] = -__builtin_inff();
+      lrun[i] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[i][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+
+    const long long head_off = ((long long)b * p.Hkv + g) * p.max_ctx * D;
+    const bf16_t* kc = p.k + head_off;
+    const bf16_t* vc = p.v + head_off;
+
+    u32x4 kreg[KL], va[VL], vb[VL];
+
+    load_slice<D, SL>(kreg, va, vb, kc, vc, k_start, k_end);
+    for (int k0 = k_start; k0 < k_end; k0 += SL) {
+      store_slice<D, SL>(ks, vt, kreg, va, vb);
+      __syncthreads();
+      // prefetch the next slice (past the end it re-reads the last key: valid
+      // memory, never used)
+      load_slice<D, SL>(kreg, va, vb, kc, vc, k0 + SL, k_end);
+      constexpr int KT = SL / 16;  // 16-key tiles per slice
+      // S^T tiles of every query tile of the wave; each K fragment is read from
+      // LDS once and feeds all of them
+      f32x4_t sacc[QPW][KT];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      *reinterpret_cast<f32x4_t*>(p.po + (base + rr) * D + dt * 16 + 4 * gq) = o[i][dt];
-  }
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int i = 0; i < QPW; ++i) sacc[i][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int key = kt * 16 + r;
+#pragma unroll
+        for (int ds = 0; ds < D / 32; ++ds) {
+          const u32x4 a = ks[key * DC + ((ds * 4 + gq) ^ (key & (DC - 1)))];
+#pragma unroll
+          for (int i = 0; i < QPW; ++i) sacc[i][kt] = mfma16x16x32(a, qreg[i][ds], sacc[i][kt]);
+        }
+      }
+      // keys past the end exist only in the chunk's last slice; in a causal
+      // block, row j also drops the block keys after its own position
+      const int lim0 = Lk - p.B + 1;  // key limit of block row 0
+      if (k0 + SL > k_end || (p.causal && k0 + SL > lim0)) {
+        int lim[QPW];
+#pragma unroll
+        for (int i = 0; i < QPW; ++i) lim[i] = p.causal ? min(k_end, lim0 + jrow[i]) : k_end;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = k0 + kt * 16 + 4 * gq + e;
+#pragma unroll
+            for (int i = 0; i < QPW; ++i)
+              if (key >= lim[i]) sacc[i][kt][e] = -__builtin_inff();
+          }
+      }
+      // online softmax on raw scores: the running max is kept in scaled base-2
+      // units, and max(s) * c == max(s * c) for the positive scale c
+      u32x4 pb[QPW][KT / 2];
+#pragma unroll
+      for (int i = 0; i < QPW; ++i) {
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[i][kt][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(mrun[i], mx * p.scale_log2);
+        // a causal row may have no visible key yet: weights against 0 are then
+        // exp2(-inf) = 0 instead of NaN
+        const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
+        const float alpha = fast_exp2(mrun[i] - mref);
+        float rs = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pv = fast_exp2(__builtin_fmaf(sacc[i][kt][e], p.scale_log2, -mref));
+            sacc[i][kt][e] = pv;
+            rs += pv;
+          }
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
+        lrun[i] = lrun[i] * alpha + rs;
+        mrun[i] = mnew;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[i][dt] *= alpha;
+        // P^T as the B operand: keys 32h + 4gq.. and 32h + 16 + 4gq.. of lane
+        // group gq, the same key order as the V^T operand below
+#pragma unroll
+        for (int h = 0; h < KT / 2; ++h)
+          pb[i][h] = u32x4{pack_bf2(sacc[i][2 * h][0], sacc[i][2 * h][1]),
+                           pack_bf2(sacc[i][2 * h][2], sacc[i][2 * h][3]),
+                           pack_bf2(sacc[i][2 * h + 1][0], sacc[i][2 * h + 1][1]),
+                           pack_bf2(sacc[i][2 * h + 1][2], sacc[i][2 * h + 1][3])};
+      }
+      // O^T += V^T P^T; each V^T fragment is read once for all query tiles
+#pragma unroll
+      for (int h = 0; h < KT / 2; ++h) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const bf16_t* row = vt + (dt * 16 + r) * VT + 32 * h + 4 * gq;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
+          const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int i = 0; i < QPW; ++i) o[i][dt] = mfma16x16x32(a, pb[i][h], o[i][dt]);
+        }
+      }
+      __syncthreads();
+    }
+
+    const long long base = ((long long)g * p.slots + slot) * p.gb_pad;
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int qt = wave + 4 * i;
+      if (qt >= QT) continue;
+      const int rr = qt * 16 + r;
+      if (gq == 0) {
+        p.pm[base + rr] = mrun[i];
+        p.pl[base + rr] = lrun[i];
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        *reinterpret_cast<f32x4_t*>(p.po + (base + rr) * D + dt * 16 + 4 * gq) = o[i][dt];
+    }
+  };
+
+  run_chunk(b_u, Lk_u, k0_u, min(Lk_u, k0_u + C), u);
 }
 
-// o[m][h] = sum_c exp2(m_c - M) O_c / sum_c exp2(m_c - M) l_c over the chunks
-// that hold keys of the sequence. One wave per (row, head); lane c holds
-// chunk c's statistics, lane d output elements d and d + 64. The statistics
-// and the first NB chunks' partial outputs are loaded in one round trip (NB
-// covers the plan's chunk count up to 32); the weights are applied once the
-// wave's maximum is known.
+// o[m][h] = sum_c exp2(m_c - M) O_c / sum_c exp2(m_c - M) l_c over the
+// chunks of the sequence. One wave per (row, head); lane c holds chunk c's
+// statistics, lane d output elements d and d + 64. The statistics and the
+// first NB chunks' partial outputs are loaded in one round trip (NB covers
+// the typical chunk count up to 32; more take further rounds); the weights
+// are applied once the wave's maximum is known.
 template <int NB>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   constexpr int kMergeBatch = NB;
@@ -312,10 +305,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const int st = p.status[b];
   const int G = p.Hq / p.Hkv;
   const int g = h / G, rr = (h % G) * p.B + j;
-  const int Lk = p.ctx_len[b] + p.B;
-  const int cl = chunk_len(p.ctx_len, p.batch, p.B, p.n_chunks, p.slice);
-  const int nch = max(0, min(p.n_chunks, (int)(((long long)Lk + cl - 1) / cl)));
-  const long long base = ((long long)b * p.Hkv + g) * p.n_chunks;
+  // the sequence's chunks: nch consecutive slots from its first (none for a
+  // sequence with an error status; at most 64 by the chunk length's bound)
+  const int32_t* first = p.plan + 1 + 2 * p.n_ranges;
+  const int s0 = first[b], nch = first[p.batch + b];
+  // (a sequence without chunks may have s0 == slots: its loads, never used,
+  // stay in the buffer)
+  const long long base = (long long)g * p.slots + min(s0, p.slots - 1);
   const bool two = p.D > 64;
   // Loads are unconditional at clamped chunk indexes: a guarded load becomes a
   // branch, and the compiler waits for every outstanding load where branches
@@ -368,7 +364,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 
 template <int D, int SL>
 hipError_t launch_ds(const AttnParams& p, hipStream_t st) {
-  dim3 grid(p.n_chunks, p.Hkv, p.batch);
+  dim3 grid(p.n_ranges, p.Hkv);
   const int qt = p.gb_pad / 16;
   if (qt <= 4)
     hipLaunchKernelGGL((attn_kernel<D, 1, SL>), grid, dim3(256), 0, st, p);
@@ -390,20 +386,20 @@ hipError_t launch_d(const AttnParams& p, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, int D, hipStream_t st) {
-  if (p.n_chunks < 1 || p.n_chunks > 64) return hipErrorInvalidValue;
+  if (p.n_ranges < p.batch || p.batch < 1 || p.slots < p.n_ranges) return hipErrorInvalidValue;
   if (D == 128) return launch_d<128>(p, st);
   if (D == 64) return launch_d<64>(p, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t st) {
-  if (p.n_chunks < 1 || p.n_chunks > 64) return hipErrorInvalidValue;
+  if (p.n_ranges < p.batch || p.batch < 1 || p.slots < p.n_ranges) return hipErrorInvalidValue;
   const dim3 grid((p.Hq + 3) / 4, p.batch * p.B);
-  if (p.n_chunks <= 4)
+  if (p.seg_hint <= 4)
     hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(256), 0, st, p);
-  else if (p.n_chunks <= 8)
+  else if (p.seg_hint <= 8)
     hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(256), 0, st, p);
-  else if (p.n_chunks <= 16)
+  else if (p.seg_hint <= 16)
     hipLaunchKernelGGL(merge_kernel<16>, grid, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL(merge_kernel<32>, grid, dim3(256), 0, st, p);

@@ -86,15 +86,16 @@ struct AttnParams {
   const int32_t* ctx_len;
   const int32_t* status;
   int batch, Hq, Hkv, B, max_ctx;
-  int n_chunks;  // key chunks per (b, g) (grid x, <= 64); chunk length for the batch
-                 // = max(slice, max_b(L_b) + B split n_chunks ways, rounded up to slice)
+  int n_ranges;  // chunk workgroups per kv head (grid x, >= batch)
+  int slots;     // partial slots per kv head (>= n_ranges; slot = chunk number)
+  const int32_t* plan;  // the batch's chunk split (attn_split.h), written earlier in the pass
   int causal;    // 0: every block row sees all L_b + B keys; 1: block row j sees keys < L_b + j + 1
   int slice;     // keys per LDS slice (64)
   int gb_pad;    // query rows per (b, g), padded to 16
   float scale_log2;
-  float* pm;   // [batch][Hkv][n_chunks][gb_pad]
+  float* pm;   // [Hkv][slots][gb_pad]
   float* pl;
-  float* po;   // [batch][Hkv][n_chunks][gb_pad][D]
+  float* po;   // [Hkv][slots][gb_pad][D]
 };
 
 hipError_t launch_attention(const AttnParams& p, int D, hipStream_t st);
@@ -105,7 +106,9 @@ struct MergeParams {
   const float* po;
   const int32_t* ctx_len;
   const int32_t* status;
-  int batch, Hq, Hkv, B, D, n_chunks, slice, gb_pad;
+  int batch, Hq, Hkv, B, D, n_ranges, slots, gb_pad;
+  int seg_hint;   // typical chunks per sequence (picks how many partials one load batch reads)
+  const int32_t* plan;  // the batch's chunk split (attn_split.h)
   uint16_t* out;  // [batch*B, Hq*D]
 };
 
@@ -164,6 +167,8 @@ struct QkvPostParams {
   uint16_t* q;        // [rows, Hq, D]
   uint16_t* kc;       // layer base [batch][Hkv][max_ctx][D]
   uint16_t* vc;
+  int32_t* plan;      // if not NULL, one more workgroup writes the attention chunk split
+  int n_ranges, slice;  // of the batch (attn_split.h) with n_ranges chunks per kv head
 };
 
 hipError_t launch_qkv_post(const QkvPostParams& p, hipStream_t st);

@@ -7,6 +7,7 @@
 // All are bound by a few kilobytes per row; they exist to keep every fp32
 // statistic (RMSNorm sums, residual stream, RoPE) on the device between the
 // bf16 MFMA GEMMs.
+#include "attn_split.h"
 #include "common.h"
 #include "internal.h"
 
@@ -255,6 +256,13 @@ __device__ __forceinline__ void sum_pair(const float* src, long long s_stride, i
 __global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = blockIdx.y;
+  // the extra row of workgroups: the first one's first wave writes the
+  // attention chunk split (the embedding pass has set every status)
+  if (m == p.batch * p.B) {
+    if (blockIdx.x == 0 && wave == 0)
+      attn_plan_wave(p.ctx_len, p.status, p.batch, p.B, p.n_ranges, p.slice, p.plan);
+    return;
+  }
   const int head = blockIdx.x * 4 + wave;
   const int nh = p.Hq + 2 * p.Hkv;
   if (head >= nh) return;
@@ -486,7 +494,8 @@ hipError_t launch_row_norm(const RowNormParams& p, hipStream_t st) {
 
 hipError_t launch_qkv_post(const QkvPostParams& p, hipStream_t st) {
   const int nh = p.Hq + 2 * p.Hkv;
-  hipLaunchKernelGGL(qkv_post_kernel, dim3((nh + 3) / 4, p.batch * p.B), dim3(256), 0, st, p);
+  if (p.plan && (p.n_ranges < p.batch || p.slice < 1)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qkv_post_kernel, dim3((nh + 3) / 4, p.batch * p.B + (p.plan ? 1 : 0)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -104,10 +104,18 @@ SHAPES = {
     "long-d128": synth.DraftConfig(name="long-d128", hidden=512, n_layers=1, n_q_heads=16, n_kv_heads=4,
                                    head_dim=128, intermediate=512, vocab=1024, n_tap=2, block=16,
                                    batch=4, ctx_len=0),
+    # one long sequence among many short ones, one kv head: the attention
+    # chunk length is set by the 64-chunks-per-sequence bound (the batch's
+    # average alone would cut the long sequence into 94 chunks), so it gets
+    # 47 chunks over two merge load rounds
+    "ragged-1long": synth.DraftConfig(name="ragged-1long", hidden=256, n_layers=1, n_q_heads=4, n_kv_heads=1,
+                                      head_dim=64, intermediate=512, vocab=1024, n_tap=2, block=16,
+                                      batch=24, ctx_len=0),
 }
 
 CTX = {"gqa-d128": [1, 300, 777, 0, 64], "g8-d64": [500, 33], "b12": [129, 0, 64],
        "tiled-b9": [17, 260, 0, 64, 1, 333, 90, 128, 2],
        "long-d64": [8900, 8500, 8193, 100], "long-d128": [16900, 16000, 9000, 3],
        "mlp-wide": [40, 0, 17, 300, 64, 1, 129, 90, 33, 7], "mlp-wide-b2": [70, 250],
-       "big-b19": [0, 1, 17, 64, 129, 260, 300, 33, 90, 5, 200, 150, 75, 12, 280, 45, 100, 3, 64]}
+       "big-b19": [0, 1, 17, 64, 129, 260, 300, 33, 90, 5, 200, 150, 75, 12, 280, 45, 100, 3, 64],
+       "ragged-1long": [6000, 0, 1, 5, 17, 3, 64, 2, 0, 9, 33, 1, 7, 0, 12, 4, 65, 1, 2, 8, 0, 3, 1, 6]}
