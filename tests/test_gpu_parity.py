@@ -179,6 +179,39 @@ def test_draft_block_capacity_status(gpu_lib):
     gh.check_tokens(d[:2], logits[:2], r["logits"], what="tokens beside a failed sequence")
 
 
+def test_draft_block_batch_over_64(gpu_lib):
+    """70 sequences: the attention chunk split walks two groups of 64 sequences
+    (chunk counts and first slots carried from the first group to the second),
+    ragged and empty contexts, and a last sequence past its cache capacity
+    (no chunks, draft -1, the others unaffected); 560 block rows take the
+    large-tile GEMMs."""
+    torch = _torch()
+    cfg = synth.DraftConfig(name="batch70", hidden=256, n_layers=1, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                            intermediate=512, vocab=512, n_tap=2, block=8, batch=70, ctx_len=0)
+    gh.log("[draft_block] batch of 70")
+    g = np.random.Generator(np.random.PCG64(70))
+    lens = [int(x) for x in g.integers(0, 301, size=cfg.batch)]
+    lens[3] = lens[64] = 0
+    lens[65] = 300
+    W, WO, ocfg, dr, cache, taps = make_case(cfg, lens)
+    bad = cfg.batch - 1
+    dr.ctx_len[bad] = dr.max_ctx - cfg.block + 1  # one slot past the cache
+    anchor = synth.make_anchors(cfg)
+    dr.anchor.copy_(torch.from_numpy(anchor))
+    B, V = cfg.block, cfg.vocab
+    lg = torch.empty((cfg.batch * (B - 1), V), dtype=torch.float32, device="cuda")
+    dr.draft_block(dbg_logits=lg)
+    torch.cuda.synchronize()
+    assert dr.status.cpu().tolist() == [0] * bad + [-5]
+    d = dr.draft.cpu().numpy()
+    assert (d[bad] == -1).all()
+    r = ref.draft_block(ocfg, WO, cache, lens[:bad], anchor[:bad])
+    logits = lg.cpu().numpy().astype(np.float64).reshape(cfg.batch, B - 1, V)
+    gh.check_rel(logits[:bad], r["logits"], what="logits of 69 sequences")
+    band = gh.check_tokens(d[:bad], logits[:bad], r["logits"], what="tokens of 69 sequences")
+    gh.log(f"    tie-band rows {band}/{d[:bad].size}")
+
+
 def test_dead_slots_do_not_leak(gpu_lib):
     """Rollback by construction: NaN in every slot >= ctx_len changes nothing."""
     torch = _torch()
