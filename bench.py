@@ -273,7 +273,7 @@ def main():
                     help="also time the same steps captured in one HIP graph")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "bench.py measures one GPU; runs on several GPUs are not implemented",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

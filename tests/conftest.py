@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The HIP library and a visible device, or a loud failure on a GPU machine."""
+    """The HIP library and a visible device, or a loud failure where a device is visible."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
