@@ -179,6 +179,43 @@ def test_draft_block_capacity_status(gpu_lib):
     gh.check_tokens(d[:2], logits[:2], r["logits"], what="tokens beside a failed sequence")
 
 
+@pytest.mark.parametrize("B", [2, 3, 5])
+def test_small_blocks_draft_and_verify(gpu_lib, B):
+    """Blocks of 2 (one drafted token), 3 and 5: G*B = 8, 12 and 20 query rows
+    per kv head (padded query tiles), LM heads of 1, 2 and 4 rows per sequence;
+    the draft block end to end against the oracle, then verify bit exact."""
+    torch = _torch()
+    cfg = synth.DraftConfig(name=f"small-b{B}", hidden=256, n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                            intermediate=512, vocab=640, n_tap=2, block=B, batch=3, ctx_len=0)
+    gh.log(f"[draft_block] block {B}")
+    lens = [0, 70, 5]
+    W, WO, ocfg, dr, cache, taps = make_case(cfg, lens)
+    anchor = synth.make_anchors(cfg)
+    dr.anchor.copy_(torch.from_numpy(anchor))
+    V = cfg.vocab
+    lg = torch.empty((cfg.batch * (B - 1), V), dtype=torch.float32, device="cuda")
+    dr.draft_block(dbg_logits=lg)
+    torch.cuda.synchronize()
+    assert dr.status.cpu().tolist() == [0] * cfg.batch
+    d = dr.draft.cpu().numpy()
+    logits = lg.cpu().numpy().astype(np.float64).reshape(cfg.batch, B - 1, V)
+    r = ref.draft_block(ocfg, WO, cache, lens, anchor)
+    gh.check_rel(logits, r["logits"], what=f"logits, block {B}")
+    gh.check_tokens(d, logits, r["logits"], what=f"tokens, block {B}")
+    for step in range(4):
+        m = synth.geometric_accept(cfg.batch, B, 0.8, step=step)
+        tgt = synth.synth_target_tokens(d, m, V, step=step)
+        dr.verify_accept(torch.from_numpy(tgt).cuda())
+        torch.cuda.synchronize()
+        rv = ref.verify_accept(d, tgt, lens)
+        assert dr.accept_len.cpu().numpy().tolist() == rv["accept_len"].tolist() == m.tolist()
+        assert np.array_equal(dr.emitted.cpu().numpy(), rv["emitted"])
+        assert np.array_equal(dr.n_emit.cpu().numpy(), rv["n_emit"])
+        assert np.array_equal(dr.anchor_out.cpu().numpy(), rv["anchor_out"])
+        n = int(dr.n_commit.item())
+        assert np.array_equal(dr.commit_rows.cpu().numpy()[:n], rv["commit_rows"])
+
+
 def test_draft_block_batch_over_64(gpu_lib):
     """70 sequences: the attention chunk split walks two groups of 64 sequences
     (chunk counts and first slots carried from the first group to the second),
