@@ -216,8 +216,9 @@ def target_verify(cfg, W, lens, args, dr):
     return res
 
 
-def cpu_baseline(cfg, W, L, repeats: int):
-    """The fp64 oracle's draft step on the host cores (median of repeats)."""
+def cpu_baseline(cfg, W, L, repeats: int, seconds: float):
+    """The fp64 oracle's draft step on the host cores: steps repeated until at
+    least `repeats` of them and `seconds` of timed work have run; the median."""
     from threadpoolctl import threadpool_info
 
     from block_diffusion_drafter_target_amd import synth
@@ -234,7 +235,8 @@ def cpu_baseline(cfg, W, L, repeats: int):
     taps = synth.bf16_to_f64(synth.make_taps(cfg, batch * B, tid=999))
     anchor = synth.make_anchors(cfg)
     times = []
-    for _ in range(repeats):
+    t_all = time.perf_counter()
+    while len(times) < repeats or (time.perf_counter() - t_all < seconds and len(times) < 10000):
         t = time.perf_counter()
         ctx = ref.fuse_ctx(ocfg, WO, taps)
         ref.inject_kv(ocfg, WO, ctx, [(b * B + i, b, L - B + i) for b in range(batch) for i in range(B)], cache)
@@ -248,8 +250,9 @@ def cpu_baseline(cfg, W, L, repeats: int):
     return {"value": batch * (B - 1) / t_step, "unit": "drafted tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": (f"one full draft step (fuse+inject of {batch * B} rows, {cfg.n_layers} layers at "
-                       f"context {L}, full LM head, verify) in fp64 numpy, median of {repeats}; "
-                       f"step {t_step * 1e3:.0f} ms; weight upcast to fp64 ({prep:.1f} s) not timed"),
+                       f"context {L}, full LM head, verify) in fp64 numpy, median of {len(times)} steps "
+                       f"({sum(times):.1f} s of timed work); step {t_step * 1e3:.0f} ms; weight upcast to "
+                       f"fp64 ({prep:.1f} s) not timed"),
             "ms_per_step": t_step * 1e3}
 
 
@@ -261,7 +264,9 @@ def main():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--block", type=int, default=0, help="override the block size")
     ap.add_argument("--batch", type=int, default=0, help="override the batch")
-    ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--cpu-repeats", type=int, default=3, help="fewest oracle steps of the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="least timed work of the CPU baseline (seconds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--target-verify", action="store_true",
                     help="also time the target's causal verify pass (Qwen3-8B-shaped 36-layer target)")
@@ -467,7 +472,7 @@ def main():
     del dr
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
-        out["cpu_baseline"] = cpu_baseline(cfg, W, int(lens.max()), args.cpu_repeats)
+        out["cpu_baseline"] = cpu_baseline(cfg, W, int(lens.max()), args.cpu_repeats, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
