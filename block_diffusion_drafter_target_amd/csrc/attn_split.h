@@ -24,8 +24,6 @@ namespace dfl {
 
 inline long long attn_plan_ints(int n_ranges, int batch) { return 1 + 2ll * n_ranges + 2ll * batch; }
 
-#if defined(__HIPCC__)
-
 // Inclusive prefix sum over the 64 lanes of a wave.
 template <typename T>
 __device__ __forceinline__ T split_wave_scan(T v) {
@@ -125,7 +123,5 @@ __device__ __forceinline__ void attn_plan_wave(const int32_t* ctx_len, const int
   }
   for (int u = total + lane; u < n_ranges; u += 64) seq_of[u] = -1;
 }
-
-#endif  // __HIPCC__
 
 }  // namespace dfl
