@@ -123,6 +123,14 @@ void attn_kernel(const AttnParams p) {
   // measured 1-2% slower there, and 12% slower for chunks of one slice)
   constexpr bool kPipe = D == 64;
   constexpr int NBUF = kPipe ? 2 : 1;
+  // With the pipeline the softmax VALU work also counts (measured 546 -> 530
+  // us per step): the softmax reference moves only when a score exceeds it by
+  // more than 2^8 (a wave-uniform branch, so the rescale of O is skipped on
+  // almost every slice; weights stay <= 256, exact in fp32 and in the bf16
+  // operand), and the row sums come out of the matrix cores as one more O^T
+  // tile against an all-ones operand. Not with four query tiles per wave
+  // (the extra accumulators would spill).
+  constexpr bool kLean = kPipe && QPW <= 2;
   __shared__ __align__(16) u32x4 ks[NBUF][SL * DC];
   __shared__ __align__(16) bf16_t vt[NBUF][D * VT];
 
@@ -161,15 +169,21 @@ void attn_kernel(const AttnParams p) {
       for (int ds = 0; ds < D / 32; ++ds) qreg[i][ds] = *reinterpret_cast<const u32x4*>(qrow + ds * 32) & keep;
     }
 
+    // mrun: the lane's softmax reference (scaled base-2 units); o and the row
+    // sums (lrun, or lsum: an O^T tile of the all-ones operand whose every
+    // element is the row sum of the bf16 probabilities) hold sums of
+    // exp2(s * c - mrun)
     float mrun[QPW], lrun[QPW];
-    f32x4_t o[QPW][D / 16];
+    f32x4_t o[QPW][D / 16], lsum[QPW];
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       mrun[i] = -__builtin_inff();
       lrun[i] = 0.f;
+      lsum[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) o[i][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
     const long long head_off = ((long long)b * p.Hkv + g) * p.max_ctx * D;
     const bf16_t* kc = p.k + head_off;
@@ -227,26 +241,35 @@ void attn_kernel(const AttnParams p) {
           for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[i][kt][e]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrun[i], mx * p.scale_log2);
+        const float mc = mx * p.scale_log2;
+        if (!kLean || __builtin_amdgcn_ballot_w64(mc > mrun[i] + 8.f) != 0) {
+          const float mnew = fmaxf(mrun[i], mc);
+          const float alpha = mnew == -__builtin_inff() ? 1.f : fast_exp2(mrun[i] - mnew);
+          mrun[i] = mnew;
+          if constexpr (kLean)
+            lsum[i] *= alpha;
+          else
+            lrun[i] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) o[i][dt] *= alpha;
+        }
         // a causal row may have no visible key yet: weights against 0 are then
         // exp2(-inf) = 0 instead of NaN
-        const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
-        const float alpha = fast_exp2(mrun[i] - mref);
-        float rs = 0.f;
+        const float mref = mrun[i] == -__builtin_inff() ? 0.f : mrun[i];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float pv = fast_exp2(__builtin_fmaf(sacc[i][kt][e], p.scale_log2, -mref));
-            sacc[i][kt][e] = pv;
-            rs += pv;
-          }
-        rs += __shfl_xor(rs, 16);
-        rs += __shfl_xor(rs, 32);
-        lrun[i] = lrun[i] * alpha + rs;
-        mrun[i] = mnew;
+          for (int e = 0; e < 4; ++e) sacc[i][kt][e] = fast_exp2(__builtin_fmaf(sacc[i][kt][e], p.scale_log2, -mref));
+        if constexpr (!kLean) {
+          float rs = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[i][dt] *= alpha;
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rs += sacc[i][kt][e];
+          rs += __shfl_xor(rs, 16);
+          rs += __shfl_xor(rs, 32);
+          lrun[i] += rs;
+        }
         // P^T as the B operand: keys 32h + 4gq.. and 32h + 16 + 4gq.. of lane
         // group gq, the same key order as the V^T operand below
 #pragma unroll
@@ -267,6 +290,10 @@ void attn_kernel(const AttnParams p) {
           const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
           for (int i = 0; i < QPW; ++i) o[i][dt] = mfma16x16x32(a, pb[i][h], o[i][dt]);
+        }
+        if constexpr (kLean) {
+#pragma unroll
+          for (int i = 0; i < QPW; ++i) lsum[i] = mfma16x16x32(ones, pb[i][h], lsum[i]);
         }
       }
     };
@@ -325,7 +352,7 @@ void attn_kernel(const AttnParams p) {
       const int rr = qt * 16 + r;
       if (gq == 0) {
         p.pm[base + rr] = mrun[i];
-        p.pl[base + rr] = lrun[i];
+        p.pl[base + rr] = kLean ? lsum[i][0] : lrun[i];
       }
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt)
