@@ -359,14 +359,20 @@ def main():
     assert int(dr.status.abs().max()) == 0, "a sequence ran out of cache"
     after_warmup = {k: getattr(dr, k).clone() for k in ("ctx_len", "anchor_out", "commit_rows", "n_commit")}
     bd.dflash_profile_enable(["lm_head"])
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event at every step boundary: the mean over the K steps and the
+    # spread of single steps (median, p10, p90)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    start, stop = evs[0], evs[-1]
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
         step(targets[1 + args.warmup + i])
-    stop.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
+    per_step = np.array([1e3 * evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    spread = {"p10": round(float(np.percentile(per_step, 10)), 1), "median": round(float(np.median(per_step)), 1),
+              "p90": round(float(np.percentile(per_step, 90)), 1)}
     lm_ms, lm_n = bd.dflash_profile_read("lm_head")
     bd.dflash_profile_enable([])
     ctx_after = dr.ctx_len.cpu().numpy()
@@ -448,6 +454,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "latency_us": round(ms * 1e3, 1),
+        "latency_us_spread": spread,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": (f"{cfg.name} drafter: H {H}, {cfg.n_q_heads}/{cfg.n_kv_heads} heads of "
