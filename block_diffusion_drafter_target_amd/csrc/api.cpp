@@ -798,6 +798,7 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
     qp.max_ctx = kv->max_ctx;
     qp.eps = c.rms_eps;
     qp.q = q;
+    qp.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
     qp.kc = static_cast<uint16_t*>(kv->k) + l * layer_kv;
     qp.vc = static_cast<uint16_t*>(kv->v) + l * layer_kv;
     // the attention chunk split holds for the whole pass (lengths and statuses
@@ -825,7 +826,6 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
     at.slice = ap.slice;
     at.gb_pad = ap.gb_pad;
     at.causal = io.causal;
-    at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
     at.pm = pm;
     at.pl = pl;
     at.po = po;

@@ -184,6 +184,11 @@ void attn_kernel(const AttnParams p) {
       for (int dt = 0; dt < D / 16; ++dt) o[i][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    // lean path: the score MFMAs start from -mref (mref = mrun, or 0 before
+    // the first visible key), so their results are already s * c - mref
+    f32x4_t cref[QPW];
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) cref[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const long long head_off = ((long long)b * p.Hkv + g) * p.max_ctx * D;
     const bf16_t* kc = p.k + head_off;
@@ -197,14 +202,15 @@ void attn_kernel(const AttnParams p) {
     auto scores = [&](int bi, f32x4_t(&sacc)[QPW][KT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int i = 0; i < QPW; ++i) sacc[i][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         const int key = kt * 16 + r;
 #pragma unroll
         for (int ds = 0; ds < D / 32; ++ds) {
           const u32x4 a = ks[bi][key * DC + ((ds * 4 + gq) ^ (key & (DC - 1)))];
 #pragma unroll
-          for (int i = 0; i < QPW; ++i) sacc[i][kt] = mfma16x16x32(a, qreg[i][ds], sacc[i][kt]);
+          for (int i = 0; i < QPW; ++i) {
+            const f32x4_t c0 = kLean ? cref[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            sacc[i][kt] = mfma16x16x32(a, qreg[i][ds], ds == 0 ? c0 : sacc[i][kt]);
+          }
         }
       }
     };
@@ -227,10 +233,12 @@ void attn_kernel(const AttnParams p) {
           }
       }
     };
-    // online softmax of one slice's scores (the running max kept in scaled
-    // base-2 units: max(s) * c == max(s * c) for the positive scale c), then
-    // O^T += V^T P^T from the V slice in buffer bi
-    auto accumulate = [&](int bi, f32x4_t(&sacc)[QPW][KT]) __attribute__((always_inline)) {
+    // online softmax of one slice's scores (s * c, the running max in the same
+    // scaled base-2 units), then O^T += V^T P^T from the V slice in buffer bi.
+    // The lean path's scores arrive relative to the reference (s * c - mref):
+    // when the reference moves by delta, this slice's scores and the next
+    // slice's (nxt: already issued against the old reference) drop by delta.
+    auto accumulate = [&](int bi, f32x4_t(&sacc)[QPW][KT], f32x4_t(&nxt)[QPW][KT]) __attribute__((always_inline)) {
       u32x4 pb[QPW][KT / 2];
 #pragma unroll
       for (int i = 0; i < QPW; ++i) {
@@ -241,25 +249,46 @@ void attn_kernel(const AttnParams p) {
           for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[i][kt][e]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mc = mx * p.scale_log2;
-        if (!kLean || __builtin_amdgcn_ballot_w64(mc > mrun[i] + 8.f) != 0) {
-          const float mnew = fmaxf(mrun[i], mc);
+        // a causal row may have no visible key yet: its reference is then 0,
+        // and its weights exp2(-inf) = 0 instead of NaN
+        if constexpr (kLean) {
+          const float mref = mrun[i] == -__builtin_inff() ? 0.f : mrun[i];
+          const float thr = mrun[i] == -__builtin_inff() ? -__builtin_inff() : 8.f;
+          if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
+            const float mnew = fmaxf(mrun[i], mref + mx);
+            const float alpha = mnew == -__builtin_inff() ? 1.f : fast_exp2(mrun[i] - mnew);
+            mrun[i] = mnew;
+            lsum[i] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) o[i][dt] *= alpha;
+            const float rnew = mnew == -__builtin_inff() ? 0.f : mnew;
+            const float delta = rnew - mref;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                sacc[i][kt][e] -= delta;
+                nxt[i][kt][e] -= delta;
+              }
+            cref[i] = f32x4_t{-rnew, -rnew, -rnew, -rnew};
+          }
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sacc[i][kt][e] = fast_exp2(sacc[i][kt][e]);
+        } else {
+          const float mnew = fmaxf(mrun[i], mx);
           const float alpha = mnew == -__builtin_inff() ? 1.f : fast_exp2(mrun[i] - mnew);
           mrun[i] = mnew;
-          if constexpr (kLean)
-            lsum[i] *= alpha;
-          else
-            lrun[i] *= alpha;
+          lrun[i] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < D / 16; ++dt) o[i][dt] *= alpha;
+          const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sacc[i][kt][e] = fast_exp2(sacc[i][kt][e] - mref);
         }
-        // a causal row may have no visible key yet: weights against 0 are then
-        // exp2(-inf) = 0 instead of NaN
-        const float mref = mrun[i] == -__builtin_inff() ? 0.f : mrun[i];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sacc[i][kt][e] = fast_exp2(__builtin_fmaf(sacc[i][kt][e], p.scale_log2, -mref));
         if constexpr (!kLean) {
           float rs = 0.f;
 #pragma unroll
@@ -316,7 +345,7 @@ void attn_kernel(const AttnParams p) {
         load_slice<D, SL>(kreg, va, vb, kc, vc, k0 + 2 * SL, k_end);
         mask(k0, cur);
         scores(bi ^ 1, nxt);
-        accumulate(bi, cur);
+        accumulate(bi, cur, nxt);
         __syncthreads();
       };
       f32x4_t sb[QPW][KT];
@@ -339,7 +368,7 @@ void attn_kernel(const AttnParams p) {
         load_slice<D, SL>(kreg, va, vb, kc, vc, k0 + SL, k_end);
         scores(0, sa);
         mask(k0, sa);
-        accumulate(0, sa);
+        accumulate(0, sa, sa);
         __syncthreads();
       }
     }

@@ -92,7 +92,8 @@ struct AttnParams {
   int causal;    // 0: every block row sees all L_b + B keys; 1: block row j sees keys < L_b + j + 1
   int slice;     // keys per LDS slice (64)
   int gb_pad;    // query rows per (b, g), padded to 16
-  float scale_log2;
+                 // (q carries the softmax scale in base 2, log2(e) / sqrt(D): the
+                 // scores come out of the MFMAs as s * c)
   float* pm;   // [Hkv][slots][gb_pad]
   float* pl;
   float* po;   // [Hkv][slots][gb_pad][D]
@@ -164,7 +165,8 @@ struct QkvPostParams {
   const int32_t* status;
   int batch, B, Hq, Hkv, D, max_ctx;
   float eps;
-  uint16_t* q;        // [rows, Hq, D]
+  uint16_t* q;        // [rows, Hq, D], multiplied by q_scale before rounding
+  float q_scale;      // log2(e) / sqrt(D): the attention scores in base 2
   uint16_t* kc;       // layer base [batch][Hkv][max_ctx][D]
   uint16_t* vc;
   int32_t* plan;      // if not NULL, one more workgroup writes the attention chunk split

@@ -301,14 +301,16 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
   const float o1 = y1 * cs.x - y2 * cs.y;
   const float o2 = y1 * cs.y + y2 * cs.x;
   bf16_t* dst;
+  float sc = 1.f;
   if (head < p.Hq) {
     dst = p.q + ((long long)m * p.Hq + head) * D;
+    sc = p.q_scale;  // queries carry the softmax scale (one rounding to bf16)
   } else {
     const int g = head - p.Hq;
     dst = p.kc + (((long long)b * p.Hkv + g) * p.max_ctx + pos) * D;
   }
-  dst[lane] = f2bf(o1);
-  dst[lane + half] = f2bf(o2);
+  dst[lane] = f2bf(o1 * sc);
+  dst[lane + half] = f2bf(o2 * sc);
 }
 
 // ---------------------------------------------------------------------------
