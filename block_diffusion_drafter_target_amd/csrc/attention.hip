@@ -52,20 +52,24 @@ __device__ __forceinline__ void load_slice(u32x4 (&kreg)[(Slice<D, SL>::KL)], u3
                                            u32x4 (&vb)[(Slice<D, SL>::VL)], const bf16_t* kc,
                                            const bf16_t* vc, int k0, int k_end) {
   constexpr int DC = Slice<D, SL>::DC;
+  // 32-bit byte offsets from the (uniform) head base: one sequence's and kv
+  // head's cache slab is below 4 GB (checked at launch)
+  const char* kb = reinterpret_cast<const char*>(kc);
+  const char* vb_ = reinterpret_cast<const char*>(vc);
 #pragma unroll
   for (int t = 0; t < Slice<D, SL>::KL; ++t) {
     const int e = threadIdx.x + t * 256;
     const int key = e / DC, ch = e % DC;
-    const int kidx = min(k0 + key, k_end - 1);
-    kreg[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + (long long)kidx * D + ch * 8));
+    const uint32_t kidx = (uint32_t)min(k0 + key, k_end - 1);
+    kreg[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (kidx * (2u * D) + 16u * ch)));
   }
 #pragma unroll
   for (int t = 0; t < Slice<D, SL>::VL; ++t) {
     const int e = threadIdx.x + t * 256;
     const int kp = e / DC, ch = e % DC;
-    const int k0i = min(k0 + 2 * kp, k_end - 1), k1i = min(k0 + 2 * kp + 1, k_end - 1);
-    va[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + (long long)k0i * D + ch * 8));
-    vb[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + (long long)k1i * D + ch * 8));
+    const uint32_t k0i = (uint32_t)min(k0 + 2 * kp, k_end - 1), k1i = (uint32_t)min(k0 + 2 * kp + 1, k_end - 1);
+    va[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb_ + (k0i * (2u * D) + 16u * ch)));
+    vb[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb_ + (k1i * (2u * D) + 16u * ch)));
   }
 }
 
@@ -492,6 +496,8 @@ hipError_t launch_d(const AttnParams& p, hipStream_t st) {
 
 hipError_t launch_attention(const AttnParams& p, int D, hipStream_t st) {
   if (p.n_ranges < p.batch || p.batch < 1 || p.slots < p.n_ranges) return hipErrorInvalidValue;
+  // the slice loads address one (sequence, kv head) slab with 32-bit byte offsets
+  if (p.max_ctx < 1 || (long long)p.max_ctx * D * 2 > 0xFFFFFFFFll) return hipErrorInvalidValue;
   if (D == 128) return launch_d<128>(p, st);
   if (D == 64) return launch_d<64>(p, st);
   return hipErrorInvalidValue;
