@@ -17,11 +17,12 @@
 // reads it. Workgroups past the last chunk exit at once. A chunk is walked
 // in 64-key slices
 // staged through LDS (K row-major with a 16-byte XOR swizzle over the row's
-// chunks, V transposed),
+// chunks, V row-major in padded rows, read through gfx950's transposing LDS
+// loads),
 // the next slice's global loads issued before the current slice's math.
 // Wave w owns query tiles w, w+4, ... (16 query rows each).
 //   S^T = K Q^T    A = K slice rows (LDS), B = Q^T (registers for the chunk)
-//   O^T += V^T P^T A = V^T (LDS, transposed), B = P^T straight from the S^T
+//   O^T += V^T P^T A = V^T (transposing LDS reads), B = P^T straight from the S^T
 //                  accumulators, so each lane keeps one query's softmax state
 // Online softmax in base 2 (scale * log2 e folded in); row max and row sum
 // combine the four lanes that share a query with two xor shuffles. Each
@@ -41,7 +42,9 @@ struct Slice {
   static constexpr int DC = D / 8;  // 16-byte chunks per key row
   static constexpr int KL = SL * DC / 256;
   static constexpr int VL = (SL / 2) * DC / 256;
-  static constexpr int VT = SL + 4;  // bf16 per transposed V row (8-byte pad)
+  // bf16 per V row in LDS: 32 bytes of padding put the eight rows that one
+  // transposing read serves at a time on disjoint banks
+  static constexpr int VP = D + 16;
 };
 
 // Global -> registers: the K and V rows of keys [k0, k0 + SL), clamped to the
@@ -73,21 +76,14 @@ __device__ __forceinline__ void load_slice(u32x4 (&kreg)[(Slice<D, SL>::KL)], u3
   }
 }
 
-template <int VT>
-__device__ __forceinline__ void store_vpair(bf16_t* vt, int d, int kp, uint32_t a, uint32_t b) {
-  // a holds keys 2kp's elements (d, d+1), b the same of key 2kp+1
-  *reinterpret_cast<uint32_t*>(vt + d * VT + 2 * kp) = (a & 0xFFFFu) | (b << 16);
-  *reinterpret_cast<uint32_t*>(vt + (d + 1) * VT + 2 * kp) = (a >> 16) | (b & 0xFFFF0000u);
-}
-
 // Registers -> LDS: K row-major with the 16-byte chunk index XOR (key & (DC-1));
-// V transposed to [d][key] so that a lane reads 4 keys of one d in 8 bytes.
+// V row-major too (padded rows): the O^T pass reads it transposed.
 template <int D, int SL>
-__device__ __forceinline__ void store_slice(u32x4* ks, bf16_t* vt, const u32x4 (&kreg)[(Slice<D, SL>::KL)],
+__device__ __forceinline__ void store_slice(u32x4* ks, bf16_t* vr, const u32x4 (&kreg)[(Slice<D, SL>::KL)],
                                             const u32x4 (&va)[(Slice<D, SL>::VL)],
                                             const u32x4 (&vb)[(Slice<D, SL>::VL)]) {
   constexpr int DC = Slice<D, SL>::DC;
-  constexpr int VT = Slice<D, SL>::VT;
+  constexpr int VP = Slice<D, SL>::VP;
 #pragma unroll
   for (int t = 0; t < Slice<D, SL>::KL; ++t) {
     const int e = threadIdx.x + t * 256;
@@ -98,11 +94,19 @@ __device__ __forceinline__ void store_slice(u32x4* ks, bf16_t* vt, const u32x4 (
   for (int t = 0; t < Slice<D, SL>::VL; ++t) {
     const int e = threadIdx.x + t * 256;
     const int kp = e / DC, ch = e % DC;
-    store_vpair<VT>(vt, ch * 8 + 0, kp, va[t].x, vb[t].x);
-    store_vpair<VT>(vt, ch * 8 + 2, kp, va[t].y, vb[t].y);
-    store_vpair<VT>(vt, ch * 8 + 4, kp, va[t].z, vb[t].z);
-    store_vpair<VT>(vt, ch * 8 + 6, kp, va[t].w, vb[t].w);
+    *reinterpret_cast<u32x4*>(vr + (2 * kp) * VP + ch * 8) = va[t];
+    *reinterpret_cast<u32x4*>(vr + (2 * kp + 1) * VP + ch * 8) = vb[t];
   }
+}
+
+// gfx950's transposing LDS read of 16-bit data: within each group of 16
+// lanes, lane i receives element i & 3 of the 8-byte chunks addressed by
+// lanes 4e + (i >> 2), e = 0..3 (so lanes 4e..4e+3 address four consecutive
+// chunks of one row, and lane i gets column i of four rows).
+__device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // Waves per SIMD the register budget targets: two where a wave's accumulators,
@@ -119,7 +123,7 @@ void attn_kernel(const AttnParams p) {
   constexpr int DC = Slice<D, SL>::DC;
   constexpr int KL = Slice<D, SL>::KL;
   constexpr int VL = Slice<D, SL>::VL;
-  constexpr int VT = Slice<D, SL>::VT;
+  constexpr int VP = Slice<D, SL>::VP;
   static_assert(KL >= 1 && VL >= 1, "slice too small");
   // D = 64: scores one slice ahead of the softmax, slices in two LDS buffers
   // (measured on MI355X: the gpt-oss-shaped attention 573 -> 544 us per step);
@@ -136,7 +140,7 @@ void attn_kernel(const AttnParams p) {
   // (the extra accumulators would spill).
   constexpr bool kLean = kPipe && QPW <= 2;
   __shared__ __align__(16) u32x4 ks[NBUF][SL * DC];
-  __shared__ __align__(16) bf16_t vt[NBUF][D * VT];
+  __shared__ __align__(16) bf16_t vt[NBUF][SL * VP];
 
   const int u = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -317,9 +321,10 @@ void attn_kernel(const AttnParams p) {
       for (int h = 0; h < KT / 2; ++h) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-          const bf16_t* row = vt[bi] + (dt * 16 + r) * VT + 32 * h + 4 * gq;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
+          // lane (gq, r) gets V[keys 32h + 4gq + 0..3 (lo), + 16 (hi)][d = 16dt + r]
+          const bf16_t* row = vt[bi] + (32 * h + 4 * gq + (r >> 2)) * VP + dt * 16 + 4 * (r & 3);
+          const u32x2 lo = lds_read_tr16(row);
+          const u32x2 hi = lds_read_tr16(row + 16 * VP);
           const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
           for (int i = 0; i < QPW; ++i) o[i][dt] = mfma16x16x32(a, pb[i][h], o[i][dt]);
