@@ -131,14 +131,14 @@ void attn_kernel(const AttnParams p) {
   // measured 1-2% slower there, and 12% slower for chunks of one slice)
   constexpr bool kPipe = D == 64;
   constexpr int NBUF = kPipe ? 2 : 1;
-  // With the pipeline the softmax VALU work also counts (measured 546 -> 530
-  // us per step): the softmax reference moves only when a score exceeds it by
-  // more than 2^8 (a wave-uniform branch, so the rescale of O is skipped on
-  // almost every slice; weights stay <= 256, exact in fp32 and in the bf16
-  // operand), and the row sums come out of the matrix cores as one more O^T
-  // tile against an all-ones operand. Not with four query tiles per wave
-  // (the extra accumulators would spill).
-  constexpr bool kLean = kPipe && QPW <= 2;
+  // Lean softmax: the reference moves only when a score exceeds it by more
+  // than 2^8 (a wave-uniform branch, so the rescale of O is skipped on almost
+  // every slice; weights stay <= 256, exact in fp32 and in the bf16 operand),
+  // and the row sums come out of the matrix cores as one more O^T tile
+  // against an all-ones operand (measured with the D = 64 pipeline 546 -> 530
+  // us per step; at D = 128 1-2% once the V store stopped transposing). Not
+  // with four query tiles per wave (the extra accumulators would spill).
+  constexpr bool kLean = QPW <= 2;
   __shared__ __align__(16) u32x4 ks[NBUF][SL * DC];
   __shared__ __align__(16) bf16_t vt[NBUF][SL * VP];
 
@@ -276,7 +276,7 @@ void attn_kernel(const AttnParams p) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 sacc[i][kt][e] -= delta;
-                nxt[i][kt][e] -= delta;
+                if constexpr (kPipe) nxt[i][kt][e] -= delta;
               }
             cref[i] = f32x4_t{-rnew, -rnew, -rnew, -rnew};
           }
