@@ -376,3 +376,38 @@ def test_run_twice_is_bit_identical(gpu_lib):
         outs.append((dr.draft.cpu().numpy().copy(), lg.cpu().numpy()))
     assert np.array_equal(outs[0][0], outs[1][0])
     assert np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("shape", ["long-d64", "long-d128"])
+def test_attention_reference_moves_mid_chunk(gpu_lib, shape):
+    """Keys whose scores jump far above the running softmax reference in the
+    middle of an attention chunk: a few cached keys of every layer are scaled by
+    16 (exact in bf16), so their base-2 scores exceed the reference taken from
+    the chunk's earlier slices by much more than 8. The lazy reference then
+    moves mid-chunk, and in the two-buffer D = 64 loop the next slice's scores,
+    already computed against the old reference, are shifted too. Every layer
+    is replayed in fp64 from the device's own input and (modified) cache."""
+    torch = _torch()
+    cfg = gh.SHAPES[shape]
+    lens = gh.CTX[shape]
+    gh.log(f"[attention reference moves] {shape}")
+    W, WO, ocfg, dr, cache, taps = make_case(cfg, lens)
+    batch, B, H, NL = len(lens), cfg.block, cfg.hidden, cfg.n_layers
+    for b, L in enumerate(lens):
+        slots = sorted({min(L - 1, L * k // 7 + 37) for k in range(1, 7)}) if L > 1 else []
+        for s in slots:
+            dr.k[:, b, :, s] *= 16
+    anchor = synth.make_anchors(cfg.with_(batch=batch))
+    dr.anchor.copy_(torch.from_numpy(anchor))
+    dbg_hidden = torch.empty((NL + 1, batch * B, H), dtype=torch.float32, device="cuda")
+    dr.draft_block(dbg_hidden=dbg_hidden)
+    torch.cuda.synchronize()
+    assert dr.status.cpu().tolist() == [0] * batch
+    hidden = dbg_hidden.cpu().numpy().astype(np.float64).reshape(NL + 1, batch, B, H)
+    for b, L in enumerate(lens):
+        pos = L + np.arange(B)
+        for l in range(NL):
+            kc, vc = gpu_cache(dr, l, b, L)
+            want, _, _ = ref.decoder_layer(ocfg, WO, l, hidden[l, b], pos, kc, vc)
+            e = gh.check_rel(hidden[l + 1, b], want, tol=1e-2, what=f"replay layer {l} seq {b}")
+            gh.log(f"    layer {l} seq {b} (context {L}): rel err {e:.2e}")
