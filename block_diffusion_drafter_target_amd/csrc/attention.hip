@@ -24,8 +24,10 @@
 //   S^T = K Q^T    A = K slice rows (LDS), B = Q^T (registers for the chunk)
 //   O^T += V^T P^T A = V^T (transposing LDS reads), B = P^T straight from the S^T
 //                  accumulators, so each lane keeps one query's softmax state
-// Online softmax in base 2 (scale * log2 e folded in); row max and row sum
-// combine the four lanes that share a query with two xor shuffles. Each
+// Online softmax in base 2 (the queries arrive multiplied by log2(e)/sqrt(D));
+// the row max combines the four lanes that share a query with two xor
+// shuffles; the row sum comes from the matrix cores (one more O^T tile) with
+// up to two query tiles per wave, else from the same shuffles. Each
 // workgroup writes (max, sum, unnormalised O) to its chunk's slot; the merge
 // kernel combines the chunks of a sequence with the log-sum-exp rule.
 #include "attn_split.h"
