@@ -313,24 +313,29 @@ struct AttnPlan {
   int slice, gb_pad;
 };
 
-constexpr int kAttnTargetWGs = 512;  // attention workgroups when every sequence is at full length
+// attention workgroups when every sequence is at full length, by head size
+// (measured on MI355X with 256/384/512/768: D = 64 is fastest at 512, D = 128
+// at 384 for the block-sweep batch, 261 against 272 us per step, the batch-32
+// and batch-1 splits being the same at both)
+constexpr int kAttnTargetWGsD64 = 512;
+constexpr int kAttnTargetWGsD128 = 384;
 constexpr int kAttnMaxChunks = 32;   // per (sequence, kv head): 64 measured slower at batch 1
 
-// Attention chunks: about kAttnTargetWGs workgroups (one per CU slot at two
-// per CU) over the batch, n_chunks per sequence and kv head at full length,
-// without chunks shorter than 64 keys of the cache. The device picks one
+// Attention chunks: about the target number of workgroups over the batch,
+// n_chunks per sequence and kv head at full length, without chunks shorter
+// than 64 keys of the cache. The device picks one
 // chunk length for the batch from the real lengths so that all chunks fit the
 // n_chunks * batch workgroups per kv head: in a ragged batch the long
 // sequences take more chunks than the short ones and no workgroup holds more
 // keys than the chunk length (with equal lengths this is the per-sequence
 // split). Measured on MI355X: 768, 1024 and 2048 workgroups were slower at
-// every configuration.
+// every configuration, 256 too.
 AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx, int B) {
   AttnPlan a;
   const int G = c.n_q_heads / c.n_kv_heads;
   a.gb_pad = (int)cdiv(G * B, 16) * 16;
   const long long units = (long long)batch * c.n_kv_heads;
-  long long n = cdiv(kAttnTargetWGs, units);
+  long long n = cdiv(c.head_dim == 64 ? kAttnTargetWGsD64 : kAttnTargetWGsD128, units);
   n = std::min<long long>(n, cdiv(max_ctx, 64));
   a.n_chunks = (int)std::max<long long>(1, std::min<long long>(n, kAttnMaxChunks));
   a.n_ranges = a.n_chunks * batch;
