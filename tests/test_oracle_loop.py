@@ -276,3 +276,35 @@ def test_draft_block_ignores_dead_slots_and_is_batch_independent():
         assert np.array_equal(rb["draft"][0], r["draft"][b])
     # the tokens are the argmax of the logits of rows 1..B-1
     assert np.array_equal(r["draft"], np.argmax(r["logits"], axis=-1))
+
+
+def test_draft_block_equals_per_row_evaluation_of_the_whole_stack():
+    """Every drafted row's logits from a pass that carries that row alone
+    through every layer (its own query against the context plus the block's
+    K/V of that layer) and then the final norm and LM head: one block pass
+    equals B independent per-position evaluations under the same mask."""
+    cfg, W, g = _small()
+    L = 6
+    cache = _filled_cache(cfg, W, g, [L], 20)
+    anchor = 11
+    r = ref.draft_block(cfg, W, cache, [L], [anchor])
+    B, Hq, D = cfg.block, cfg.n_q_heads, cfg.head_dim
+    toks = [anchor] + [cfg.mask_id] * (B - 1)
+    for j in range(B):
+        x = W["embed"][toks[j]][None, :]
+        p = np.array([L + j])
+        for l in range(cfg.n_layers):
+            pre = f"layers.{l}."
+            K = np.concatenate([cache["k"][l, 0, :L], r["block_k"][0, l]])
+            V = np.concatenate([cache["v"][l, 0, :L], r["block_v"][0, l]])
+            u = ref.rms_norm(x, W[pre + "g_in"], cfg.rms_eps)
+            q = (u @ W[pre + "w_qkv"][:Hq * D].T).reshape(1, Hq, D)
+            q = ref.rope(ref.rms_norm(q, W[pre + "g_q"], cfg.rms_eps), p, cfg.rope_theta)
+            x = x + ref.attention(q, K, V).reshape(1, -1) @ W[pre + "w_o"].T
+            w = ref.rms_norm(x, W[pre + "g_post"], cfg.rms_eps)
+            x = x + (ref.silu(w @ W[pre + "w_gate"].T) * (w @ W[pre + "w_up"].T)) @ W[pre + "w_down"].T
+            assert np.allclose(x[0], r["hidden"][0, l + 1, j], atol=1e-11)
+        if j:
+            z = ref.rms_norm(x, W["g_final"], cfg.rms_eps) @ W["lm_head"].T
+            assert np.allclose(z[0], r["logits"][0, j - 1], atol=1e-11)
+            assert int(np.argmax(z[0])) == int(r["draft"][0, j - 1])

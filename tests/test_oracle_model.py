@@ -186,3 +186,87 @@ def test_inject_writes_every_layer_at_commit_positions():
             assert np.allclose(cache["v"][l, b, p], v[0], rtol=0, atol=1e-12)
     written = sum(1 for _ in rows) * cfg.n_layers * cfg.n_kv_heads * cfg.head_dim
     assert np.sum(~np.isnan(cache["k"])) == written
+
+
+# ---------------------------------------------------------------- whole draft block
+
+def _hf_block(model, cfg, ctx, L, ids, pos, causal=False):
+    """The library model run over one block: context K/V made by each library
+    layer's own k/v projections, k-norm and rotary embedding from the context
+    feature rows ``ctx`` (at positions 0..L-1), then a forward over ``ids`` at
+    ``pos``. Returns (logits [n, V], hidden states (embeddings, then each
+    layer's output), the final norm's input, the final norm's output)."""
+    n = len(ids)
+    rot = model.model.rotary_emb
+    seen = {}
+    hook = model.model.norm.register_forward_hook(
+        lambda m, a, o: seen.update(pre=a[0].clone(), post=o.clone()))
+    try:
+        with torch.no_grad():
+            cache = DynamicCache()
+            if L:
+                for l, layer in enumerate(model.model.layers):
+                    kh, vh = _hf_ctx_kv(layer, cfg, rot, ctx, np.arange(L))
+                    cache.update(kh.contiguous(), vh.contiguous(), l)
+            allowed = np.ones((n, L + n), bool)
+            if causal:
+                allowed = np.arange(L + n)[None, :] <= np.asarray(pos)[:, None]
+            mask = torch.from_numpy(np.where(allowed, 0.0, -np.inf))[None, None]
+            out = model(input_ids=torch.tensor([list(ids)]), position_ids=torch.tensor([list(pos)]),
+                        past_key_values=cache if L else None, attention_mask=mask, use_cache=True,
+                        output_hidden_states=True)
+    finally:
+        hook.remove()
+    hs = [h[0].numpy() for h in out.hidden_states]
+    return out.logits[0].numpy(), hs, seen["pre"][0].numpy(), seen["post"][0].numpy()
+
+
+@pytest.mark.parametrize("L", [0, 1, 29])
+def test_draft_block_matches_library_model(L):
+    """ref.draft_block's assembly against the library model run over the block.
+
+    The reading pinned here: row 0 holds the anchor and rows 1..B-1 the mask id,
+    the rows sit at positions L..L+B-1 after a context injected at 0..L-1 with
+    each layer's own k/v projections, attention inside the block is unmasked,
+    the drafter's own final norm precedes the shared LM head, and rows 1..B-1
+    (no shift) give the B-1 drafted tokens. [P1 "Hva gjør DFlash annerledes
+    enn vanlig spekulativ dekoding?"; P3 "Come funziona il drafting a
+    blocchi"; P3 "L'idea chiave: Il target sa meglio"]"""
+    cfg = small_cfg(block=16)
+    NL, B = cfg.n_layers, cfg.block
+    W = rand_weights(cfg, NL, seed=21)
+    model = hf_model(cfg, W, NL)
+    g = np.random.default_rng(100 + L)
+    ctx = g.standard_normal((L, cfg.hidden))
+    anchor = int(g.integers(0, cfg.vocab - 1))
+    cache = ref.new_cache(cfg, 1, L + B + 3, fill=np.nan)
+    ref.inject_kv(cfg, W, ctx, [(r, 0, r) for r in range(L)], cache)
+    r = ref.draft_block(cfg, W, cache, [L], [anchor])
+
+    ids = [anchor] + [cfg.mask_id] * (B - 1)
+    pos = L + np.arange(B)
+    z, hs, pre, post = _hf_block(model, cfg, ctx, L, ids, pos)
+    for l in range(NL):
+        assert ref.rel_err(r["hidden"][0, l], hs[l]) < TOL, f"hidden after layer {l}"
+    assert ref.rel_err(r["hidden"][0, NL], pre) < TOL
+    assert ref.rel_err(r["final"][0], post) < TOL
+    assert ref.rel_err(r["logits"][0], z[1:]) < TOL
+    zs = np.sort(z[1:], axis=1)
+    assert np.all(zs[:, -1] - zs[:, -2] > 1e-3), "a near tie would make the token check meaningless"
+    assert np.array_equal(r["draft"][0], np.argmax(z[1:], axis=1))
+
+    # Each plausible slip in the assembly moves the result far outside the
+    # tolerance, so an oracle that made it would fail the checks above.
+    # (With no context every position shift is a global shift, which rotary
+    # embeddings cannot see: the position slip is only checked for L >= 1.)
+    far = 100 * TOL
+    if L:
+        z_pos = _hf_block(model, cfg, ctx, L, ids, pos + 1)
+        assert ref.rel_err(z_pos[0][1:], z[1:]) > far, "block positions L+1+j"
+    z_mask = _hf_block(model, cfg, ctx, L, [cfg.mask_id] * B, pos)
+    assert ref.rel_err(z_mask[0][1:], z[1:]) > far, "row 0 holding the mask"
+    assert ref.rel_err(z[:-1], z[1:]) > far, "LM rows shifted by one"
+    z_nonorm = pre @ W["lm_head"].T
+    assert ref.rel_err(z_nonorm[1:], z[1:]) > far, "final norm dropped"
+    z_causal = _hf_block(model, cfg, ctx, L, ids, pos, causal=True)
+    assert ref.rel_err(z_causal[0][1:], z[1:]) > far, "causal mask inside the block"
