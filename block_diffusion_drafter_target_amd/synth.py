@@ -223,22 +223,43 @@ def gain_shapes(cfg: DraftConfig) -> list[tuple[str, int]]:
     return out
 
 
-def make_weights(cfg: DraftConfig, seed: int = SEED_WEIGHTS, only: set[str] | None = None) -> dict[str, np.ndarray]:
-    """Drafter weights: matrices N(0, 0.02^2), norm gains 1.0.
+# random norm gains (opt-in): 1 + GAIN_STD * N(0, 1), every gain vector drawn
+# from its own stream so that each differs from 1 and from every other gain
+GAIN_STD = 0.3
+_GAIN_TID0 = 1 << 16  # tensor ids of gain streams (clear of the matrices' ids)
+
+
+def _gain(n: int, fp32: bool, seed: int | None, tid: int) -> np.ndarray:
+    if seed is None:
+        a = np.ones(n, np.float32)
+    else:
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _GAIN_TID0 + tid])))
+        a = (1.0 + GAIN_STD * g.standard_normal(n)).astype(np.float32)
+    b = f32_to_bf16(a)
+    return bf16_to_f32(b) if fp32 else b
+
+
+def make_weights(cfg: DraftConfig, seed: int = SEED_WEIGHTS, only: set[str] | None = None,
+                 gains: str = "ones") -> dict[str, np.ndarray]:
+    """Drafter weights: matrices N(0, 0.02^2); norm gains 1.0, or with
+    ``gains="random"`` 1 + 0.3 N(0, 1) on the bf16 grid, each gain vector from
+    its own seeded stream.
 
     bf16 bits (uint16) unless ``cfg.weights_fp32`` (then fp32 values that lie on
     the bf16 grid, so the oracle and a bf16 device path read identical numbers).
     """
+    if gains not in ("ones", "random"):
+        raise ValueError("gains must be 'ones' or 'random'")
     w: dict[str, np.ndarray] = {}
     for tid, (name, r, c) in enumerate(weight_shapes(cfg)):
         if only is not None and name not in only:
             continue
         w[name] = normal_tensor(seed, tid, r, c, WEIGHT_STD, fp32=cfg.weights_fp32)
-    one = np.float32(1.0)
-    for name, n in gain_shapes(cfg):
+    gseed = seed if gains == "random" else None
+    for tid, (name, n) in enumerate(gain_shapes(cfg)):
         if only is not None and name not in only:
             continue
-        w[name] = np.full(n, one, np.float32) if cfg.weights_fp32 else f32_to_bf16(np.full(n, one, np.float32))
+        w[name] = _gain(n, cfg.weights_fp32, gseed, tid)
     return w
 
 
@@ -268,19 +289,21 @@ def target_weight_shapes(cfg: DraftConfig) -> list[tuple[str, int, int]]:
 
 
 def make_target_weights(cfg: DraftConfig, drafter: dict[str, np.ndarray],
-                        seed: int = SEED_TARGET_WEIGHTS) -> dict[str, np.ndarray]:
+                        seed: int = SEED_TARGET_WEIGHTS, gains: str = "ones") -> dict[str, np.ndarray]:
+    """Target weights (embedding and LM head shared with the drafter); gains as
+    in :func:`make_weights`."""
+    if gains not in ("ones", "random"):
+        raise ValueError("gains must be 'ones' or 'random'")
     w: dict[str, np.ndarray] = {"embed": drafter["embed"], "lm_head": drafter["lm_head"]}
     for tid, (name, r, c) in enumerate(target_weight_shapes(cfg)):
         w[name] = normal_tensor(seed, tid, r, c, WEIGHT_STD, fp32=cfg.weights_fp32)
-    one = np.ones(cfg.hidden, np.float32)
-    oned = np.ones(cfg.head_dim, np.float32)
-    cvt = (lambda a: a) if cfg.weights_fp32 else f32_to_bf16
-    w["g_final"] = cvt(one)
+    gseed = seed if gains == "random" else None
+    names = [("g_final", cfg.hidden)]
     for l in range(cfg.target_layers):
-        w[f"layers.{l}.g_in"] = cvt(one)
-        w[f"layers.{l}.g_post"] = cvt(one)
-        w[f"layers.{l}.g_q"] = cvt(oned)
-        w[f"layers.{l}.g_k"] = cvt(oned)
+        names += [(f"layers.{l}.g_in", cfg.hidden), (f"layers.{l}.g_post", cfg.hidden),
+                  (f"layers.{l}.g_q", cfg.head_dim), (f"layers.{l}.g_k", cfg.head_dim)]
+    for tid, (name, n) in enumerate(names):
+        w[name] = _gain(n, cfg.weights_fp32, gseed, tid)
     return w
 
 

@@ -99,9 +99,10 @@ def test_fullsize_lm_head_and_tokens(c2):
     cfg, W, dr, taps, anchor, out = c2
     gh.log("[fullsize c2] LM head (full vocabulary, fp64)")
     fin = ref.rms_norm(out["hidden"][cfg.n_layers][1:], synth.bf16_to_f64(W["g_final"]), cfg.rms_eps)
-    z = fin @ synth.bf16_to_f64(W["lm_head"]).T
+    lm = synth.bf16_to_f64(W["lm_head"])
+    z = fin @ lm.T
     e = gh.check_rel(out["logits"], z, tol=1e-2, what="logits")
-    band = gh.check_tokens(out["draft"], out["logits"], z, what="draft tokens")
+    band = gh.check_tokens(out["draft"], out["logits"], z, gh.replay_band(fin, lm), what="draft tokens")
     gh.log(f"    rel err {e:.2e}, tie-band rows {band}/{len(out['draft'])}")
 
 
@@ -117,7 +118,7 @@ def test_fullsize_end_to_end(c2):
     for l in range(cfg.n_layers + 1):
         gh.check_rel(out["hidden"][l], r["hidden"][0, l], what=f"hidden {l}")
     e = gh.check_rel(out["logits"], r["logits"][0], what="logits")
-    band = gh.check_tokens(out["draft"], out["logits"], r["logits"][0], what="tokens")
+    band = gh.check_tokens(out["draft"], out["logits"], r["logits"][0], gh.e2e_band(r["logits"][0]), what="tokens")
     gh.log(f"    logits rel err {e:.2e}, tie-band rows {band}")
 
 
@@ -135,3 +136,52 @@ def test_fullsize_verify(c2):
         n = int(dr.n_commit.item())
         assert np.array_equal(dr.commit_rows.cpu().numpy()[:n], r["commit_rows"])
         assert np.array_equal(dr.emitted.cpu().numpy(), r["emitted"])
+
+
+def test_fullsize_random_gains_layer(gpu_lib):
+    """One layer of the benchmarked shape with random norm gains (g_fc, g_in,
+    g_q, g_k, g_post, g_final each its own draw): fused rows, injected K/V, the
+    layer replayed from the device's input and cache, and the full LM head."""
+    import torch
+    cfg = synth.CONFIGS["c2"].with_(n_layers=1)
+    L, B = cfg.ctx_len, cfg.block
+    ocfg = ref.OracleConfig.from_any(cfg)
+    gh.log("[fullsize c2, random gains] one layer, context 1024")
+    W = synth.make_weights(cfg, gains="random")
+    dr = Drafter(cfg, W, batch=1, max_ctx=L + 2 * B, max_rows=L)
+    taps = synth.make_taps(cfg, L, tid=0)
+    dr.ingest(0, _bf16_dev(torch, taps))
+    dr.anchor.copy_(torch.from_numpy(synth.make_anchors(cfg)))
+    logits = torch.empty((B - 1, cfg.vocab), dtype=torch.float32, device="cuda")
+    hidden = torch.empty((2, B, cfg.hidden), dtype=torch.float32, device="cuda")
+    dr.draft_block(dbg_logits=logits, dbg_hidden=hidden)
+    rows = [0, 333, L - 1]
+    ctx = torch.empty((len(rows), cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    dr.fuse_ctx(_bf16_dev(torch, taps[rows]), len(rows), ctx)
+    torch.cuda.synchronize()
+    assert dr.status.cpu().tolist() == [0]
+    LW = _layer_w(W, 0)
+    WF = {"w_fc": synth.bf16_to_f64(W["w_fc"]), "g_fc": synth.bf16_to_f64(W["g_fc"])}
+    got = gh.to_np_bf16(ctx)
+    gh.check_rel(got, ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps[rows])), what="fuse rows")
+    k, v = ref.project_kv(ocfg, LW, 0, got, np.array(rows))
+    gh.check_rel(gh.to_np_bf16(dr.k[0, 0][:, rows]).transpose(1, 0, 2), k, what="K rows")
+    gh.check_rel(gh.to_np_bf16(dr.v[0, 0][:, rows]).transpose(1, 0, 2), v, what="V rows")
+    hid = hidden.cpu().numpy().astype(np.float64)
+    # the embedding row is the embedding itself (the input norm's gain acts inside the layer)
+    E = synth.bf16_to_f64(W["embed"])
+    toks = [int(dr.anchor.item())] + [cfg.mask_id] * (B - 1)
+    assert np.array_equal(hid[0], E[toks])
+    kc = gh.to_np_bf16(dr.k[0, 0, :, :L]).transpose(1, 0, 2)
+    vc = gh.to_np_bf16(dr.v[0, 0, :, :L]).transpose(1, 0, 2)
+    want, kb, vb = ref.decoder_layer(ocfg, LW, 0, hid[0], L + np.arange(B), kc, vc)
+    e = gh.check_rel(hid[1], want, tol=1e-2, what="layer 0")
+    gh.check_rel(gh.to_np_bf16(dr.k[0, 0, :, L:L + B]).transpose(1, 0, 2), kb, what="block K")
+    gh.check_rel(gh.to_np_bf16(dr.v[0, 0, :, L:L + B]).transpose(1, 0, 2), vb, what="block V")
+    fin = ref.rms_norm(hid[1][1:], synth.bf16_to_f64(W["g_final"]), cfg.rms_eps)
+    lm = synth.bf16_to_f64(W["lm_head"])
+    z = fin @ lm.T
+    el = gh.check_rel(logits.cpu().numpy(), z, tol=1e-2, what="logits")
+    band = gh.check_tokens(dr.draft.cpu().numpy()[0], logits.cpu().numpy(), z, gh.replay_band(fin, lm),
+                           what="tokens")
+    gh.log(f"    layer rel err {e:.2e}, logits {el:.2e}, tie-band rows {band}")

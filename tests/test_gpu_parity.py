@@ -20,9 +20,9 @@ def _torch():
     return torch
 
 
-def make_case(cfg, ctx_lens, extra_ctx=48):
+def make_case(cfg, ctx_lens, extra_ctx=48, gains="ones"):
     torch = _torch()
-    W = synth.make_weights(cfg)
+    W = synth.make_weights(cfg, gains=gains)
     WO = gh.oracle_weights(W)
     ocfg = ref.OracleConfig.from_any(cfg)
     batch = len(ctx_lens)
@@ -62,13 +62,21 @@ def test_pack_matrix_layout(gpu_lib):
         assert np.array_equal(got.reshape(rows, cols), want)
 
 
-@pytest.mark.parametrize("shape", sorted(gh.SHAPES))
-def test_fuse_ctx_parity(gpu_lib, shape):
+# every shape with unit gains, and the shapes below again with random gains
+# (each gain vector its own draw, so a swapped, unused or misindexed gain
+# changes the compared values)
+GAIN_SHAPES = ["gqa-d128", "g8-d64", "tiled-b9", "big-b19", "mlp-wide-b2", "b12"]
+CASES = [(s, "ones") for s in sorted(gh.SHAPES)] + [(s, "random") for s in GAIN_SHAPES]
+CASE_IDS = [f"{s}-{g}" for s, g in CASES]
+
+
+@pytest.mark.parametrize("shape,gains", CASES, ids=CASE_IDS)
+def test_fuse_ctx_parity(gpu_lib, shape, gains):
     torch = _torch()
     cfg = gh.SHAPES[shape]
-    gh.log(f"[fuse] {shape}")
-    W = synth.make_weights(cfg, only={"w_fc", "g_fc"})
-    full = synth.make_weights(cfg)
+    gh.log(f"[fuse] {shape} gains {gains}")
+    W = synth.make_weights(cfg, only={"w_fc", "g_fc"}, gains=gains)
+    full = synth.make_weights(cfg, gains=gains)
     WO = gh.oracle_weights(W)
     ocfg = ref.OracleConfig.from_any(cfg)
     n = 300  # tiled GEMM: three row tiles, the last ragged
@@ -83,13 +91,13 @@ def test_fuse_ctx_parity(gpu_lib, shape):
     gh.log(f"    rel err {e:.2e}")
 
 
-@pytest.mark.parametrize("shape", sorted(gh.SHAPES))
-def test_inject_kv_parity(gpu_lib, shape):
+@pytest.mark.parametrize("shape,gains", CASES, ids=CASE_IDS)
+def test_inject_kv_parity(gpu_lib, shape, gains):
     torch = _torch()
     cfg = gh.SHAPES[shape]
-    gh.log(f"[inject] {shape}")
+    gh.log(f"[inject] {shape} gains {gains}")
     lens = gh.CTX[shape]
-    W, WO, ocfg, dr, cache, taps = make_case(cfg, lens)
+    W, WO, ocfg, dr, cache, taps = make_case(cfg, lens, gains=gains)
     assert dr.ctx_len.cpu().tolist() == lens
     assert dr.status.cpu().tolist() == [0] * len(lens)
     for b, L in enumerate(lens):
@@ -113,13 +121,13 @@ def test_inject_kv_parity(gpu_lib, shape):
         assert float(dr.k[:, b, :, L:].abs().max()) == 0.0
 
 
-@pytest.mark.parametrize("shape", sorted(gh.SHAPES))
-def test_draft_block_parity(gpu_lib, shape):
+@pytest.mark.parametrize("shape,gains", CASES, ids=CASE_IDS)
+def test_draft_block_parity(gpu_lib, shape, gains):
     torch = _torch()
     cfg = gh.SHAPES[shape]
-    gh.log(f"[draft_block] {shape}")
+    gh.log(f"[draft_block] {shape} gains {gains}")
     lens = gh.CTX[shape]
-    W, WO, ocfg, dr, cache, taps = make_case(cfg, lens)
+    W, WO, ocfg, dr, cache, taps = make_case(cfg, lens, gains=gains)
     batch, B, H, NL, V = len(lens), cfg.block, cfg.hidden, cfg.n_layers, cfg.vocab
     anchor = synth.make_anchors(cfg.with_(batch=batch))
     dr.anchor.copy_(torch.from_numpy(anchor))
@@ -138,7 +146,7 @@ def test_draft_block_parity(gpu_lib, shape):
     for l in range(NL + 1):
         gh.check_rel(hidden[l], r["hidden"][:, l], what=f"hidden after layer {l}")
     gh.check_rel(logits, r["logits"], what="logits")
-    band = gh.check_tokens(draft, logits, r["logits"], what="draft tokens")
+    band = gh.check_tokens(draft, logits, r["logits"], gh.e2e_band(r["logits"]), what="draft tokens")
     gh.log(f"    tie-band rows (end to end): {band}/{draft.size}")
 
     # stage replay: every layer from the device's own input and cached context
@@ -155,7 +163,7 @@ def test_draft_block_parity(gpu_lib, shape):
         fin = ref.rms_norm(hidden[NL, b], WO["g_final"], cfg.rms_eps)
         z = fin[1:] @ WO["lm_head"].T
         gh.check_rel(logits[b], z, tol=1e-2, what=f"replay lm head seq {b}")
-        gh.check_tokens(draft[b], logits[b], z, what=f"replay tokens seq {b}")
+        gh.check_tokens(draft[b], logits[b], z, gh.replay_band(fin[1:], WO["lm_head"]), what=f"replay tokens seq {b}")
 
 
 def test_draft_block_capacity_status(gpu_lib):
@@ -176,7 +184,7 @@ def test_draft_block_capacity_status(gpu_lib):
     r = ref.draft_block(ocfg, WO, cache, lens[:2], [1, 2])
     logits = lg.cpu().numpy().astype(np.float64).reshape(3, cfg.block - 1, cfg.vocab)
     gh.check_rel(logits[:2], r["logits"], what="logits beside a failed sequence")
-    gh.check_tokens(d[:2], logits[:2], r["logits"], what="tokens beside a failed sequence")
+    gh.check_tokens(d[:2], logits[:2], r["logits"], gh.e2e_band(r["logits"]), what="tokens beside a failed sequence")
 
 
 @pytest.mark.parametrize("B", [2, 3, 5])
@@ -201,7 +209,7 @@ def test_small_blocks_draft_and_verify(gpu_lib, B):
     logits = lg.cpu().numpy().astype(np.float64).reshape(cfg.batch, B - 1, V)
     r = ref.draft_block(ocfg, WO, cache, lens, anchor)
     gh.check_rel(logits, r["logits"], what=f"logits, block {B}")
-    gh.check_tokens(d, logits, r["logits"], what=f"tokens, block {B}")
+    gh.check_tokens(d, logits, r["logits"], gh.e2e_band(r["logits"]), what=f"tokens, block {B}")
     for step in range(4):
         m = synth.geometric_accept(cfg.batch, B, 0.8, step=step)
         tgt = synth.synth_target_tokens(d, m, V, step=step)
@@ -245,7 +253,7 @@ def test_draft_block_batch_over_64(gpu_lib):
     r = ref.draft_block(ocfg, WO, cache, lens[:bad], anchor[:bad])
     logits = lg.cpu().numpy().astype(np.float64).reshape(cfg.batch, B - 1, V)
     gh.check_rel(logits[:bad], r["logits"], what="logits of 69 sequences")
-    band = gh.check_tokens(d[:bad], logits[:bad], r["logits"], what="tokens of 69 sequences")
+    band = gh.check_tokens(d[:bad], logits[:bad], r["logits"], gh.e2e_band(r["logits"]), what="tokens of 69 sequences")
     gh.log(f"    tie-band rows {band}/{d[:bad].size}")
 
 
