@@ -25,7 +25,11 @@ EXPORTED = ("dflash_model_create", "dflash_model_destroy", "dflash_rope_table",
             "dflash_draft_block", "dflash_verify_accept", "dflash_status_string",
             "dflash_profile_enable", "dflash_profile_read", "dflash_pack_matrix",
             "dflash_target_create", "dflash_target_forward", "dflash_kv_commit",
-            "dflash_draft_block_sample", "dflash_verify_sample", "dflash_sample_logits")
+            "dflash_draft_block_sample", "dflash_verify_sample", "dflash_sample_logits",
+            "dflash_draft_block_noalloc")
+
+# bytes of the static device workspace behind dflash_draft_block_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 PHASES = {"lm_head": 0, "attention": 1, "qkv": 2, "o": 3, "gate_up": 4, "down": 5, "fuse": 6,
           "inject": 7, "verify": 8}
@@ -82,6 +86,7 @@ def load() -> C.CDLL:
     lib.dflash_fuse_ctx.argtypes = [vp, vp, i32, vp, vp, sz, vp]
     lib.dflash_inject_kv.argtypes = [vp, vp, i32, vp, vp, i32, C.POINTER(dflash_kv), vp, sz, vp]
     lib.dflash_draft_block.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp, vp, sz, vp]
+    lib.dflash_draft_block_noalloc.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp, vp]
     lib.dflash_target_create.argtypes = [C.POINTER(dflash_config), C.POINTER(dflash_weights), vp, C.POINTER(vp)]
     lib.dflash_target_forward.argtypes = [vp, C.POINTER(dflash_kv), vp, i32, vp, vp, vp, vp, sz, vp]
     lib.dflash_kv_commit.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, i32, vp]
@@ -103,7 +108,7 @@ def load() -> C.CDLL:
     for fn in ("dflash_model_create", "dflash_rope_table", "dflash_fuse_ctx", "dflash_inject_kv",
                "dflash_draft_block", "dflash_verify_accept", "dflash_target_create",
                "dflash_target_forward", "dflash_kv_commit", "dflash_draft_block_sample",
-               "dflash_verify_sample", "dflash_sample_logits"):
+               "dflash_verify_sample", "dflash_sample_logits", "dflash_draft_block_noalloc"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -168,6 +173,11 @@ def dflash_inject_kv(model, ctx, n_ctx_rows, commit_rows, n_commit, max_commit, 
 def dflash_draft_block(model, kv, anchor, draft, dbg_logits, dbg_hidden, ws, ws_bytes, stream) -> None:
     _check("dflash_draft_block", load().dflash_draft_block(model, C.byref(kv), anchor, draft, dbg_logits,
                                                            dbg_hidden, ws, ws_bytes, stream))
+
+
+def dflash_draft_block_noalloc(model, kv, anchor, draft, dbg_logits, dbg_hidden, stream) -> None:
+    _check("dflash_draft_block_noalloc", load().dflash_draft_block_noalloc(model, C.byref(kv), anchor, draft,
+                                                                           dbg_logits, dbg_hidden, stream))
 
 
 def dflash_target_forward(model, kv, tokens, n, argmax, taps, dbg_logits, ws, ws_bytes, stream) -> None:

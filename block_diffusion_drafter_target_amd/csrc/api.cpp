@@ -36,12 +36,13 @@ struct Rec {
 uint32_t mask = 0;
 std::vector<Rec> recs;  // events are created once and reused
 size_t used = 0;
+thread_local bool suspended = false;  // set while a call that must not allocate runs
 
 struct Scope {
   Rec* r = nullptr;
   hipStream_t st;
   Scope(int phase, hipStream_t s) : st(s) {
-    if (!(mask >> phase & 1u)) return;
+    if (suspended || !(mask >> phase & 1u)) return;
     if (used == recs.size()) {
       Rec n{phase, nullptr, nullptr};
       if (hipEventCreate(&n.a) != hipSuccess || hipEventCreate(&n.b) != hipSuccess) return;
@@ -971,13 +972,22 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
 
 }  // namespace
 
-dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
-                                 int32_t* draft, float* dbg_logits, float* dbg_hidden, void* ws,
-                                 size_t ws_bytes, void* stream) {
-  if (!m || !anchor || !draft || !ws) return DFLASH_ERR_NULL;
+}  // extern "C"
+
+dflash_status dfl::draft_block_check(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                                     const int32_t* draft, size_t* ws_need) {
+  if (!m || !anchor || !draft) return DFLASH_ERR_NULL;
   if (m->target) return DFLASH_ERR_UNSUPPORTED;
   dflash_status ks = check_kv(m, kv);
   if (ks != DFLASH_OK) return ks;
+  const int B = m->cfg.block;
+  *ws_need = stack_ws(m->cfg, kv->batch, kv->max_ctx, B, B - 1).total;
+  return DFLASH_OK;
+}
+
+dflash_status dfl::draft_block_run(const dflash_model* m, dflash_kv* kv, const int32_t* anchor, int32_t* draft,
+                                   float* dbg_logits, float* dbg_hidden, void* ws, size_t ws_bytes, void* stream,
+                                   bool no_events) {
   StackIO io;
   io.anchor = anchor;
   io.B = m->cfg.block;
@@ -985,7 +995,24 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
   io.out = draft;
   io.dbg_logits = dbg_logits;
   io.dbg_hidden = dbg_hidden;
-  return run_stack(m, kv, io, ws, ws_bytes, stream);
+  const bool was = prof::suspended;
+  prof::suspended = was || no_events;
+  const dflash_status s = run_stack(m, kv, io, ws, ws_bytes, stream);
+  prof::suspended = was;
+  return s;
+}
+
+extern "C" {
+
+dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
+                                 int32_t* draft, float* dbg_logits, float* dbg_hidden, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  const dflash_status s = dfl::draft_block_check(m, kv, anchor, draft, &need);
+  if (s != DFLASH_OK) return s;
+  if (!ws) return DFLASH_ERR_NULL;
+  if (ws_bytes < need) return DFLASH_ERR_WORKSPACE;
+  return dfl::draft_block_run(m, kv, anchor, draft, dbg_logits, dbg_hidden, ws, ws_bytes, stream, false);
 }
 
 dflash_status dflash_draft_block_sample(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,

@@ -2,11 +2,23 @@
 // the C ABI implementation (api.cpp); not part of the public interface.
 #pragma once
 
+#include <dflash.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace dfl {
+
+// The draft-block pass of dflash_draft_block (api.cpp), shared with the
+// allocation-free entry point. draft_block_check runs every host-side check
+// and returns the workspace the pass needs through *ws_need; draft_block_run
+// enqueues the pass on a workspace of ws_bytes (no event timing when
+// no_events is set).
+dflash_status draft_block_check(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                                const int32_t* draft, size_t* ws_need);
+dflash_status draft_block_run(const dflash_model* m, dflash_kv* kv, const int32_t* anchor, int32_t* draft,
+                              float* dbg_logits, float* dbg_hidden, void* ws, size_t ws_bytes, void* stream,
+                              bool no_events);
 
 constexpr int kMaxZ = 16;       // weight matrices batched in one GEMM launch
 constexpr int kMaxLayers = 16;  // draft layers supported

@@ -143,6 +143,14 @@ class Drafter:
                               bd.ptr(dbg_hidden), bd.ptr(self.ws), self.ws_bytes, self.stream())
         return self.draft
 
+    def draft_block_noalloc(self, anchor=None, dbg_logits=None, dbg_hidden=None):
+        """The draft block on the library's static workspace (no workspace
+        argument; for callers that cannot allocate)."""
+        a = self.anchor if anchor is None else anchor
+        bd.dflash_draft_block_noalloc(self.model, self.kv, bd.ptr(a), bd.ptr(self.draft), bd.ptr(dbg_logits),
+                                      bd.ptr(dbg_hidden), self.stream())
+        return self.draft
+
     def draft_block_sample(self, temperature: float, seed: int, step: int, anchor=None, step_dev=None):
         """Sampling-mode draft block: tokens sampled from the drafter's own
         distributions (Gumbel-max, Philox draws of (seed, step)); the raw logits

@@ -195,6 +195,26 @@ dflash_status dflash_draft_block(const dflash_model* m, dflash_kv* kv, const int
                                  int32_t* draft, float* dbg_logits, float* dbg_hidden, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/* Allocation-free draft block, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same pass, arguments (without ws), outputs, cache effects and
+ * status rules as dflash_draft_block; the workspace is a static device array
+ * of DFLASH_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU that
+ * the library runs on, held until the process ends. The call uses the current
+ * device's copy (stream must belong to that device) and calls nothing that
+ * allocates (phase timing is skipped in it).
+ *   Returns DFLASH_ERR_WORKSPACE, before any HIP call, when the pass needs more
+ *   than DFLASH_NOALLOC_SCRATCH_BYTES (the draft-block part of
+ *   dflash_workspace_bytes for kv->batch and kv->max_ctx; for example a
+ *   Qwen3-8B-shaped drafter at batch 32 needs about 118 MiB).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (the pass reads only what it wrote in the same call, so nothing
+ * needs clearing). Calls that overlap on one GPU, from different streams or
+ * threads, race on the array: the caller must order them. */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dflash_status dflash_draft_block_noalloc(const dflash_model* m, dflash_kv* kv, const int32_t* anchor,
+                                         int32_t* draft, float* dbg_logits, float* dbg_hidden, void* stream);
+
 /* Sampling mode, draft side (temperature > 0). [P4 "Ejecutando DFlash": the
  * user call takes a temperature; P2 results: speed-ups are quoted under
  * sampling too] The pages give no sampling rule; the plain reading is standard

@@ -248,3 +248,35 @@ def test_sampling_entry_points_check_arguments_without_a_gpu():
         assert sl(h, P, 3, 1.0, 7, 0, 0, P, P, 8, None) == bd.DFLASH_ERR_WORKSPACE
     finally:
         bd.dflash_model_destroy(h)
+
+
+def test_noalloc_draft_block_checks_without_a_gpu():
+    """The allocation-free draft block runs the draft block's checks and
+    rejects a pass whose workspace exceeds its static array, all before any
+    HIP call."""
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    m = re.search(r"#define DFLASH_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == bd.NOALLOC_SCRATCH_BYTES
+    lib = bd.load()
+    w, keep = _fake_weights(5)
+    rc, h = _create(_cfg(), w)
+    assert rc == 0
+    try:
+        # Qwen3-8B-shaped drafter at batch 32 with 4096-key contexts: ~118 MiB
+        kv = bd.dflash_kv(k=0x1000, v=0x1000, batch=32, max_ctx=4096 + 64, ctx_len=0x1000, status=0x1000)
+        assert bd.dflash_workspace_bytes(h, 32, 4096 + 64, 1) > bd.NOALLOC_SCRATCH_BYTES
+        assert lib.dflash_draft_block_noalloc(h, C.byref(kv), 0x1000, 0x1000, None, None,
+                                              None) == bd.DFLASH_ERR_WORKSPACE
+        one = bd.dflash_kv(k=0x1000, v=0x1000, batch=1, max_ctx=2048, ctx_len=0x1000, status=0x1000)
+        assert bd.dflash_workspace_bytes(h, 1, 2048, 1) < bd.NOALLOC_SCRATCH_BYTES
+        assert lib.dflash_draft_block_noalloc(h, C.byref(one), None, 0x1000, None, None,
+                                              None) == bd.DFLASH_ERR_NULL
+        assert lib.dflash_draft_block_noalloc(h, C.byref(one), 0x1000, None, None, None,
+                                              None) == bd.DFLASH_ERR_NULL
+        assert lib.dflash_draft_block_noalloc(None, C.byref(one), 0x1000, 0x1000, None, None,
+                                              None) == bd.DFLASH_ERR_NULL
+        small = bd.dflash_kv(k=0x1000, v=0x1000, batch=1, max_ctx=8, ctx_len=0x1000, status=0x1000)
+        assert lib.dflash_draft_block_noalloc(h, C.byref(small), 0x1000, 0x1000, None, None,
+                                              None) == bd.DFLASH_ERR_SHAPE
+    finally:
+        bd.dflash_model_destroy(h)
