@@ -147,7 +147,10 @@ def target_verify(cfg, W, lens, args, dr):
         toks = torch.from_numpy(np.stack([synth.make_prompt(cfg, n, seed=1000 + 7 * b + i0)
                                           for b in range(batch)]).astype(np.int32)).to(dev)
         tgt.pass_tokens(toks)
-        tgt.ctx_len.copy_(torch.minimum(tgt.ctx_len + n, torch.from_numpy(lens.astype(np.int32)).to(dev)))
+        rows = [(b * n + j, b, i0 + j) for b in range(batch) for j in range(n) if i0 + j < int(lens[b])]
+        if rows:
+            tgt.commit(torch.tensor(rows, dtype=torch.int32, device=dev),
+                       torch.tensor([len(rows)], dtype=torch.int32, device=dev), len(rows))
     torch.cuda.synchronize()
     assert tgt.ctx_len.cpu().numpy().tolist() == lens.tolist()
     toks = torch.from_numpy(np.stack([synth.make_prompt(cfg, B, seed=5000 + b) for b in range(batch)])

@@ -26,7 +26,7 @@ EXPORTED = ("dflash_model_create", "dflash_model_destroy", "dflash_rope_table",
             "dflash_profile_enable", "dflash_profile_read", "dflash_pack_matrix",
             "dflash_target_create", "dflash_target_forward", "dflash_kv_commit",
             "dflash_draft_block_sample", "dflash_verify_sample", "dflash_sample_logits",
-            "dflash_draft_block_noalloc")
+            "dflash_draft_block_noalloc", "dflash_loop_tokens", "dflash_loop_advance")
 
 # bytes of the static device workspace behind dflash_draft_block_noalloc
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -87,6 +87,8 @@ def load() -> C.CDLL:
     lib.dflash_inject_kv.argtypes = [vp, vp, i32, vp, vp, i32, C.POINTER(dflash_kv), vp, sz, vp]
     lib.dflash_draft_block.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp, vp, sz, vp]
     lib.dflash_draft_block_noalloc.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp, vp]
+    lib.dflash_loop_tokens.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp]
+    lib.dflash_loop_advance.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.dflash_target_create.argtypes = [C.POINTER(dflash_config), C.POINTER(dflash_weights), vp, C.POINTER(vp)]
     lib.dflash_target_forward.argtypes = [vp, C.POINTER(dflash_kv), vp, i32, vp, vp, vp, vp, sz, vp]
     lib.dflash_kv_commit.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, i32, vp]
@@ -108,7 +110,8 @@ def load() -> C.CDLL:
     for fn in ("dflash_model_create", "dflash_rope_table", "dflash_fuse_ctx", "dflash_inject_kv",
                "dflash_draft_block", "dflash_verify_accept", "dflash_target_create",
                "dflash_target_forward", "dflash_kv_commit", "dflash_draft_block_sample",
-               "dflash_verify_sample", "dflash_sample_logits", "dflash_draft_block_noalloc"):
+               "dflash_verify_sample", "dflash_sample_logits", "dflash_draft_block_noalloc",
+               "dflash_loop_tokens", "dflash_loop_advance"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -178,6 +181,17 @@ def dflash_draft_block(model, kv, anchor, draft, dbg_logits, dbg_hidden, ws, ws_
 def dflash_draft_block_noalloc(model, kv, anchor, draft, dbg_logits, dbg_hidden, stream) -> None:
     _check("dflash_draft_block_noalloc", load().dflash_draft_block_noalloc(model, C.byref(kv), anchor, draft,
                                                                            dbg_logits, dbg_hidden, stream))
+
+
+def dflash_loop_tokens(model, kv, anchor, draft, tokens, stream) -> None:
+    _check("dflash_loop_tokens", load().dflash_loop_tokens(model, C.byref(kv), anchor, draft, tokens, stream))
+
+
+def dflash_loop_advance(model, kv, anchor_out, emitted, n_emit, done, out, ld_out: int, max_new: int, cursor,
+                        alive, anchor, step_dev, stream) -> None:
+    _check("dflash_loop_advance", load().dflash_loop_advance(model, C.byref(kv), anchor_out, emitted, n_emit, done,
+                                                             out, ld_out, max_new, cursor, alive, anchor, step_dev,
+                                                             stream))
 
 
 def dflash_target_forward(model, kv, tokens, n, argmax, taps, dbg_logits, ws, ws_bytes, stream) -> None:

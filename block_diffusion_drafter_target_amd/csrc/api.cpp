@@ -1122,6 +1122,42 @@ dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,
   return hip_status(dfl::launch_verify(p, as_stream(stream)));
 }
 
+dflash_status dflash_loop_tokens(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                                 const int32_t* draft, int32_t* tokens, void* stream) {
+  if (!m || !anchor || !draft || !tokens) return DFLASH_ERR_NULL;
+  if (m->target) return DFLASH_ERR_UNSUPPORTED;
+  const dflash_status ks = check_kv(m, kv);
+  if (ks != DFLASH_OK) return ks;
+  return hip_status(dfl::launch_loop_tokens(anchor, draft, tokens, kv->batch, m->cfg.block, as_stream(stream)));
+}
+
+dflash_status dflash_loop_advance(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor_out,
+                                  const int32_t* emitted, const int32_t* n_emit, const int32_t* done, int32_t* out,
+                                  int32_t ld_out, int32_t max_new, int32_t* cursor, int32_t* alive,
+                                  int32_t* anchor, int32_t* step_dev, void* stream) {
+  if (!m || !anchor_out || !emitted || !n_emit || !done || !out || !cursor || !alive || !anchor)
+    return DFLASH_ERR_NULL;
+  if (m->target) return DFLASH_ERR_UNSUPPORTED;
+  const dflash_status ks = check_kv(m, kv);
+  if (ks != DFLASH_OK) return ks;
+  if (max_new < 0 || ld_out < max_new) return DFLASH_ERR_SHAPE;
+  dfl::LoopAdvanceParams p;
+  p.anchor_out = anchor_out;
+  p.emitted = emitted;
+  p.n_emit = n_emit;
+  p.done = done;
+  p.out = out;
+  p.ld_out = ld_out;
+  p.max_new = max_new;
+  p.cursor = cursor;
+  p.alive = alive;
+  p.anchor = anchor;
+  p.step_dev = step_dev;
+  p.batch = kv->batch;
+  p.B = m->cfg.block;
+  return hip_status(dfl::launch_loop_advance(p, as_stream(stream)));
+}
+
 dflash_status dflash_sample_logits(const dflash_model* m, const float* logits, int32_t rows, float temperature,
                                    uint64_t seed, int32_t step, int32_t row0, int32_t* tokens, void* ws,
                                    size_t ws_bytes, void* stream) {

@@ -218,6 +218,30 @@ hipError_t launch_argmax_finish(const unsigned long long* keys, int n_tiles, con
 hipError_t launch_kv_commit(const int32_t* commit_rows, const int32_t* n_commit, int max_commit, int batch,
                             int max_ctx, int32_t* ctx_len, hipStream_t st);
 
+// On-device loop (loop.hip). tokens[b] = [anchor[b], draft[b][0..B-2]].
+hipError_t launch_loop_tokens(const int32_t* anchor, const int32_t* draft, int32_t* tokens, int batch, int B,
+                              hipStream_t st);
+
+// End of a loop step, per sequence b: while alive[b], the first n_emit[b]
+// emitted tokens go to out[b][cursor[b] + i] (positions below max_new only)
+// and cursor[b] += n_emit[b]; alive[b] drops once done[b] is set; anchor[b] =
+// anchor_out[b]; *step_dev += 1 when step_dev is not NULL.
+struct LoopAdvanceParams {
+  const int32_t* anchor_out;
+  const int32_t* emitted;  // [batch, B]
+  const int32_t* n_emit;
+  const int32_t* done;
+  int32_t* out;            // [batch, ld_out]
+  long long ld_out;
+  int max_new;
+  int32_t* cursor;
+  int32_t* alive;
+  int32_t* anchor;
+  int32_t* step_dev;
+  int batch, B;
+};
+hipError_t launch_loop_advance(const LoopAdvanceParams& p, hipStream_t st);
+
 struct VerifyParams {
   const int32_t* draft;
   const int32_t* target;

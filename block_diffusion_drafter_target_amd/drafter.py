@@ -192,6 +192,22 @@ class Drafter:
                                 int(row0), bd.ptr(out), bd.ptr(self.ws), self.ws_bytes, self.stream())
         return out
 
+    def loop_tokens(self, tokens, anchor=None, draft=None):
+        """tokens [batch, B] = [anchor, draft] (the target's input of a loop step)."""
+        a = self.anchor if anchor is None else anchor
+        d = self.draft if draft is None else draft
+        bd.dflash_loop_tokens(self.model, self.kv, bd.ptr(a), bd.ptr(d), bd.ptr(tokens), self.stream())
+        return tokens
+
+    def loop_advance(self, out, max_new: int, cursor, alive, step_dev=None):
+        """End of a loop step: the emitted tokens of running sequences appended
+        to out [batch, ld] at cursor, cursor/alive/anchor advanced, step_dev
+        incremented (sampling mode)."""
+        bd.dflash_loop_advance(self.model, self.kv, bd.ptr(self.anchor_out), bd.ptr(self.emitted),
+                               bd.ptr(self.n_emit), bd.ptr(self.done), bd.ptr(out), out.shape[1], max_new,
+                               bd.ptr(cursor), bd.ptr(alive), bd.ptr(self.anchor), bd.ptr(step_dev),
+                               self.stream())
+
     def verify_accept(self, target_argmax, stop_ids=None, budget=None, draft=None):
         d = self.draft if draft is None else draft
         n_stop = 0 if stop_ids is None else int(stop_ids.numel())
@@ -296,32 +312,46 @@ class DeviceTarget:
                             Drafter.stream())
 
     # -- loop protocol (batch 1) ---------------------------------------------
+    # The host-driven loop knows the committed length; a pass's rows are kept
+    # with dflash_kv_commit, and a truncation (rollback) writes the length the
+    # loop decided.
     def reset(self) -> None:
+        self._len = 0
         self.ctx_len.zero_()
         self.status.zero_()
 
     def forward(self, tokens: Sequence[int], logits: bool = False):
-        """Append tokens (in passes of up to max_n); returns (argmax as numpy
-        [n], taps as a device bf16 tensor [n, n_tap*H]), and with logits=True
-        also the fp32 logits of the last pass's rows (device [rows, V])."""
+        """Append tokens (in passes of up to max_n, each committed); returns
+        (argmax as numpy [n], taps as a device bf16 tensor [n, n_tap*H]), and
+        with logits=True also the fp32 logits of the last pass's rows (device
+        [rows, V])."""
         torch = _torch()
+        if self.batch != 1:
+            raise ValueError("the loop protocol drives one sequence")
         toks = torch.tensor(list(tokens), dtype=torch.int32, device=self.device)
         outs, taps = [], []
         z = None
+        L = getattr(self, "_len", 0)
         for i in range(0, len(toks), self.max_n):
             part = toks[i:i + self.max_n][None, :]
+            n = part.shape[1]
             if logits:
-                z = torch.empty((part.shape[1], self.cfg.vocab), dtype=torch.float32, device=self.device)
+                z = torch.empty((n, self.cfg.vocab), dtype=torch.float32, device=self.device)
             a, t = self.pass_tokens(part, dbg_logits=z)
             outs.append(a[0].clone())
             taps.append(t.clone())
-            self.ctx_len += part.shape[1]
+            rows = torch.tensor([[j, 0, L + j] for j in range(n)], dtype=torch.int32, device=self.device)
+            self.commit(rows, torch.tensor([n], dtype=torch.int32, device=self.device), n)
+            L += n
+        self._len = L
         if logits:
             return torch.cat(outs).cpu().numpy(), torch.cat(taps), z
         return torch.cat(outs).cpu().numpy(), torch.cat(taps)
 
     def truncate(self, length: int) -> None:
-        self.ctx_len.fill_(length)
+        torch = _torch()
+        self._len = int(length)
+        self.ctx_len.copy_(torch.tensor([self._len], dtype=torch.int32))
 
 
 class Target(Protocol):
@@ -453,12 +483,10 @@ class _LoopState:
     def __init__(self, torch, batch, B, max_new, dev, stops, temperature=0.0, seed=0, vocab=0):
         i32 = dict(dtype=torch.int32, device=dev)
         self.tokens = torch.zeros((batch, B), **i32)       # target input [anchor, d_1..d_{B-1}]
-        self.out = torch.full((batch, max_new + 1), -1, **i32)  # last column: sink of unused lanes
+        self.out = torch.full((batch, max(1, max_new)), -1, **i32)
         self.cursor = torch.zeros(batch, **i32)
         self.alive = torch.ones(batch, **i32)
         self.budget = torch.zeros(batch, **i32)
-        self.lane = torch.arange(B, **i32)[None, :]
-        self.row = (torch.arange(batch, **i32) * (max_new + 1))[:, None]
         self.stops = stops
         self.max_new = max_new
         self.temperature, self.seed = float(temperature), int(seed)
@@ -510,12 +538,13 @@ def _prefill_device(drafter: Drafter, target: DeviceTarget, prompts, st: _LoopSt
 
 
 def device_step(drafter: Drafter, target: DeviceTarget, st: _LoopState) -> None:
-    """One speculative step with no host synchronisation: draft, target pass
-    over [anchor, draft], verify, commit in both caches, next anchor, and the
-    emitted tokens of sequences still running appended to the output. In
-    sampling mode the block is sampled, the target pass keeps its logits, the
-    verify is speculative sampling, and the device step counter advances."""
-    torch = _torch()
+    """One speculative step with no host synchronisation, every part a library
+    call: draft, the target's input row, target pass over [anchor, draft],
+    verify, commit in both caches, fuse and inject of the accepted rows' taps,
+    and the advance (emitted tokens of sequences still running appended to the
+    output, cursors, running flags, next anchors). In sampling mode the block
+    is sampled, the target pass keeps its logits, the verify is speculative
+    sampling, and the advance also moves the device step counter."""
     B = drafter.cfg.block
     batch = drafter.batch
     sampling = st.temperature > 0.0
@@ -523,26 +552,16 @@ def device_step(drafter: Drafter, target: DeviceTarget, st: _LoopState) -> None:
         drafter.draft_block_sample(st.temperature, st.seed, 0, anchor=drafter.anchor, step_dev=st.step)
     else:
         drafter.draft_block(anchor=drafter.anchor)
-    st.tokens[:, 0].copy_(drafter.anchor)
-    st.tokens[:, 1:].copy_(drafter.draft)
+    drafter.loop_tokens(st.tokens)
     a, taps = target.pass_tokens(st.tokens, dbg_logits=st.zt if sampling else None)
     if sampling:
         drafter.verify_sample(st.zt, st.temperature, st.seed, 0, st.stops, st.budget, step_dev=st.step)
-        st.step += 1
     else:
         drafter.verify_accept(a, st.stops, st.budget)
     target.commit(drafter.commit_rows, drafter.n_commit, batch * B)
     drafter.fuse_ctx(taps, batch * B, drafter.ctx)
     drafter.inject_kv(drafter.ctx, batch * B, drafter.commit_rows, drafter.n_commit, batch * B)
-    drafter.anchor.copy_(drafter.anchor_out)
-    n = drafter.n_emit * st.alive
-    pos = st.cursor[:, None] + st.lane
-    keep = (st.lane < n[:, None]) & (pos < st.max_new)
-    # kept lanes write distinct slots; every other lane writes the sink column
-    idx = (st.row + torch.where(keep, pos, st.max_new)).reshape(-1)
-    st.out.view(-1).scatter_(0, idx, drafter.emitted.reshape(-1))
-    st.cursor += n
-    st.alive *= 1 - drafter.done
+    drafter.loop_advance(st.out, st.max_new, st.cursor, st.alive, step_dev=st.step if sampling else None)
 
 
 def spec_generate_device(drafter: Drafter, target: DeviceTarget, prompts, max_new_tokens: int,

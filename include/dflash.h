@@ -347,6 +347,35 @@ dflash_status dflash_target_forward(const dflash_model* m, dflash_kv* kv, const 
 dflash_status dflash_kv_commit(const dflash_model* m, dflash_kv* kv, const int32_t* commit_rows,
                                const int32_t* n_commit, int32_t max_commit, void* stream);
 
+/* On-device speculative loop: the two steps of the greedy loop that are
+ * neither drafting, verification nor commit, so that a whole step (draft
+ * block, target pass, verify, commits, fuse, inject, advance) runs without
+ * host synchronisation and can be captured in a graph. [P4 "Ejecutando
+ * DFlash": the user call generates up to a token budget with stop ids; P2
+ * introduction: the target checks the drafted block and the longest valid
+ * prefix is kept]
+ *
+ * dflash_loop_tokens: the target's input row of the step,
+ *   tokens[b][0] = anchor[b], tokens[b][j] = draft[b][j-1] for 1 <= j < B
+ *   anchor device int32 [batch]; draft device int32 [batch, B-1];
+ *   tokens device int32 [batch, B] out. */
+dflash_status dflash_loop_tokens(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
+                                 const int32_t* draft, int32_t* tokens, void* stream);
+
+/* dflash_loop_advance: the end of a step, from dflash_verify_accept's (or
+ * dflash_verify_sample's) outputs. For each sequence b with alive[b] != 0:
+ *   out[b][cursor[b] + i] = emitted[b][i] for i < n_emit[b] and
+ *   cursor[b] + i < max_new; cursor[b] += n_emit[b]; alive[b] = 0 once done[b];
+ * for every sequence anchor[b] = anchor_out[b]; and *step_dev += 1 when
+ * step_dev is not NULL (the step counter of the sampling mode's draws).
+ *   out     device int32 [batch, ld_out], ld_out >= max_new >= 0
+ *   cursor, alive, anchor  device int32 [batch], in/out
+ * A sequence that is not alive is left as it is (cursor, output, flag). */
+dflash_status dflash_loop_advance(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor_out,
+                                  const int32_t* emitted, const int32_t* n_emit, const int32_t* done, int32_t* out,
+                                  int32_t ld_out, int32_t max_new, int32_t* cursor, int32_t* alive,
+                                  int32_t* anchor, int32_t* step_dev, void* stream);
+
 /* Kernel timing for benchmarks. dflash_profile_enable(mask) times the phases
  * whose bit (1 << phase) is set in mask (0 switches timing off): every launch
  * of such a phase is bracketed by two HIP events recorded on the call's

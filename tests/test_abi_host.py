@@ -280,3 +280,26 @@ def test_noalloc_draft_block_checks_without_a_gpu():
                                               None) == bd.DFLASH_ERR_SHAPE
     finally:
         bd.dflash_model_destroy(h)
+
+
+def test_loop_entry_points_check_arguments_without_a_gpu():
+    lib = bd.load()
+    w, keep = _fake_weights(5)
+    rc, h = _create(_cfg(), w)
+    assert rc == 0
+    try:
+        kv = bd.dflash_kv(k=0x1000, v=0x1000, batch=2, max_ctx=2048, ctx_len=0x1000, status=0x1000)
+        p = 0x1000
+        assert lib.dflash_loop_tokens(h, C.byref(kv), None, p, p, None) == bd.DFLASH_ERR_NULL
+        assert lib.dflash_loop_tokens(h, C.byref(kv), p, p, None, None) == bd.DFLASH_ERR_NULL
+        bad = bd.dflash_kv(k=0x1000, v=0x1000, batch=0, max_ctx=2048, ctx_len=0x1000, status=0x1000)
+        assert lib.dflash_loop_tokens(h, C.byref(bad), p, p, p, None) == bd.DFLASH_ERR_SHAPE
+        # out row stride below the token budget; negative budget; missing cursor
+        assert lib.dflash_loop_advance(h, C.byref(kv), p, p, p, p, p, 10, 11, p, p, p, None,
+                                       None) == bd.DFLASH_ERR_SHAPE
+        assert lib.dflash_loop_advance(h, C.byref(kv), p, p, p, p, p, 10, -1, p, p, p, None,
+                                       None) == bd.DFLASH_ERR_SHAPE
+        assert lib.dflash_loop_advance(h, C.byref(kv), p, p, p, p, p, 10, 10, None, p, p, None,
+                                       None) == bd.DFLASH_ERR_NULL
+    finally:
+        bd.dflash_model_destroy(h)
