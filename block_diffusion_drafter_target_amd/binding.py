@@ -10,7 +10,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdflash.so")
+# DFLASH_LIB selects another build of the library (the sanitized one of the
+# CPU tests); by default the in-tree libdflash.so
+LIB_PATH = os.environ.get("DFLASH_LIB") or os.path.join(HERE, "libdflash.so")
 
 DFLASH_OK = 0
 DFLASH_ERR_NULL = -1

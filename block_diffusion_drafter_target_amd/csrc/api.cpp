@@ -637,6 +637,8 @@ dflash_status dflash_inject_kv(const dflash_model* m, const void* ctx, int32_t n
   if (!ctx || !commit_rows || !n_commit || !ws) return DFLASH_ERR_NULL;
   if (n_ctx_rows == 0) return DFLASH_ERR_SHAPE;
   if (m->target) return DFLASH_ERR_UNSUPPORTED;
+  // gathered context rows are addressed with 32-bit element offsets
+  if ((long long)n_ctx_rows * m->cfg.hidden > 0x7FFFFFFFll) return DFLASH_ERR_UNSUPPORTED;
   dflash_status ks = check_kv(m, kv);
   if (ks != DFLASH_OK) return ks;
   const dflash_config& c = m->cfg;

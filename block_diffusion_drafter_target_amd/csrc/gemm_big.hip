@@ -58,20 +58,6 @@ struct BigShape {
   static constexpr int kThreads = 64 * WAVES;
 };
 
-// Workgroup barrier for LDS data published by direct loads. The barrier
-// intrinsic alone does not order memory accesses in the compiler, so LDS
-// reads could be hoisted above it; the empty asm with a memory clobber keeps
-// every memory access on its side, and the scheduling barriers keep the
-// machine scheduler from moving instructions across. No s_waitcnt comes with
-// it: each wave waits for its own direct loads (vmcnt) before calling it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 template <int MODE, int WAVES>
 __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
   using S = BigShape<WAVES>;
@@ -333,6 +319,9 @@ hipError_t launch_gemm_big(const GemmParams& p, int mode, int nz, hipStream_t st
     return hipErrorInvalidValue;
   if (mode == kGemmSwiglu && p.splits != 1) return hipErrorInvalidValue;
   if (mode == kGemmArgmax && p.splits != 1) return hipErrorInvalidValue;
+  // the kernel addresses activation rows with 32-bit element offsets from p.A
+  const long long rows = p.a_idx ? p.a_idx_max : p.M;
+  if ((rows - 1) * p.lda + p.K > 0x7FFFFFFFll) return hipErrorInvalidValue;
   const long long m_tiles = (p.M + kBM - 1) / kBM;
   const long long n_tiles = (p.N + gemm_big_cols(mode) - 1) / gemm_big_cols(mode);
   const long long total = m_tiles * n_tiles * p.splits * nz;

@@ -171,7 +171,8 @@ dflash_status dflash_fuse_ctx(const dflash_model* m, const void* taps, int32_t n
  *   commit_rows  device int32 [max_commit, 3]
  *   n_commit     device int32 [1], clamped to [0, max_commit]
  * A row with src, seq or pos out of range is skipped; out-of-range pos also
- * sets status[seq] = DFLASH_ERR_CAPACITY. */
+ * sets status[seq] = DFLASH_ERR_CAPACITY. n_ctx_rows * H above 2^31 - 1
+ * returns DFLASH_ERR_UNSUPPORTED (rows are addressed with 32-bit offsets). */
 dflash_status dflash_inject_kv(const dflash_model* m, const void* ctx, int32_t n_ctx_rows,
                                const int32_t* commit_rows, const int32_t* n_commit,
                                int32_t max_commit, dflash_kv* kv, void* ws, size_t ws_bytes,

@@ -27,6 +27,13 @@ def test_header_declares_the_step_calls():
     assert set(names) == set(bd.EXPORTED)
 
 
+def test_loaded_library_is_the_selected_build():
+    lib = bd.load()
+    assert os.path.realpath(lib._name) == os.path.realpath(bd.LIB_PATH)
+    if os.environ.get("DFLASH_LIB"):  # the sanitized build: its runtime is in the process
+        assert hasattr(C.CDLL(None), "__asan_init")
+
+
 def test_library_exports_every_declared_symbol():
     lib = bd.load()
     for n in declared_functions():
@@ -121,6 +128,9 @@ def test_calls_reject_bad_arguments_without_a_gpu():
                                     None) == bd.DFLASH_ERR_NULL
         assert lib.dflash_inject_kv(h, 0x1000, 16, 0x1000, 0x1000, 16, C.byref(kv), 0x1000, 16,
                                     None) == bd.DFLASH_ERR_WORKSPACE
+        # context rows beyond 32-bit element offsets (2^31 / 4096 rows)
+        assert lib.dflash_inject_kv(h, 0x1000, (1 << 31) // 4096 + 1, 0x1000, 0x1000, 16, C.byref(kv), 0x1000,
+                                    1 << 30, None) == bd.DFLASH_ERR_UNSUPPORTED
         # verify: negative stop count, stop ids missing
         args = [0x1000] * 2
         outs = [0x1000] * 7
