@@ -219,10 +219,11 @@ def target_verify(cfg, W, lens, args, dr):
     return res
 
 
-def cpu_baseline(cfg, W, L, repeats: int, seconds: float):
+def cpu_baseline(cfg, W, L, repeats: int, seconds: float, threads: int | None = None):
     """The fp64 oracle's draft step on the host cores: steps repeated until at
-    least `repeats` of them and `seconds` of timed work have run; the median."""
-    from threadpoolctl import threadpool_info
+    least `repeats` of them and `seconds` of timed work have run; the median.
+    threads: BLAS threads (None: the library's default, one per core)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from block_diffusion_drafter_target_amd import synth
     from oracle import ref
@@ -238,17 +239,18 @@ def cpu_baseline(cfg, W, L, repeats: int, seconds: float):
     taps = synth.bf16_to_f64(synth.make_taps(cfg, batch * B, tid=999))
     anchor = synth.make_anchors(cfg)
     times = []
-    t_all = time.perf_counter()
-    while len(times) < repeats or (time.perf_counter() - t_all < seconds and len(times) < 10000):
-        t = time.perf_counter()
-        ctx = ref.fuse_ctx(ocfg, WO, taps)
-        ref.inject_kv(ocfg, WO, ctx, [(b * B + i, b, L - B + i) for b in range(batch) for i in range(B)], cache)
-        r = ref.draft_block(ocfg, WO, cache, [L] * batch, anchor)
-        tgt = np.concatenate([r["draft"], np.zeros((batch, 1), np.int64)], axis=1)
-        ref.verify_accept(r["draft"], tgt, [L] * batch)
-        times.append(time.perf_counter() - t)
-    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-    cores = int(blas[0]["num_threads"]) if blas else (os.cpu_count() or 1)
+    with threadpool_limits(limits=threads, user_api="blas"):
+        t_all = time.perf_counter()
+        while len(times) < repeats or (time.perf_counter() - t_all < seconds and len(times) < 10000):
+            t = time.perf_counter()
+            ctx = ref.fuse_ctx(ocfg, WO, taps)
+            ref.inject_kv(ocfg, WO, ctx, [(b * B + i, b, L - B + i) for b in range(batch) for i in range(B)], cache)
+            r = ref.draft_block(ocfg, WO, cache, [L] * batch, anchor)
+            tgt = np.concatenate([r["draft"], np.zeros((batch, 1), np.int64)], axis=1)
+            ref.verify_accept(r["draft"], tgt, [L] * batch)
+            times.append(time.perf_counter() - t)
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = int(blas[0]["num_threads"]) if blas else (os.cpu_count() or 1)
     t_step = float(np.median(times))
     return {"value": batch * (B - 1) / t_step, "unit": "drafted tokens/s", "cores": cores,
             "kind": "oracle",
@@ -257,6 +259,46 @@ def cpu_baseline(cfg, W, L, repeats: int, seconds: float):
                        f"({sum(times):.1f} s of timed work); step {t_step * 1e3:.0f} ms; weight upcast to "
                        f"fp64 ({prep:.1f} s) not timed"),
             "ms_per_step": t_step * 1e3}
+
+
+def phase_roofline(cfg, phases, ctx0, ctx1):
+    """Achieved fraction of the MI355X roofline of every timed phase of the
+    step, from its per-step time (library HIP events, breakdown steps) and its
+    algorithmic work: weight bytes (HBM) and GEMM flops (MFMA) of the GEMMs,
+    K/V bytes of the attention (at the breakdown steps' mean context)."""
+    B, batch, NL, H = cfg.block, cfg.batch, cfg.n_layers, cfg.hidden
+    I, V, D, Hkv = cfg.intermediate, cfg.vocab, cfg.head_dim, cfg.n_kv_heads
+    Mb, Ml = batch * B, batch * (B - 1)
+    gemms = {  # name: (weight bytes, activation rows) per step
+        "qkv": (NL * 2 * cfg.qkv_width * H, Mb), "o": (NL * 2 * H * cfg.q_width, Mb),
+        "gate_up": (NL * 2 * 2 * I * H, Mb), "down": (NL * 2 * H * I, Mb), "lm_head": (2 * V * H, Ml),
+        "fuse": (2 * H * cfg.tap_width, Mb), "inject": (NL * 2 * 2 * cfg.kv_width * H, Mb)}
+    out = {}
+    tot_b = tot_us = 0.0
+    for name, (wb, rows) in gemms.items():
+        if name not in phases:
+            continue
+        us = phases[name]["us_per_step"]
+        flops = rows * wb  # 2 flops per weight (2 bytes) and activation row
+        out[name] = {"us_per_step": us, "weight_bytes": wb, "GBps": round(wb / us * 1e-3, 1),
+                     "hbm_frac": round(wb / us * 1e-3 / HBM_PEAK_GBS, 4),
+                     "tflops": round(flops / us * 1e-6, 1),
+                     "mfma_frac": round(flops / us * 1e-6 / MFMA_PEAK_TFLOPS, 4)}
+        tot_b += wb
+        tot_us += us
+    if tot_us:
+        out["weight_gemms"] = {"us_per_step": round(tot_us, 2), "weight_bytes": int(tot_b),
+                               "GBps": round(tot_b / tot_us * 1e-3, 1),
+                               "hbm_frac": round(tot_b / tot_us * 1e-3 / HBM_PEAK_GBS, 4)}
+    keys = float(np.mean((ctx0 + ctx1) / 2.0 + B)) * batch  # keys read per kv head and layer
+    kv_bytes = keys * Hkv * D * 2 * 2 * NL
+    for name, parts in (("attention", ("attention",)), ("attention_with_merge", ("attention", "merge"))):
+        if all(p in phases for p in parts):
+            us = sum(phases[p]["us_per_step"] for p in parts)
+            out[name] = {"us_per_step": round(us, 2), "kv_bytes": int(kv_bytes),
+                         "GBps": round(kv_bytes / us * 1e-3, 1),
+                         "hbm_frac": round(kv_bytes / us * 1e-3 / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def main():
@@ -279,6 +321,10 @@ def main():
                     help="also time the step in sampling mode at this temperature")
     ap.add_argument("--graph", action="store_true",
                     help="also time the same steps captured in one HIP graph")
+    ap.add_argument("--evict-mb", type=int, default=0,
+                    help="also time steps one by one with this many MiB written between them (outside "
+                         "each step's events), so that no step finds the previous one's data in the "
+                         "256 MB Infinity Cache")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py measures one GPU; runs on several GPUs are not implemented",
@@ -383,6 +429,31 @@ def main():
     # the replay accepted exactly the recorded prefix lengths
     assert dr.accept_len.cpu().numpy().tolist() == m_all[args.warmup + args.steps].cpu().numpy().tolist()
 
+    cold = None
+    if args.evict_mb:
+        # the same timed steps again from the same state, each bracketed by its
+        # own events, with a scratch write of evict_mb MiB between steps
+        end_state = {k: getattr(dr, k).clone() for k in ("ctx_len", "anchor_out", "commit_rows", "n_commit")}
+        for k, v in after_warmup.items():
+            getattr(dr, k).copy_(v)
+        scratch = torch.empty(args.evict_mb << 20, dtype=torch.uint8, device=dev)
+        ea = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        eb = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            scratch.fill_(i & 255)
+            ea[i].record()
+            step(targets[1 + args.warmup + i])
+            eb[i].record()
+        torch.cuda.synchronize()
+        cold_us = np.array([1e3 * ea[i].elapsed_time(eb[i]) for i in range(args.steps)])
+        for k, v in end_state.items():
+            assert torch.equal(getattr(dr, k), v), f"the cold-cache replay diverged ({k})"
+        del scratch
+        cold = {"evict_mb": args.evict_mb, "us_per_step_median": round(float(np.median(cold_us)), 1),
+                "us_per_step_mean": round(float(cold_us.mean()), 1),
+                "drafted_tokens_per_s": round(batch * (B - 1) / (float(np.median(cold_us)) * 1e-6), 1)}
+
     graph_ms = None
     if args.graph:
         # the same timed steps, launched as one captured graph from the same state
@@ -410,10 +481,12 @@ def main():
     if args.temperature > 0:
         sampling = sampling_steps(torch, dr, cfg, args, taps_step, after_warmup)
 
+    ctx_break0 = dr.ctx_len.cpu().numpy().astype(np.int64)
     bd.dflash_profile_enable(list(bd.PHASES))
     for i in range(n_break):
         step(targets[1 + args.warmup + args.steps + i])
     torch.cuda.synchronize()
+    ctx_break1 = dr.ctx_len.cpu().numpy().astype(np.int64)
     phases = {}
     for name in bd.PHASES:
         t, n = bd.dflash_profile_read(name)
@@ -474,15 +547,21 @@ def main():
                    "mfma_frac": round(ingest_flop / (ingest_ms * 1e-3) * 1e-12 / MFMA_PEAK_TFLOPS, 4),
                    "note": "fuse + inject of every context row (GEMM flops), second pass timed"},
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "cold_cache": cold,
         "sampling": sampling,
         "phases": phases,
+        "phase_roofline": phase_roofline(cfg, phases, ctx_break0, ctx_break1),
     }
     if args.target_verify:
         out["target_verify"] = target_verify(cfg, W, lens, args, dr)
     del dr
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
-        out["cpu_baseline"] = cpu_baseline(cfg, W, int(lens.max()), args.cpu_repeats, args.cpu_seconds)
+        cb = cpu_baseline(cfg, W, int(lens.max()), args.cpu_repeats, args.cpu_seconds)
+        # the same step on one BLAS thread: a bounded sample of a few steps
+        one = cpu_baseline(cfg, W, int(lens.max()), 2, min(6.0, args.cpu_seconds), threads=1)
+        cb["single_thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample", "ms_per_step")}
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 

@@ -34,7 +34,7 @@ EXPORTED = ("dflash_model_create", "dflash_model_destroy", "dflash_rope_table",
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 PHASES = {"lm_head": 0, "attention": 1, "qkv": 2, "o": 3, "gate_up": 4, "down": 5, "fuse": 6,
-          "inject": 7, "verify": 8}
+          "inject": 7, "verify": 8, "merge": 9}
 
 
 class dflash_config(C.Structure):

@@ -860,7 +860,11 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
     mp.plan = plan;
     mp.gb_pad = ap.gb_pad;
     mp.out = ao;
-    if ((e = dfl::launch_attn_merge(mp, st)) != hipSuccess) return DFLASH_ERR_HIP;
+    {
+      prof::Scope ps(DFLASH_PHASE_MERGE, st);
+      e = dfl::launch_attn_merge(mp, st);
+    }
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
     // o projection, residual, post-attention norm
     GemmCall go;
     go.A = ao;

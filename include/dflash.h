@@ -395,7 +395,8 @@ typedef enum dflash_phase {
   DFLASH_PHASE_FUSE = 6,      /* fusion GEMM (S1) */
   DFLASH_PHASE_INJECT = 7,    /* injection GEMM (S2) */
   DFLASH_PHASE_VERIFY = 8,    /* verify kernel (S11) */
-  DFLASH_N_PHASES = 9
+  DFLASH_PHASE_MERGE = 9,     /* log-sum-exp merge of the attention chunks (S6) */
+  DFLASH_N_PHASES = 10
 } dflash_phase;
 
 dflash_status dflash_profile_enable(uint32_t phase_mask);
