@@ -74,12 +74,16 @@ struct GemmPlan {
   int ng;      // tiled: weight row groups per wave (64*ng columns per workgroup); mt: 16-row tiles
   int splits, k_per_split;
   bool swiglu_split;  // SwiGLU as split-K partials over [gate; up] plus a combine pass
+  bool ws = false;    // tiled: the deep-prefetch kernel (gemm_ws.hip) instead of gemm_tile.hip
 };
 
 constexpr int kStreamMaxRows = 32;   // more rows take the tiled kernel
 constexpr int kBigMinRows = 256;     // this many rows take the large-tile kernel
 constexpr int kBigSlots = 256;       // large-tile workgroups resident at once (one per CU)
 constexpr int kSwigluMinWGs = 256;   // fewer single-pass SwiGLU workgroups: split-K path
+constexpr int kWsSlots = 256;        // deep-prefetch tiled workgroups per round (one per CU at 128 rows)
+constexpr int kWsSwigluMinWGs = 128; // single-pass SwiGLU workgroups from which that kernel takes it
+constexpr int kWsMinK = 8192;        // partial-mode K from which that kernel takes it
 
 // Kernel, tile shape and split-K for Y = A W^T.
 // From kBigMinRows rows: the large-tile kernel (256 x 256 tiles, both
@@ -129,6 +133,28 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
     g.nf = 0;
     g.mt = M <= 64 ? 4 : 8;
     const long long m_tiles = cdiv(M, 16 * g.mt);
+    const int slabs = (int)cdiv(K, 128);
+    // the deep-prefetch tiled kernel (gemm_ws.hip) for the single-pass SwiGLU
+    // with at least kWsSwigluMinWGs workgroups and for partial-mode products
+    // over long K: there it beats the other tiled kernel (c4: gate/up 67 ->
+    // 62 us, down 36 -> 34, fuse 51 -> 46 per launch); elsewhere (qkv, o, the
+    // LM head, the gpt-oss-shaped 64-row GEMMs) it measured equal or slower
+    g.ws = (mode == dfl::kGemmSwiglu && cdiv(N, 64) * m_tiles * nz >= kWsSwigluMinWGs) ||
+           (mode == dfl::kGemmPartial && K >= kWsMinK);
+    if (g.ws) {
+      g.ng = 2;
+      const long long n_tiles = mode == dfl::kGemmSwiglu ? cdiv(N, 64) : cdiv(N, 128);
+      const long long base = n_tiles * m_tiles * nz;
+      int s = 1;
+      if (mode == dfl::kGemmPartial) {  // at most one round of kWsSlots workgroups
+        s = (int)std::max<long long>(1, kWsSlots / base);
+        s = std::min(s, std::max(1, slabs / 2));  // at least two 128-k slabs per split
+      }
+      const int per = (int)cdiv(slabs, s);
+      g.splits = (int)cdiv(slabs, per);
+      g.k_per_split = per * 128;
+      return g;
+    }
     if (mode == dfl::kGemmSwiglu && cdiv(N, 64) * m_tiles * nz < kSwigluMinWGs) {
       GemmPlan p = plan_gemm(M, 2 * N, K, nz, dfl::kGemmPartial);
       p.swiglu_split = true;
@@ -137,7 +163,6 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
     g.ng = (mode == dfl::kGemmPartial && g.mt == 4) ? 1 : 2;
     const long long n_tiles = mode == dfl::kGemmSwiglu ? cdiv(N, 64) : cdiv(N, 64 * g.ng);
     const long long base = n_tiles * m_tiles * nz;
-    const int slabs = (int)cdiv(K, 128);
     int s = 1;
     if (mode == dfl::kGemmPartial) {
       const int target = m_tiles > 1 ? 512 : (g.mt == 4 ? 384 : 256);  // see above
@@ -263,7 +288,9 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     p.P = c.P;
     p.p_s_stride = (long long)c.M * c.N;
     p.p_z_stride = (long long)g.splits * c.M * c.N;
-    return g.big ? dfl::launch_gemm_big(p, c.mode, c.nz, st) : dfl::launch_gemm_tile(p, g.ng, g.mt, c.mode, c.nz, st);
+    if (g.big) return dfl::launch_gemm_big(p, c.mode, c.nz, st);
+    return g.ws ? dfl::launch_gemm_ws(p, g.ng, g.mt, c.mode, c.nz, st)
+                : dfl::launch_gemm_tile(p, g.ng, g.mt, c.mode, c.nz, st);
   }
   for (int m0 = 0; m0 < c.M; m0 += kGemmRows) {
     GemmParams p;

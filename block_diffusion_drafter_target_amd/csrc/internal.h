@@ -72,6 +72,10 @@ hipError_t launch_gemm_stream(const GemmParams& p, int mt, int nf, int mode, int
 // mt 16-row activation tiles per workgroup; (ng, mt) in {1, 2} x {4, 8}.
 hipError_t launch_gemm_tile(const GemmParams& p, int ng, int mt, int mode, int nz, hipStream_t st);
 
+// The same tiles with weights three slabs ahead of the MFMAs and activations
+// through registers into an LDS ring (gemm_ws.hip). (ng, mt) in {1, 2} x {4, 8}.
+hipError_t launch_gemm_ws(const GemmParams& p, int ng, int mt, int mode, int nz, hipStream_t st);
+
 // Large-tile variant for M >= 256 (256 x 256 tiles of 8 waves, both operands
 // staged through LDS by direct loads; K and k_per_split multiples of 32).
 // Argmax keys: one per gemm_big_cols(mode) columns; SwiGLU and argmax take
