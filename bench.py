@@ -36,17 +36,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# The sources the LM-head kernel compiles from; the PMC summary records their
-# hash, and a change to any of them voids its traffic figure.
-TRAFFIC_SOURCES = ("gemm_stream.hip", "internal.h", "common.h")
+# What the LM-head kernel compiles from: its source, the device helpers and,
+# of the launch header, the GEMM parameter block and modes. The PMC summary
+# records their hash, and a change to any of them voids its traffic figure.
+TRAFFIC_SOURCES = ("gemm_stream.hip", "common.h")
 
 
 def kernel_source_hash(root):
     import hashlib
+    import re
+    csrc = os.path.join(root, "block_diffusion_drafter_target_amd", "csrc")
     h = hashlib.sha256()
     for name in TRAFFIC_SOURCES:
-        with open(os.path.join(root, "block_diffusion_drafter_target_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    hdr = open(os.path.join(csrc, "internal.h")).read()
+    for pat in (r"struct GemmParams \{.*?\n\};", r"enum GemmMode \{[^}]*\};"):
+        m = re.search(pat, hdr, re.S)
+        h.update(m.group(0).encode() if m else b"?")
     return h.hexdigest()
 
 

@@ -34,10 +34,31 @@ def to_np_bf16(t) -> np.ndarray:
     return synth.bf16_to_f64(u)
 
 
-def check_rel(got, want, tol=TOL, what=""):
+def check_rel(got, want, tol=TOL, what="", axis=None, rows=False):
+    """max|got - want| / max|want| <= tol over the whole tensor, and, so that
+    an error confined to small-magnitude parts cannot hide under the largest
+    values, also over every slice along ``axis`` (e.g. each kv head of a cache
+    [n, Hkv, D]) and, with ``rows``, over every row (last axis: one row of
+    logits or of a hidden state). The slices are held to the stated 2e-2
+    (TOL) even where the whole tensor takes a tighter tolerance (stage
+    replays): a slice normalised by its own smaller maximum carries a larger
+    relative rounding error. Returns the largest of these errors."""
+    stol = max(tol, TOL)
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
     e = ref.rel_err(got, want)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     assert e <= tol, f"{what}: rel err {e:.3e} > {tol}"
+    if axis is not None:
+        for i in range(got.shape[axis]):
+            ei = ref.rel_err(np.take(got, i, axis=axis), np.take(want, i, axis=axis))
+            assert ei <= stol, f"{what}: slice {i} of axis {axis}: rel err {ei:.3e} > {stol}"
+            e = max(e, ei)
+    if rows and got.size:
+        g2, w2 = got.reshape(-1, got.shape[-1]), want.reshape(-1, want.shape[-1])
+        for i in range(len(g2)):
+            ei = ref.rel_err(g2[i], w2[i])
+            assert ei <= stol, f"{what}: row {i}: rel err {ei:.3e} > {stol}"
+            e = max(e, ei)
     return e
 
 

@@ -67,15 +67,15 @@ def test_fullsize_fuse_and_inject(c2):
     got = gh.to_np_bf16(ctx)
     WF = {"w_fc": synth.bf16_to_f64(W["w_fc"]), "g_fc": synth.bf16_to_f64(W["g_fc"])}
     want = ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps[rows]))
-    gh.check_rel(got, want, what="fuse rows")
+    gh.check_rel(got, want, what="fuse rows", rows=True)
     # injected K/V of those positions in every layer, from the device's ctx
     for l in range(cfg.n_layers):
         LW = _layer_w(W, l)
         k, v = ref.project_kv(ocfg, LW, l, got, np.array(rows))
         kd = gh.to_np_bf16(dr.k[l, 0][:, rows]).transpose(1, 0, 2)
         vd = gh.to_np_bf16(dr.v[l, 0][:, rows]).transpose(1, 0, 2)
-        gh.check_rel(kd, k, what=f"K layer {l}")
-        gh.check_rel(vd, v, what=f"V layer {l}")
+        gh.check_rel(kd, k, what=f"K layer {l}", axis=1)
+        gh.check_rel(vd, v, what=f"V layer {l}", axis=1)
 
 
 def test_fullsize_layers_stage_replay(c2):
@@ -89,10 +89,10 @@ def test_fullsize_layers_stage_replay(c2):
         kc = gh.to_np_bf16(dr.k[l, 0, :, :L]).transpose(1, 0, 2)
         vc = gh.to_np_bf16(dr.v[l, 0, :, :L]).transpose(1, 0, 2)
         want, kb, vb = ref.decoder_layer(ocfg, LW, l, out["hidden"][l], pos, kc, vc)
-        e = gh.check_rel(out["hidden"][l + 1], want, tol=1e-2, what=f"layer {l}")
+        e = gh.check_rel(out["hidden"][l + 1], want, tol=1e-2, what=f"layer {l}", rows=True)
         gh.log(f"    rel err {e:.2e}")
         kbl = gh.to_np_bf16(dr.k[l, 0, :, L:L + B]).transpose(1, 0, 2)
-        gh.check_rel(kbl, kb, what=f"block K layer {l}")
+        gh.check_rel(kbl, kb, what=f"block K layer {l}", axis=1)
 
 
 def test_fullsize_lm_head_and_tokens(c2):
@@ -101,7 +101,7 @@ def test_fullsize_lm_head_and_tokens(c2):
     fin = ref.rms_norm(out["hidden"][cfg.n_layers][1:], synth.bf16_to_f64(W["g_final"]), cfg.rms_eps)
     lm = synth.bf16_to_f64(W["lm_head"])
     z = fin @ lm.T
-    e = gh.check_rel(out["logits"], z, tol=1e-2, what="logits")
+    e = gh.check_rel(out["logits"], z, tol=1e-2, what="logits", rows=True)
     band = gh.check_tokens(out["draft"], out["logits"], z, gh.replay_band(fin, lm), what="draft tokens")
     gh.log(f"    rel err {e:.2e}, tie-band rows {band}/{len(out['draft'])}")
 
@@ -116,8 +116,8 @@ def test_fullsize_end_to_end(c2):
                   [(r, 0, r) for r in range(cfg.ctx_len)], cache)
     r = ref.draft_block(ocfg, WO, cache, [cfg.ctx_len], anchor)
     for l in range(cfg.n_layers + 1):
-        gh.check_rel(out["hidden"][l], r["hidden"][0, l], what=f"hidden {l}")
-    e = gh.check_rel(out["logits"], r["logits"][0], what="logits")
+        gh.check_rel(out["hidden"][l], r["hidden"][0, l], what=f"hidden {l}", rows=True)
+    e = gh.check_rel(out["logits"], r["logits"][0], what="logits", rows=True)
     band = gh.check_tokens(out["draft"], out["logits"], r["logits"][0], gh.e2e_band(r["logits"][0]), what="tokens")
     gh.log(f"    logits rel err {e:.2e}, tie-band rows {band}")
 
@@ -163,10 +163,10 @@ def test_fullsize_random_gains_layer(gpu_lib):
     LW = _layer_w(W, 0)
     WF = {"w_fc": synth.bf16_to_f64(W["w_fc"]), "g_fc": synth.bf16_to_f64(W["g_fc"])}
     got = gh.to_np_bf16(ctx)
-    gh.check_rel(got, ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps[rows])), what="fuse rows")
+    gh.check_rel(got, ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps[rows])), what="fuse rows", rows=True)
     k, v = ref.project_kv(ocfg, LW, 0, got, np.array(rows))
-    gh.check_rel(gh.to_np_bf16(dr.k[0, 0][:, rows]).transpose(1, 0, 2), k, what="K rows")
-    gh.check_rel(gh.to_np_bf16(dr.v[0, 0][:, rows]).transpose(1, 0, 2), v, what="V rows")
+    gh.check_rel(gh.to_np_bf16(dr.k[0, 0][:, rows]).transpose(1, 0, 2), k, what="K rows", axis=1)
+    gh.check_rel(gh.to_np_bf16(dr.v[0, 0][:, rows]).transpose(1, 0, 2), v, what="V rows", axis=1)
     hid = hidden.cpu().numpy().astype(np.float64)
     # the embedding row is the embedding itself (the input norm's gain acts inside the layer)
     E = synth.bf16_to_f64(W["embed"])
@@ -175,13 +175,13 @@ def test_fullsize_random_gains_layer(gpu_lib):
     kc = gh.to_np_bf16(dr.k[0, 0, :, :L]).transpose(1, 0, 2)
     vc = gh.to_np_bf16(dr.v[0, 0, :, :L]).transpose(1, 0, 2)
     want, kb, vb = ref.decoder_layer(ocfg, LW, 0, hid[0], L + np.arange(B), kc, vc)
-    e = gh.check_rel(hid[1], want, tol=1e-2, what="layer 0")
-    gh.check_rel(gh.to_np_bf16(dr.k[0, 0, :, L:L + B]).transpose(1, 0, 2), kb, what="block K")
-    gh.check_rel(gh.to_np_bf16(dr.v[0, 0, :, L:L + B]).transpose(1, 0, 2), vb, what="block V")
+    e = gh.check_rel(hid[1], want, tol=1e-2, what="layer 0", rows=True)
+    gh.check_rel(gh.to_np_bf16(dr.k[0, 0, :, L:L + B]).transpose(1, 0, 2), kb, what="block K", axis=1)
+    gh.check_rel(gh.to_np_bf16(dr.v[0, 0, :, L:L + B]).transpose(1, 0, 2), vb, what="block V", axis=1)
     fin = ref.rms_norm(hid[1][1:], synth.bf16_to_f64(W["g_final"]), cfg.rms_eps)
     lm = synth.bf16_to_f64(W["lm_head"])
     z = fin @ lm.T
-    el = gh.check_rel(logits.cpu().numpy(), z, tol=1e-2, what="logits")
+    el = gh.check_rel(logits.cpu().numpy(), z, tol=1e-2, what="logits", rows=True)
     band = gh.check_tokens(dr.draft.cpu().numpy()[0], logits.cpu().numpy(), z, gh.replay_band(fin, lm),
                            what="tokens")
     gh.log(f"    layer rel err {e:.2e}, logits {el:.2e}, tie-band rows {band}")

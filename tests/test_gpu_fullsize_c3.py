@@ -92,10 +92,10 @@ def test_c3_layers_stage_replay(c3):
             kc, vc = _cache(dr, l, b, 0, L)
             x = out["hidden"][l, b * B:(b + 1) * B].astype(np.float64)
             want, kb, vb = ref.decoder_layer(ocfg, LW, l, x, L + np.arange(B), kc, vc)
-            e = gh.check_rel(out["hidden"][l + 1, b * B:(b + 1) * B], want, tol=1e-2, what=f"layer {l} seq {b}")
+            e = gh.check_rel(out["hidden"][l + 1, b * B:(b + 1) * B], want, tol=1e-2, what=f"layer {l} seq {b}", rows=True)
             kbd, vbd = _cache(dr, l, b, L, L + B)
-            gh.check_rel(kbd, kb, what=f"block K layer {l} seq {b}")
-            gh.check_rel(vbd, vb, what=f"block V layer {l} seq {b}")
+            gh.check_rel(kbd, kb, what=f"block K layer {l} seq {b}", axis=1)
+            gh.check_rel(vbd, vb, what=f"block V layer {l} seq {b}", axis=1)
             gh.log(f"[fullsize c3] layer {l} seq {b} (context {L}): rel err {e:.2e}")
 
 
@@ -109,7 +109,7 @@ def test_c3_lm_head_and_tokens(c3):
         fin = ref.rms_norm(hid, g, cfg.rms_eps)
         z = fin @ lm.T
         got = out["logits"][b * (B - 1):(b + 1) * (B - 1)].astype(np.float64)
-        e = gh.check_rel(got, z, tol=1e-2, what=f"logits seq {b}")
+        e = gh.check_rel(got, z, tol=1e-2, what=f"logits seq {b}", rows=True)
         band = gh.check_tokens(out["draft"][b], got, z, gh.replay_band(fin, lm), what=f"tokens seq {b}")
         gh.log(f"[fullsize c3] LM head seq {b}: rel err {e:.2e}, tie-band rows {band}")
 
@@ -124,13 +124,13 @@ def test_c3_fuse_and_inject_sampled(c3):
         dr.fuse_ctx(_bf16_dev(torch, taps), len(pick), ctx)
         torch.cuda.synchronize()
         got = gh.to_np_bf16(ctx)
-        gh.check_rel(got, ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps)), what=f"fuse seq {b}")
+        gh.check_rel(got, ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps)), what=f"fuse seq {b}", rows=True)
         for l in range(cfg.n_layers):
             k, v = ref.project_kv(ocfg, _layer_w(W, l), l, got, pick)
             kd = gh.to_np_bf16(dr.k[l, b][:, pick]).transpose(1, 0, 2)
             vd = gh.to_np_bf16(dr.v[l, b][:, pick]).transpose(1, 0, 2)
-            gh.check_rel(kd, k, what=f"K seq {b} layer {l}")
-            gh.check_rel(vd, v, what=f"V seq {b} layer {l}")
+            gh.check_rel(kd, k, what=f"K seq {b} layer {l}", axis=1)
+            gh.check_rel(vd, v, what=f"V seq {b} layer {l}", axis=1)
 
 
 def test_c3_verify_commit(c3):
@@ -163,6 +163,6 @@ def test_c3_verify_commit(c3):
         kc, vc = _cache(dr, 0, b, 0, L)
         x = nxt["hidden"][0, b * B:(b + 1) * B].astype(np.float64)
         want, _, _ = ref.decoder_layer(ocfg, W0, 0, x, L + np.arange(B), kc, vc)
-        gh.check_rel(nxt["hidden"][1, b * B:(b + 1) * B], want, tol=1e-2, what=f"step {step} next block seq {b}")
+        gh.check_rel(nxt["hidden"][1, b * B:(b + 1) * B], want, tol=1e-2, what=f"step {step} next block seq {b}", rows=True)
         gh.log(f"[fullsize c3] step {step}: accept {m.tolist()[:8]}...")
         draft = nxt["draft"]

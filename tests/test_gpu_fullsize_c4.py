@@ -100,13 +100,13 @@ def test_c4_fuse_and_inject_sampled(c4):
         dr.fuse_ctx(_bf16_dev(torch, taps_rows[b]), len(ROWS), ctx)
         torch.cuda.synchronize()
         got = gh.to_np_bf16(ctx)
-        gh.check_rel(got, ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps_rows[b])), what=f"fuse seq {b}")
+        gh.check_rel(got, ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps_rows[b])), what=f"fuse seq {b}", rows=True)
         for l in range(cfg.n_layers):
             LW = {k: synth.bf16_to_f64(v) for k, v in W.items() if k.startswith(f"layers.{l}.")}
             k, v = ref.project_kv(ocfg, LW, l, got, rows)
             kd, vd = _cache(dr, l, b, 0, L)
-            gh.check_rel(kd[rows], k, what=f"K seq {b} layer {l}")
-            gh.check_rel(vd[rows], v, what=f"V seq {b} layer {l}")
+            gh.check_rel(kd[rows], k, what=f"K seq {b} layer {l}", axis=1)
+            gh.check_rel(vd[rows], v, what=f"V seq {b} layer {l}", axis=1)
 
 
 def test_c4_layers_stage_replay(c4):
@@ -121,10 +121,10 @@ def test_c4_layers_stage_replay(c4):
                 kc, vc = _cache(drs[B], l, b, 0, L)
                 x = hid[l, b * B:(b + 1) * B]
                 want, kb, vb = ref.decoder_layer(ocfg, LW, l, x, L + np.arange(B), kc, vc)
-                e = gh.check_rel(hid[l + 1, b * B:(b + 1) * B], want, tol=1e-2, what=f"B{B} layer {l} seq {b}")
+                e = gh.check_rel(hid[l + 1, b * B:(b + 1) * B], want, tol=1e-2, what=f"B{B} layer {l} seq {b}", rows=True)
                 kbd, vbd = _cache(drs[B], l, b, L, L + B)
-                gh.check_rel(kbd, kb, what=f"B{B} block K layer {l} seq {b}")
-                gh.check_rel(vbd, vb, what=f"B{B} block V layer {l} seq {b}")
+                gh.check_rel(kbd, kb, what=f"B{B} block K layer {l} seq {b}", axis=1)
+                gh.check_rel(vbd, vb, what=f"B{B} block V layer {l} seq {b}", axis=1)
                 gh.log(f"    rel err {e:.2e}")
 
 
@@ -139,7 +139,7 @@ def test_c4_lm_head_and_tokens(c4):
         for b in SEQS:
             fin = ref.rms_norm(o["hidden"][cfg.n_layers, b * B + 1:(b + 1) * B], gf, cfg.rms_eps)
             z = fin @ lm.T
-            e = gh.check_rel(z_all[b], z, tol=1e-2, what=f"B{B} logits seq {b}")
+            e = gh.check_rel(z_all[b], z, tol=1e-2, what=f"B{B} logits seq {b}", rows=True)
             band = gh.check_tokens(o["draft"][b], z_all[b], z, gh.replay_band(fin, lm), what=f"B{B} draft tokens seq {b}")
             gh.log(f"    block {B} seq {b}: rel err {e:.2e}, tie-band rows {band}/{B - 1}")
 

@@ -91,13 +91,13 @@ def test_c5_fuse_and_inject_sampled(c5):
         dr.fuse_ctx(_bf16_dev(torch, taps_rows[b]), len(ROWS), ctx)
         torch.cuda.synchronize()
         got = gh.to_np_bf16(ctx)
-        gh.check_rel(got, ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps_rows[b])), what=f"fuse seq {b}")
+        gh.check_rel(got, ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps_rows[b])), what=f"fuse seq {b}", rows=True)
         for l in range(cfg.n_layers):
             k, v = ref.project_kv(ocfg, _layer_w(W, l), l, got, rows)
             kd = gh.to_np_bf16(dr.k[l, b][:, rows]).transpose(1, 0, 2)
             vd = gh.to_np_bf16(dr.v[l, b][:, rows]).transpose(1, 0, 2)
-            gh.check_rel(kd, k, what=f"K seq {b} layer {l}")
-            gh.check_rel(vd, v, what=f"V seq {b} layer {l}")
+            gh.check_rel(kd, k, what=f"K seq {b} layer {l}", axis=1)
+            gh.check_rel(vd, v, what=f"V seq {b} layer {l}", axis=1)
 
 
 def test_c5_layers_stage_replay(c5):
@@ -113,10 +113,10 @@ def test_c5_layers_stage_replay(c5):
             x = out["hidden"][l, b * B:(b + 1) * B]
             want, kb, vb = ref.decoder_layer(ocfg, LW, l, x, L + np.arange(B), kc, vc)
             e = gh.check_rel(out["hidden"][l + 1, b * B:(b + 1) * B], want, tol=1e-2,
-                             what=f"layer {l} seq {b}")
+                             what=f"layer {l} seq {b}", rows=True)
             kbd, vbd = _cache(dr, l, b, L, L + B)
-            gh.check_rel(kbd, kb, what=f"block K layer {l} seq {b}")
-            gh.check_rel(vbd, vb, what=f"block V layer {l} seq {b}")
+            gh.check_rel(kbd, kb, what=f"block K layer {l} seq {b}", axis=1)
+            gh.check_rel(vbd, vb, what=f"block V layer {l} seq {b}", axis=1)
             gh.log(f"    rel err {e:.2e}")
 
 
@@ -128,7 +128,7 @@ def test_c5_lm_head_and_tokens(c5):
     fin = ref.rms_norm(out["hidden"][NL][rows], synth.bf16_to_f64(W["g_final"]), cfg.rms_eps)
     lm = synth.bf16_to_f64(W["lm_head"])
     z = fin @ lm.T
-    e = gh.check_rel(out["logits"], z, tol=1e-2, what="logits")
+    e = gh.check_rel(out["logits"], z, tol=1e-2, what="logits", rows=True)
     band = gh.check_tokens(out["draft"].reshape(-1), out["logits"], z, gh.replay_band(fin, lm), what="draft tokens")
     gh.log(f"    rel err {e:.2e}, tie-band rows {band}/{len(rows)}")
 
@@ -165,19 +165,19 @@ def test_c5_verify_commit_rollback(c5):
         assert dr.ctx_len.cpu().numpy().tolist() == ctx_len.tolist()
         assert dr.status.cpu().tolist() == [0] * batch
         ctx = gh.to_np_bf16(dr.ctx[:batch * B])
-        gh.check_rel(ctx, ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps_step)), what=f"step {step} fuse")
+        gh.check_rel(ctx, ref.fuse_ctx(ocfg, WF, synth.bf16_to_f64(taps_step)), what=f"step {step} fuse", rows=True)
         for l, LW in ((0, W0), (NL - 1, WL)):
             for b in range(batch):
                 sel = rows[rows[:, 1] == b]
                 k, v = ref.project_kv(ocfg, LW, l, ctx[sel[:, 0]], sel[:, 2])
                 kd, vd = _cache(dr, l, b, int(sel[0, 2]), int(sel[-1, 2]) + 1)
-                gh.check_rel(kd, k, what=f"step {step} committed K layer {l} seq {b}")
-                gh.check_rel(vd, v, what=f"step {step} committed V layer {l} seq {b}")
+                gh.check_rel(kd, k, what=f"step {step} committed K layer {l} seq {b}", axis=1)
+                gh.check_rel(vd, v, what=f"step {step} committed V layer {l} seq {b}", axis=1)
         # next block from the new anchors; layer 0 of sequence 0 replayed over
         # [0, ctx_len) only: slots of the rejected block rows must not be read
         nxt = _draft(torch, dr, cfg, anchor=dr.anchor_out)
         L0 = int(ctx_len[0])
         kc, vc = _cache(dr, 0, 0, 0, L0)
         want, _, _ = ref.decoder_layer(ocfg, W0, 0, nxt["hidden"][0, :B], L0 + np.arange(B), kc, vc)
-        gh.check_rel(nxt["hidden"][1, :B], want, tol=1e-2, what=f"step {step} next block layer 0")
+        gh.check_rel(nxt["hidden"][1, :B], want, tol=1e-2, what=f"step {step} next block layer 0", rows=True)
         draft = nxt["draft"]

@@ -69,11 +69,11 @@ def test_target_layers_stage_replay(target):
             kc = gh.to_np_bf16(tgt.k[l, b, :, :L]).transpose(1, 0, 2)
             vc = gh.to_np_bf16(tgt.v[l, b, :, :L]).transpose(1, 0, 2)
             want, kb, vb = ref.decoder_layer(ocfg, LW, l, x, pos, kc, vc, allowed=allowed)
-            e = gh.check_rel(out["taps"][b, :, l], want, what=f"layer {l} seq {b}")
+            e = gh.check_rel(out["taps"][b, :, l], want, what=f"layer {l} seq {b}", rows=True)
             kd = gh.to_np_bf16(tgt.k[l, b, :, L:L + N]).transpose(1, 0, 2)
             vd = gh.to_np_bf16(tgt.v[l, b, :, L:L + N]).transpose(1, 0, 2)
-            gh.check_rel(kd, kb, what=f"block K layer {l} seq {b}")
-            gh.check_rel(vd, vb, what=f"block V layer {l} seq {b}")
+            gh.check_rel(kd, kb, what=f"block K layer {l} seq {b}", axis=1)
+            gh.check_rel(vd, vb, what=f"block V layer {l} seq {b}", axis=1)
             gh.log(f"    rel err {e:.2e}")
 
 
@@ -86,7 +86,7 @@ def test_target_lm_head_and_argmax(target):
         # replayed from the bf16 tap of the last layer (one more rounding per element)
         fin = ref.rms_norm(out["taps"][b, :, LAYERS - 1], gf, cfg.rms_eps)
         z = fin @ lm.T
-        e = gh.check_rel(out["logits"][b], z, what=f"logits seq {b}")
+        e = gh.check_rel(out["logits"][b], z, what=f"logits seq {b}", rows=True)
         assert np.array_equal(out["argmax"][b], np.argmax(out["logits"][b], axis=1))
         band = gh.check_tokens(out["argmax"][b], out["logits"][b], z, gh.replay_band(fin, lm, roundings=2),
                                what=f"argmax seq {b}")

@@ -87,7 +87,7 @@ def test_fuse_ctx_parity(gpu_lib, shape, gains):
     torch.cuda.synchronize()
     got = gh.to_np_bf16(ctx)
     want = ref.fuse_ctx(ocfg, WO, synth.bf16_to_f64(taps))
-    e = gh.check_rel(got, want, what="fuse")
+    e = gh.check_rel(got, want, what="fuse", rows=True)
     gh.log(f"    rel err {e:.2e}")
 
 
@@ -111,11 +111,11 @@ def test_inject_kv_parity(gpu_lib, shape, gains):
         ref.inject_kv(ocfg, WO, ctx64, [(r, 0, r) for r in range(L)], rc)
         for l in range(cfg.n_layers):
             k, v = gpu_cache(dr, l, b, L)
-            gh.check_rel(k, rc["k"][l, 0, :L], what=f"K replay l{l} b{b}")
-            gh.check_rel(v, rc["v"][l, 0, :L], what=f"V replay l{l} b{b}")
+            gh.check_rel(k, rc["k"][l, 0, :L], what=f"K replay l{l} b{b}", axis=1)
+            gh.check_rel(v, rc["v"][l, 0, :L], what=f"V replay l{l} b{b}", axis=1)
             # end to end from the taps
-            gh.check_rel(k, cache["k"][l, b, :L], what=f"K l{l} b{b}")
-            gh.check_rel(v, cache["v"][l, b, :L], what=f"V l{l} b{b}")
+            gh.check_rel(k, cache["k"][l, b, :L], what=f"K l{l} b{b}", axis=1)
+            gh.check_rel(v, cache["v"][l, b, :L], what=f"V l{l} b{b}", axis=1)
     # slots past the committed context were never written
     for b, L in enumerate(lens):
         assert float(dr.k[:, b, :, L:].abs().max()) == 0.0
@@ -144,8 +144,8 @@ def test_draft_block_parity(gpu_lib, shape, gains):
     # end to end against the oracle from the same inputs
     r = ref.draft_block(ocfg, WO, cache, lens, anchor)
     for l in range(NL + 1):
-        gh.check_rel(hidden[l], r["hidden"][:, l], what=f"hidden after layer {l}")
-    gh.check_rel(logits, r["logits"], what="logits")
+        gh.check_rel(hidden[l], r["hidden"][:, l], what=f"hidden after layer {l}", rows=True)
+    gh.check_rel(logits, r["logits"], what="logits", rows=True)
     band = gh.check_tokens(draft, logits, r["logits"], gh.e2e_band(r["logits"]), what="draft tokens")
     gh.log(f"    tie-band rows (end to end): {band}/{draft.size}")
 
@@ -155,14 +155,14 @@ def test_draft_block_parity(gpu_lib, shape, gains):
         for l in range(NL):
             kc, vc = gpu_cache(dr, l, b, L)
             want, kb, vb = ref.decoder_layer(ocfg, WO, l, hidden[l, b], pos, kc, vc)
-            gh.check_rel(hidden[l + 1, b], want, tol=1e-2, what=f"replay layer {l} seq {b}")
+            gh.check_rel(hidden[l + 1, b], want, tol=1e-2, what=f"replay layer {l} seq {b}", rows=True)
             # the block's own K/V were appended at slots L..L+B-1
             kbl, vbl = gpu_cache(dr, l, b, L + B)
-            gh.check_rel(kbl[L:], kb, what=f"block K l{l} b{b}")
-            gh.check_rel(vbl[L:], vb, what=f"block V l{l} b{b}")
+            gh.check_rel(kbl[L:], kb, what=f"block K l{l} b{b}", axis=1)
+            gh.check_rel(vbl[L:], vb, what=f"block V l{l} b{b}", axis=1)
         fin = ref.rms_norm(hidden[NL, b], WO["g_final"], cfg.rms_eps)
         z = fin[1:] @ WO["lm_head"].T
-        gh.check_rel(logits[b], z, tol=1e-2, what=f"replay lm head seq {b}")
+        gh.check_rel(logits[b], z, tol=1e-2, what=f"replay lm head seq {b}", rows=True)
         gh.check_tokens(draft[b], logits[b], z, gh.replay_band(fin[1:], WO["lm_head"]), what=f"replay tokens seq {b}")
 
 
@@ -183,7 +183,7 @@ def test_draft_block_capacity_status(gpu_lib):
     assert (d[2] == -1).all()
     r = ref.draft_block(ocfg, WO, cache, lens[:2], [1, 2])
     logits = lg.cpu().numpy().astype(np.float64).reshape(3, cfg.block - 1, cfg.vocab)
-    gh.check_rel(logits[:2], r["logits"], what="logits beside a failed sequence")
+    gh.check_rel(logits[:2], r["logits"], what="logits beside a failed sequence", rows=True)
     gh.check_tokens(d[:2], logits[:2], r["logits"], gh.e2e_band(r["logits"]), what="tokens beside a failed sequence")
 
 
@@ -208,7 +208,7 @@ def test_small_blocks_draft_and_verify(gpu_lib, B):
     d = dr.draft.cpu().numpy()
     logits = lg.cpu().numpy().astype(np.float64).reshape(cfg.batch, B - 1, V)
     r = ref.draft_block(ocfg, WO, cache, lens, anchor)
-    gh.check_rel(logits, r["logits"], what=f"logits, block {B}")
+    gh.check_rel(logits, r["logits"], what=f"logits, block {B}", rows=True)
     gh.check_tokens(d, logits, r["logits"], gh.e2e_band(r["logits"]), what=f"tokens, block {B}")
     for step in range(4):
         m = synth.geometric_accept(cfg.batch, B, 0.8, step=step)
@@ -252,7 +252,7 @@ def test_draft_block_batch_over_64(gpu_lib):
     assert (d[bad] == -1).all()
     r = ref.draft_block(ocfg, WO, cache, lens[:bad], anchor[:bad])
     logits = lg.cpu().numpy().astype(np.float64).reshape(cfg.batch, B - 1, V)
-    gh.check_rel(logits[:bad], r["logits"], what="logits of 69 sequences")
+    gh.check_rel(logits[:bad], r["logits"], what="logits of 69 sequences", rows=True)
     band = gh.check_tokens(d[:bad], logits[:bad], r["logits"], gh.e2e_band(r["logits"]), what="tokens of 69 sequences")
     gh.log(f"    tie-band rows {band}/{d[:bad].size}")
 
@@ -362,8 +362,8 @@ def test_tiny_loop_lossless_with_device_drafter(gpu_lib):
         ref.inject_kv(ocfg, WO, ref.fuse_ctx(ocfg, WO, taps), [(r, 0, r) for r in range(L)], fresh)
         for l in range(cfg.n_layers):
             k, v = gpu_cache(dr, l, 0, L)
-            gh.check_rel(k, fresh["k"][l, 0], what=f"loop cache K l{l}")
-            gh.check_rel(v, fresh["v"][l, 0], what=f"loop cache V l{l}")
+            gh.check_rel(k, fresh["k"][l, 0], what=f"loop cache K l{l}", axis=1)
+            gh.check_rel(v, fresh["v"][l, 0], what=f"loop cache V l{l}", axis=1)
     # stop token ends the loop right after it
     stop = greedy[20]
     out2, _ = spec_generate(dr, OracleTarget(tgt), prompt, cfg.n_new, stop_token_ids=[stop])
@@ -417,5 +417,5 @@ def test_attention_reference_moves_mid_chunk(gpu_lib, shape):
         for l in range(NL):
             kc, vc = gpu_cache(dr, l, b, L)
             want, _, _ = ref.decoder_layer(ocfg, WO, l, hidden[l, b], pos, kc, vc)
-            e = gh.check_rel(hidden[l + 1, b], want, tol=1e-2, what=f"replay layer {l} seq {b}")
+            e = gh.check_rel(hidden[l + 1, b], want, tol=1e-2, what=f"replay layer {l} seq {b}", rows=True)
             gh.log(f"    layer {l} seq {b} (context {L}): rel err {e:.2e}")

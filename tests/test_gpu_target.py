@@ -76,14 +76,14 @@ def test_target_pass_parity(gpu_lib, gains):
     z, tp, tk = np.concatenate(logits), np.concatenate(taps), np.concatenate(toks)
     tgt = _oracle_target(cfg, ocfg, TW)
     zr, tr = tgt.forward(prompt)
-    e = gh.check_rel(z, zr, what="target logits")
+    e = gh.check_rel(z, zr, what="target logits", rows=True)
     gh.check_tokens(tk, z, zr, gh.e2e_band(zr), what="target argmax")
-    gh.check_rel(tp, tr, what="target taps")
+    gh.check_rel(tp, tr, what="target taps", rows=True)
     for l in range(cfg.target_layers):
         k = gh.to_np_bf16(dev.k[l, 0, :, :40]).transpose(1, 0, 2)
         v = gh.to_np_bf16(dev.v[l, 0, :, :40]).transpose(1, 0, 2)
-        gh.check_rel(k, tgt.k[l], what=f"target K layer {l}")
-        gh.check_rel(v, tgt.v[l], what=f"target V layer {l}")
+        gh.check_rel(k, tgt.k[l], what=f"target K layer {l}", axis=1)
+        gh.check_rel(v, tgt.v[l], what=f"target V layer {l}", axis=1)
     gh.log(f"    logits rel err {e:.2e}")
 
 
@@ -115,9 +115,9 @@ def test_target_ragged_batch_and_commit(gpu_lib):
         tgt = _oracle_target(cfg, ocfg, TW)
         tgt.forward(t1[b, :keep[b]])
         zr, tr = tgt.forward(t2[b])
-        gh.check_rel(z[b], zr, what=f"seq {b} logits")
+        gh.check_rel(z[b], zr, what=f"seq {b} logits", rows=True)
         gh.check_tokens(a[b], z[b], zr, gh.e2e_band(zr), what=f"seq {b} argmax")
-        gh.check_rel(tp[b], tr, what=f"seq {b} taps")
+        gh.check_rel(tp[b], tr, what=f"seq {b} taps", rows=True)
 
 
 def test_target_capacity_and_commit_edges(gpu_lib):
