@@ -68,7 +68,8 @@ inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct GemmPlan {
-  bool big;    // large-tile kernel (256 x 256 tiles) over all rows
+  bool big;    // large-tile kernel (bm x 256 tiles) over all rows
+  int bm = 256;  // large-tile kernel: activation rows per tile (256 or 128)
   bool tiled;  // LDS-tiled kernel over all rows, or the streaming kernel per kGemmRows rows
   int mt, nf;  // streaming: activation tiles and weight fragments per workgroup
   int ng;      // tiled: weight row groups per wave (64*ng columns per workgroup); mt: 16-row tiles
@@ -111,20 +112,40 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
     // Large tiles (one 512-thread workgroup per CU). Split-K only in partial
     // mode and only while the grid still fits one round of kBigSlots
     // workgroups: a second, partly filled round costs more than the split
-    // saves (c3, 512 rows: qkv 240 workgroups at 5 splits, o and down 256 at
-    // 8; 6 splits of qkv, 288 workgroups, measured 47% slower than 4).
+    // saves (512 rows: 6 splits of the QKV product, 288 workgroups, measured
+    // 47% slower than 4). Where 256-row tiles need split-K, 128-row tiles
+    // halve the splits and with them the fp32 partials that the GEMM writes
+    // and the next pass reads; they are taken unless they cost more than a
+    // quarter of the grid (512 rows of the Qwen3-8B-shaped drafter: o and
+    // down 8 -> 4 splits at 256 workgroups, QKV 5 -> 2 at 240 -> 192; the
+    // inject product over five layers keeps 256-row tiles, 240 workgroups
+    // against 160; the step 2701 -> 2610 us, measured on MI355X).
     g.big = true;
     g.tiled = false;
     g.mt = g.nf = g.ng = 0;
-    const long long base = cdiv(M, dfl::gemm_big_rows()) * cdiv(N, dfl::gemm_big_cols(mode)) * nz;
+    const long long cols = cdiv(N, dfl::gemm_big_cols(mode)) * nz;
     const int chunks = K / 32;
-    int s = 1;
-    if (mode == dfl::kGemmPartial && base < kBigSlots) {
-      s = (int)(kBigSlots / base);
-      s = std::min(s, std::max(1, chunks / 8));  // at least 256 k per split
+    auto split = [&](int bm, int* per) {
+      const long long base = cdiv(M, bm) * cols;
+      int s = 1;
+      if (mode == dfl::kGemmPartial && base < kBigSlots) {
+        s = (int)(kBigSlots / base);
+        s = std::min(s, std::max(1, chunks / 8));  // at least 256 k per split
+      }
+      *per = (int)cdiv(chunks, s);
+      return (int)cdiv(chunks, *per);
+    };
+    int per = 0;
+    g.splits = split(256, &per);
+    if (g.splits > 1) {
+      int per128 = 0;
+      const int s128 = split(128, &per128);
+      if (4 * cdiv(M, 128) * s128 >= 3 * cdiv(M, 256) * g.splits) {
+        g.bm = 128;
+        g.splits = s128;
+        per = per128;
+      }
     }
-    const int per = (int)cdiv(chunks, s);
-    g.splits = (int)cdiv(chunks, per);
     g.k_per_split = per * 32;
     return g;
   }
@@ -288,7 +309,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     p.P = c.P;
     p.p_s_stride = (long long)c.M * c.N;
     p.p_z_stride = (long long)g.splits * c.M * c.N;
-    if (g.big) return dfl::launch_gemm_big(p, c.mode, c.nz, st);
+    if (g.big) return dfl::launch_gemm_big(p, c.mode, c.nz, g.bm, st);
     return g.ws ? dfl::launch_gemm_ws(p, g.ng, g.mt, c.mode, c.nz, st)
                 : dfl::launch_gemm_tile(p, g.ng, g.mt, c.mode, c.nz, st);
   }

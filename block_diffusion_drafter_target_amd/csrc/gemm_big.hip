@@ -4,11 +4,14 @@
 // row-major (optionally gathered rows). With hundreds to thousands of rows the
 // product is bound by the matrix cores, and the kernel is laid out for their
 // operand traffic rather than for the weight stream:
-//   * workgroup = 8 waves over a 256 (rows of A) x 256 (weight rows) tile;
-//     wave w owns 128 rows (w & 1) x 64 weight rows (w >> 1), 32 MFMA tiles
-//     of 16 x 16 and 128 accumulator registers (two waves per SIMD; a
-//     4-wave layout of 128 x 128 wave tiles, one wave per SIMD, measured
-//     10-25% slower: nothing hides its LDS latency);
+//   * workgroup = 8 waves over a BM (rows of A) x 256 (weight rows) tile,
+//     BM = 256 or 128; wave w owns BM / 2 rows (w & 1) x 64 weight rows
+//     (w >> 1): at BM = 256, 32 MFMA tiles of 16 x 16 and 128 accumulator
+//     registers (two waves per SIMD; a 4-wave layout of 128 x 128 wave tiles,
+//     one wave per SIMD, measured 10-25% slower: nothing hides its LDS
+//     latency). BM = 128 reads more LDS per MFMA but doubles the tiles, for
+//     products whose 256-row grid would need split-K: half the splits, half
+//     the fp32 partials written here and read by the next pass;
 //   * both operands go HBM/L2 -> LDS by gfx950's direct loads
 //     (global_load_lds_dwordx4: lane l's 16 bytes land at offset 16*l of a
 //     1 KB slot), so they take no registers on the way. A weight fragment is
@@ -16,8 +19,8 @@
 //     (16 rows x 32 k) is gathered so that it lands in MFMA operand order too.
 //     Every LDS operand read is then one ds_read_b128 of 1 KB contiguous
 //     bytes, free of bank conflicts, with no swizzle;
-//   * a stage is 32 k (16 weight + 16 activation fragments, 32 KB); five
-//     stages fill the 160 KB of LDS (one workgroup per CU). A stage's loads
+//   * a stage is 32 k (16 weight + BM / 16 activation fragments, 32 or
+//     24 KB); five stages take 160 or 120 KB of LDS (one workgroup per CU). A stage's loads
 //     are issued five stages ahead, at the end of the MFMAs of the stage
 //     whose buffer they refill; each wave waits for its own direct loads of a
 //     stage with an explicit vmcnt (the compiler does not track them) before
@@ -43,25 +46,34 @@ namespace dfl {
 
 namespace {
 
-constexpr int kBM = 256, kBN = 256;  // activation rows, weight rows per workgroup
-constexpr int kStages = 5;   // 160 KB of LDS
-constexpr int kFrags = 32;           // per stage: 16 weight fragments, then 16 activation fragments
-constexpr int kGroupM = 4;           // row tiles per group of the tile order
+constexpr int kBN = 256;      // weight rows per workgroup
+constexpr int kWF = 16;       // weight fragments per stage
+constexpr int kStages = 5;    // 5 stages of at most 32 KB: one workgroup per CU
+constexpr int kGroupM = 4;    // row tiles per group of the tile order
 
-// Wave layout of a WAVES-wave workgroup (8: wave tiles of 128 rows x 64
-// weight rows).
-template <int WAVES>
+// Wave layout of an 8-wave workgroup over BM activation rows: two waves along
+// the rows (BM / 2 each), four along the weight rows (64 each).
+template <int BM>
 struct BigShape {
-  static constexpr int kWavesN = WAVES / 2;     // waves along the weight rows
-  static constexpr int kNF = 16 / kWavesN;      // weight fragments per wave
-  static constexpr int kLoads = kFrags / WAVES; // direct loads per wave and stage
-  static constexpr int kThreads = 64 * WAVES;
+  static constexpr int kWaves = 8;
+  static constexpr int kWavesN = 4;                // waves along the weight rows
+  static constexpr int kNF = kWF / kWavesN;        // weight fragments per wave
+  static constexpr int kAF = BM / 16;              // activation fragments per stage
+  static constexpr int kAFW = kAF / 2;             // activation fragments per wave
+  static constexpr int kFrags = kWF + kAF;         // fragments per stage
+  static constexpr int kWL = kWF / kWaves;         // weight loads per wave and stage
+  static constexpr int kAL = kAF / kWaves;         // activation loads per wave and stage
+  static constexpr int kLoads = kWL + kAL;         // direct loads per wave and stage
+  static constexpr int kThreads = 64 * kWaves;
+  static_assert(kAF % kWaves == 0 && kWF % kWaves == 0, "loads split evenly over the waves");
 };
 
-template <int MODE, int WAVES>
+template <int MODE, int BM>
 __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
-  using S = BigShape<WAVES>;
+  using S = BigShape<BM>;
   constexpr int kNF = S::kNF, kLoads = S::kLoads, kWavesN = S::kWavesN;
+  constexpr int kAFW = S::kAFW, kWL = S::kWL, kAL = S::kAL, kFrags = S::kFrags;
+  constexpr int kBM = BM;
   __shared__ __align__(1024) u32x4 lds[kStages][kFrags][kWave];
   static_assert(MODE != kGemmArgmax || sizeof(unsigned long long) * kWavesN * kBM <= sizeof(lds),
                 "argmax staging fits");
@@ -96,15 +108,14 @@ __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
   const int nk = (kend - kbeg) >> 5;  // 32-k stages of this split (K % 32 == 0)
   const long long frag_row = (long long)(p.K / 32) * 512;
 
-  // this wave's kLoads / 2 weight slots and as many activation slots
-  // (slot = wave * kLoads / 2 + i); weight slot j is computed by wave
-  // j / kNF as its group j % kNF
-  constexpr int kHalf = kLoads / 2;
-  const bf16_t* wsrc[kHalf];  // uniform: the group's fragment row at the split's first stage
-  int aoff[kHalf];            // per lane: element offset of its row and k in A
+  // this wave's kWL weight slots (slot = wave * kWL + i) and kAL activation
+  // slots (slot = wave * kAL + i); weight slot j is computed by wave j / kNF
+  // as its group j % kNF
+  const bf16_t* wsrc[kWL];  // uniform: the group's fragment row at the split's first stage
+  int aoff[kAL];            // per lane: element offset of its row and k in A
 #pragma unroll
-  for (int i = 0; i < kHalf; ++i) {
-    const int slot = kHalf * wave + i;
+  for (int i = 0; i < kWL; ++i) {
+    const int slot = kWL * wave + i;
     const bf16_t* base;
     int gi;
     if (MODE == kGemmSwiglu) {  // a wave's first kNF/2 groups: gate rows, the rest: up rows of the same columns
@@ -117,6 +128,10 @@ __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
       gi = (n < p.n_split ? n : n - p.n_split) >> 4;
     }
     wsrc[i] = base + gi * frag_row + (long long)(kbeg >> 5) * 512;
+  }
+#pragma unroll
+  for (int i = 0; i < kAL; ++i) {
+    const int slot = kAL * wave + i;
     // activation slot: rows m0 + 16*slot .. +15, lane -> row r, k 8g .. 8g+7
     int m = min(m0 + slot * 16 + r, p.M - 1);
     if (p.a_idx) {
@@ -128,21 +143,23 @@ __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
   const int woff = lane * 8;  // per lane, shared by every weight fragment
 
   // this wave's direct loads of stage c into its LDS buffer (weight and
-  // activation slots alternating)
+  // activation slots alternating while both remain)
   auto issue = [&](int c) __attribute__((always_inline)) {
     const int b = c % kStages;
 #pragma unroll
-    for (int i = 0; i < kHalf; ++i) {
-      __builtin_amdgcn_global_load_lds(wsrc[i] + (long long)c * 512 + woff, (lds_void*)&lds[b][kHalf * wave + i][0], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(p.A + (aoff[i] + c * 32), (lds_void*)&lds[b][16 + kHalf * wave + i][0], 16, 0, 0);
+    for (int i = 0; i < (kWL > kAL ? kWL : kAL); ++i) {
+      if (i < kWL)
+        __builtin_amdgcn_global_load_lds(wsrc[i] + (long long)c * 512 + woff, (lds_void*)&lds[b][kWL * wave + i][0], 16, 0, 0);
+      if (i < kAL)
+        __builtin_amdgcn_global_load_lds(p.A + (aoff[i] + c * 32), (lds_void*)&lds[b][kWF + kAL * wave + i][0], 16, 0, 0);
     }
   };
 
-  f32x4_t acc[kNF][8];
+  f32x4_t acc[kNF][kAFW];
 #pragma unroll
   for (int f = 0; f < kNF; ++f)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[f][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kAFW; ++i) acc[f][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int c = 0; c < kStages; ++c)
@@ -184,20 +201,20 @@ __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
   // refilling af with stage c_next; then the direct loads of stage
   // c_next - 1 + kStages into the buffer of stage c_next - 1, whose reads
   // every wave completed before the barrier that published stage c_next
-  auto step = [&](const u32x4(&wf)[kNF], u32x4(&af)[8], int c_next) __attribute__((always_inline)) {
+  auto step = [&](const u32x4(&wf)[kNF], u32x4(&af)[kAFW], int c_next) __attribute__((always_inline)) {
     const u32x4(*st)[kWave] = lds[c_next % kStages];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kAFW; ++i) {
 #pragma unroll
       for (int f = 0; f < kNF; ++f) acc[f][i] = mfma16x16x32(wf[f], af[i], acc[f][i]);
-      af[i] = st[16 + 8 * wm + i][lane];
+      af[i] = st[kWF + kAFW * wm + i][lane];
     }
     // order for the scheduler: the weight reads issued just before, then per
     // activation fragment its MFMAs and the read that refills it (hoisting
     // the reads would keep two operand sets live and spill)
     __builtin_amdgcn_sched_group_barrier(0x100, kNF, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kAFW; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, kNF, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -205,13 +222,13 @@ __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
     const int cl = c_next - 1 + kStages;
     if (cl < nk) issue(cl);
   };
-  u32x4 wa[kNF], wb[kNF], af[8];
+  u32x4 wa[kNF], wb[kNF], af[kAFW];
   publish(0);
   read_w(0, wa);
   {
     const u32x4(*st)[kWave] = lds[0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) af[i] = st[16 + 8 * wm + i][lane];
+    for (int i = 0; i < kAFW; ++i) af[i] = st[kWF + kAFW * wm + i][lane];
   }
   // one stage past the last is published (a plain barrier: its wait is
   // vmcnt(0)) and read too (its fragments come from a stale buffer and are
@@ -230,8 +247,8 @@ __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
 #pragma unroll
     for (int f = 0; f < kNF; ++f)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int m = m0 + wm * 128 + i * 16 + r;
+      for (int i = 0; i < kAFW; ++i) {
+        const int m = m0 + wm * (kBM / 2) + i * 16 + r;
         const int nb = bx * kBN + (wn * kNF + f) * 16 + 4 * g;
         if (m < p.M && nb < p.N)
           *reinterpret_cast<f32x4_t*>(p.P + (long long)z * p.p_z_stride + (long long)s * p.p_s_stride +
@@ -241,8 +258,8 @@ __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
 #pragma unroll
     for (int fo = 0; fo < kNF / 2; ++fo)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int m = m0 + wm * 128 + i * 16 + r;
+      for (int i = 0; i < kAFW; ++i) {
+        const int m = m0 + wm * (kBM / 2) + i * 16 + r;
         const int nb = bx * kOutCols + (wn * (kNF / 2) + fo) * 16 + 4 * g;
         if (m < p.M && nb < p.N) {
           float sv[4];
@@ -258,8 +275,8 @@ __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
     unsigned long long* kbest = reinterpret_cast<unsigned long long*>(&lds[0][0][0]);  // [kWavesN][kBM]
     __syncthreads();  // every wave is done reading the stages
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + wm * 128 + i * 16 + r;
+    for (int i = 0; i < kAFW; ++i) {
+      const int m = m0 + wm * (kBM / 2) + i * 16 + r;
       float bv = -__builtin_inff();
       int bn = 0x7FFFFFFF;
 #pragma unroll
@@ -283,7 +300,7 @@ __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
           bn = on;
         }
       }
-      if (g == 0) kbest[wn * kBM + wm * 128 + i * 16 + r] = bn != 0x7FFFFFFF ? argmax_key(bv, bn) : 0ull;
+      if (g == 0) kbest[wn * kBM + wm * (kBM / 2) + i * 16 + r] = bn != 0x7FFFFFFF ? argmax_key(bv, bn) : 0ull;
     }
     __syncthreads();
     for (int i = threadIdx.x; i < kBM; i += S::kThreads) {
@@ -298,23 +315,31 @@ __device__ __forceinline__ void gemm_big_body(const GemmParams& p) {
   }
 }
 
-template <int MODE>
+template <int MODE, int BM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_big8_kernel(const GemmParams p) {
-  gemm_big_body<MODE, 8>(p);
+  gemm_big_body<MODE, BM>(p);
 }
 
-template <int MODE>
+template <int MODE, int BM>
 hipError_t launch_one(const GemmParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL(gemm_big8_kernel<MODE>, grid, dim3(512), 0, st, p);
+  hipLaunchKernelGGL((gemm_big8_kernel<MODE, BM>), grid, dim3(512), 0, st, p);
   return hipGetLastError();
+}
+
+template <int BM>
+hipError_t launch_mode(const GemmParams& p, int mode, dim3 grid, hipStream_t st) {
+  if (mode == kGemmPartial) return launch_one<kGemmPartial, BM>(p, grid, st);
+  if (mode == kGemmSwiglu) return launch_one<kGemmSwiglu, BM>(p, grid, st);
+  if (mode == kGemmArgmax) return launch_one<kGemmArgmax, BM>(p, grid, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 int gemm_big_cols(int mode) { return mode == kGemmSwiglu ? kBN / 2 : kBN; }
-int gemm_big_rows() { return kBM; }
 
-hipError_t launch_gemm_big(const GemmParams& p, int mode, int nz, hipStream_t st) {
+hipError_t launch_gemm_big(const GemmParams& p, int mode, int nz, int bm, hipStream_t st) {
+  if (bm != 256 && bm != 128) return hipErrorInvalidValue;
   if (p.K % 32 || p.k_per_split % 32 || p.k_per_split < 32 || p.n_mats != nz || p.M < 1 || p.N < 16)
     return hipErrorInvalidValue;
   if (mode == kGemmSwiglu && p.splits != 1) return hipErrorInvalidValue;
@@ -322,16 +347,13 @@ hipError_t launch_gemm_big(const GemmParams& p, int mode, int nz, hipStream_t st
   // the kernel addresses activation rows with 32-bit element offsets from p.A
   const long long rows = p.a_idx ? p.a_idx_max : p.M;
   if ((rows - 1) * p.lda + p.K > 0x7FFFFFFFll) return hipErrorInvalidValue;
-  const long long m_tiles = (p.M + kBM - 1) / kBM;
+  const long long m_tiles = (p.M + bm - 1) / bm;
   const long long n_tiles = (p.N + gemm_big_cols(mode) - 1) / gemm_big_cols(mode);
   const long long total = m_tiles * n_tiles * p.splits * nz;
   const long long grid = (total + 7) / 8 * 8;
   if (grid > 0x7FFFFFFFll) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid);
-  if (mode == kGemmPartial) return launch_one<kGemmPartial>(p, g, st);
-  if (mode == kGemmSwiglu) return launch_one<kGemmSwiglu>(p, g, st);
-  if (mode == kGemmArgmax) return launch_one<kGemmArgmax>(p, g, st);
-  return hipErrorInvalidValue;
+  return bm == 256 ? launch_mode<256>(p, mode, g, st) : launch_mode<128>(p, mode, g, st);
 }
 
 }  // namespace dfl

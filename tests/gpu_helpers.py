@@ -151,7 +151,8 @@ SHAPES = {
                                      head_dim=64, intermediate=8192, vocab=1024, n_tap=2, block=16,
                                      batch=2, ctx_len=0),
     # 19 sequences x 16 rows = 304 block rows: every layer GEMM on the
-    # large-tile kernel (two 256-row tiles, the second ragged; split-K qkv/o/down,
+    # large-tile kernel (qkv and o on two 256-row tiles, the second ragged;
+    # down and fuse split-K over three 128-row tiles, the last ragged;
     # single-pass SwiGLU), the LM head over 285 rows with a vocabulary that ends
     # inside a 256-column tile; ingests of up to 300 rows take it too
     "big-b19": synth.DraftConfig(name="big-b19", hidden=256, n_layers=2, n_q_heads=4, n_kv_heads=2,
