@@ -70,6 +70,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct GemmPlan {
   bool big;    // large-tile kernel (bm x 256 tiles) over all rows
   int bm = 256;  // large-tile kernel: activation rows per tile (256 or 128)
+  int bn = 256;  // large-tile kernel: weight rows per tile (256, or 192 for the SwiGLU)
   bool tiled;  // LDS-tiled kernel over all rows, or the streaming kernel per kGemmRows rows
   int mt, nf;  // streaming: activation tiles and weight fragments per workgroup
   int ng;      // tiled: weight row groups per wave (64*ng columns per workgroup); mt: 16-row tiles
@@ -123,7 +124,16 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
     g.big = true;
     g.tiled = false;
     g.mt = g.nf = g.ng = 0;
-    const long long cols = cdiv(N, dfl::gemm_big_cols(mode)) * nz;
+    // A SwiGLU grid of 256 x 256 tiles short of one round of kBigSlots takes
+    // 256 x 192 tiles where those fit one round (512 rows of the Qwen3-8B-
+    // shaped drafter: 192 -> 256 workgroups)
+    if (mode == dfl::kGemmSwiglu) {
+      const long long m256 = cdiv(M, 256) * nz;
+      if (m256 * cdiv(N, dfl::gemm_big_cols(mode, 256)) < kBigSlots &&
+          m256 * cdiv(N, dfl::gemm_big_cols(mode, 192)) <= kBigSlots)
+        g.bn = 192;
+    }
+    const long long cols = cdiv(N, dfl::gemm_big_cols(mode, g.bn)) * nz;
     const int chunks = K / 32;
     auto split = [&](int bm, int* per) {
       const long long base = cdiv(M, bm) * cols;
@@ -223,7 +233,7 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
 // tile and row).
 int lm_tiles(const dflash_config& c, int M) {
   const GemmPlan g = plan_gemm(M, c.vocab, c.hidden, 1, dfl::kGemmArgmax);
-  if (g.big) return (int)cdiv(c.vocab, dfl::gemm_big_cols(dfl::kGemmArgmax));
+  if (g.big) return (int)cdiv(c.vocab, dfl::gemm_big_cols(dfl::kGemmArgmax, g.bn));
   return (int)(g.tiled ? cdiv(c.vocab, 64 * g.ng) : cdiv(c.vocab, 16 * g.nf));
 }
 
@@ -309,7 +319,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     p.P = c.P;
     p.p_s_stride = (long long)c.M * c.N;
     p.p_z_stride = (long long)g.splits * c.M * c.N;
-    if (g.big) return dfl::launch_gemm_big(p, c.mode, c.nz, g.bm, st);
+    if (g.big) return dfl::launch_gemm_big(p, c.mode, c.nz, g.bm, g.bn, st);
     return g.ws ? dfl::launch_gemm_ws(p, g.ng, g.mt, c.mode, c.nz, st)
                 : dfl::launch_gemm_tile(p, g.ng, g.mt, c.mode, c.nz, st);
   }
