@@ -1,18 +1,23 @@
-// Large-tile bf16 MFMA GEMM for many activation rows (M >= 256), gfx950.
+// Large-tile bf16 MFMA GEMM with both operands staged by direct loads, gfx950:
+// for many activation rows (M >= 256) and for the split-K partials of one
+// 65..128-row tile.
 //
 // Y[m][n] = sum_k A[m][k] * W[n][k], W in the packed fragment layout and A
 // row-major (optionally gathered rows). With hundreds to thousands of rows the
 // product is bound by the matrix cores, and the kernel is laid out for their
 // operand traffic rather than for the weight stream:
 //   * workgroup = 8 waves over a BM (rows of A) x BN (weight rows) tile:
-//     256 x 256, 128 x 256 or 256 x 192. Over 256 weight rows, wave w owns
-//     BM / 2 rows (w & 1) x 64 weight rows (w >> 1): at BM = 256, 32 MFMA
+//     256 x 256, 128 x 256, 128 x 128 or 256 x 192. With WM = 2, wave w owns
+//     BM / 2 rows (w & 1) x BN / 4 weight rows (w >> 1): at 256 x 256, 32 MFMA
 //     tiles of 16 x 16 and 128 accumulator registers (two waves per SIMD; a
 //     4-wave layout of 128 x 128 wave tiles, one wave per SIMD, measured
 //     10-25% slower: nothing hides its LDS latency). BM = 128 reads more LDS
 //     per MFMA but doubles the tiles, for products whose 256-row grid would
 //     need split-K: half the splits, half the fp32 partials written here and
-//     read by the next pass. The 256 x 192 SwiGLU tile (four waves of 64 rows
+//     read by the next pass; 128 x 128 serves one tile of 65..128 rows, where
+//     the product is still bound by the weight stream and the five stages of
+//     direct loads keep 40 KB of weights in flight per workgroup. The
+//     256 x 192 SwiGLU tile (four waves of 64 rows
 //     along A, two of 96 weight rows = 48 gate and 48 up rows) fills one
 //     round of 256 CUs where 256 x 256 tiles leave a quarter of them idle;
 //   * both operands go HBM/L2 -> LDS by gfx950's direct loads
@@ -382,7 +387,7 @@ int gemm_big_cols(int mode, int bn) { return mode == kGemmSwiglu ? bn / 2 : bn; 
 hipError_t launch_gemm_big(const GemmParams& p, int mode, int nz, int bm, int bn, hipStream_t st) {
   // tile shapes: 256 x 256 for every mode, 128 x 256 for split-K partials,
   // 256 x 192 (four waves along the rows) for the SwiGLU
-  const bool ok = (bm == 256 && bn == 256) || (mode == kGemmPartial && bm == 128 && bn == 256) ||
+  const bool ok = (bm == 256 && bn == 256) || (mode == kGemmPartial && bm == 128 && (bn == 256 || bn == 128)) ||
                   (mode == kGemmSwiglu && bm == 256 && bn == 192);
   if (!ok) return hipErrorInvalidValue;
   if (p.K % 32 || p.k_per_split % 32 || p.k_per_split < 32 || p.n_mats != nz || p.M < 1 || p.N < 16)
@@ -398,8 +403,10 @@ hipError_t launch_gemm_big(const GemmParams& p, int mode, int nz, int bm, int bn
   const long long grid = (total + 7) / 8 * 8;
   if (grid > 0x7FFFFFFFll) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid);
-  if (mode == kGemmPartial)
-    return bm == 256 ? launch_one<kGemmPartial, 256, 256, 2>(p, g, st) : launch_one<kGemmPartial, 128, 256, 2>(p, g, st);
+  if (mode == kGemmPartial) {
+    if (bm == 256) return launch_one<kGemmPartial, 256, 256, 2>(p, g, st);
+    return bn == 256 ? launch_one<kGemmPartial, 128, 256, 2>(p, g, st) : launch_one<kGemmPartial, 128, 128, 2>(p, g, st);
+  }
   if (mode == kGemmSwiglu)
     return bn == 256 ? launch_one<kGemmSwiglu, 256, 256, 2>(p, g, st) : launch_one<kGemmSwiglu, 256, 192, 4>(p, g, st);
   if (mode == kGemmArgmax) return launch_one<kGemmArgmax, 256, 256, 2>(p, g, st);

@@ -76,8 +76,8 @@ hipError_t launch_gemm_tile(const GemmParams& p, int ng, int mt, int mode, int n
 // through registers into an LDS ring (gemm_ws.hip). (ng, mt) in {1, 2} x {4, 8}.
 hipError_t launch_gemm_ws(const GemmParams& p, int ng, int mt, int mode, int nz, hipStream_t st);
 
-// Large-tile variant for M >= 256 (bm x bn tiles of 8 waves: 256 x 256 in
-// every mode, 128 x 256 for split-K partials, 256 x 192 for the SwiGLU; both
+// Large-tile variant (bm x bn tiles of 8 waves: 256 x 256 in every mode,
+// 128 x 256 and 128 x 128 for split-K partials, 256 x 192 for the SwiGLU; both
 // operands staged through LDS by direct loads; K and k_per_split multiples of
 // 32). Argmax keys: one per gemm_big_cols(mode, bn) columns; SwiGLU and argmax
 // take one split.
