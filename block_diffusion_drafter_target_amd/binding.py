@@ -28,7 +28,8 @@ EXPORTED = ("dflash_model_create", "dflash_model_destroy", "dflash_rope_table",
             "dflash_profile_enable", "dflash_profile_read", "dflash_pack_matrix",
             "dflash_target_create", "dflash_target_forward", "dflash_kv_commit",
             "dflash_draft_block_sample", "dflash_verify_sample", "dflash_sample_logits",
-            "dflash_draft_block_noalloc", "dflash_loop_tokens", "dflash_loop_advance")
+            "dflash_draft_block_noalloc", "dflash_loop_tokens", "dflash_loop_advance",
+            "dflash_ingest_rows")
 
 # bytes of the static device workspace behind dflash_draft_block_noalloc
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -90,6 +91,7 @@ def load() -> C.CDLL:
     lib.dflash_draft_block.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp, vp, sz, vp]
     lib.dflash_draft_block_noalloc.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp, vp]
     lib.dflash_loop_tokens.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp]
+    lib.dflash_ingest_rows.argtypes = [vp, C.POINTER(dflash_kv), i32, i32, i32, vp, vp, vp]
     lib.dflash_loop_advance.argtypes = [vp, C.POINTER(dflash_kv), vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.dflash_target_create.argtypes = [C.POINTER(dflash_config), C.POINTER(dflash_weights), vp, C.POINTER(vp)]
     lib.dflash_target_forward.argtypes = [vp, C.POINTER(dflash_kv), vp, i32, vp, vp, vp, vp, sz, vp]
@@ -113,7 +115,7 @@ def load() -> C.CDLL:
                "dflash_draft_block", "dflash_verify_accept", "dflash_target_create",
                "dflash_target_forward", "dflash_kv_commit", "dflash_draft_block_sample",
                "dflash_verify_sample", "dflash_sample_logits", "dflash_draft_block_noalloc",
-               "dflash_loop_tokens", "dflash_loop_advance"):
+               "dflash_loop_tokens", "dflash_loop_advance", "dflash_ingest_rows"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -183,6 +185,11 @@ def dflash_draft_block(model, kv, anchor, draft, dbg_logits, dbg_hidden, ws, ws_
 def dflash_draft_block_noalloc(model, kv, anchor, draft, dbg_logits, dbg_hidden, stream) -> None:
     _check("dflash_draft_block_noalloc", load().dflash_draft_block_noalloc(model, C.byref(kv), anchor, draft,
                                                                            dbg_logits, dbg_hidden, stream))
+
+
+def dflash_ingest_rows(model, kv, seq: int, start: int, n: int, commit_rows, n_commit, stream) -> None:
+    _check("dflash_ingest_rows", load().dflash_ingest_rows(model, C.byref(kv), seq, start, n, commit_rows, n_commit,
+                                                           stream))
 
 
 def dflash_loop_tokens(model, kv, anchor, draft, tokens, stream) -> None:

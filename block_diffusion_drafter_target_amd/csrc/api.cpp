@@ -1207,6 +1207,16 @@ dflash_status dflash_verify_accept(const dflash_model* m, const dflash_kv* kv,
   return hip_status(dfl::launch_verify(p, as_stream(stream)));
 }
 
+dflash_status dflash_ingest_rows(const dflash_model* m, const dflash_kv* kv, int32_t seq, int32_t start, int32_t n,
+                                 int32_t* commit_rows, int32_t* n_commit, void* stream) {
+  if (!m || !commit_rows || !n_commit) return DFLASH_ERR_NULL;
+  if (m->target) return DFLASH_ERR_UNSUPPORTED;
+  const dflash_status ks = check_kv(m, kv);
+  if (ks != DFLASH_OK) return ks;
+  if (seq < 0 || seq >= kv->batch || start < 0 || n < 0 || (long long)start + n > kv->max_ctx) return DFLASH_ERR_SHAPE;
+  return hip_status(dfl::launch_ingest_rows(commit_rows, n_commit, seq, start, n, as_stream(stream)));
+}
+
 dflash_status dflash_loop_tokens(const dflash_model* m, const dflash_kv* kv, const int32_t* anchor,
                                  const int32_t* draft, int32_t* tokens, void* stream) {
   if (!m || !anchor || !draft || !tokens) return DFLASH_ERR_NULL;

@@ -223,6 +223,8 @@ hipError_t launch_kv_commit(const int32_t* commit_rows, const int32_t* n_commit,
                             int max_ctx, int32_t* ctx_len, hipStream_t st);
 
 // On-device loop (loop.hip). tokens[b] = [anchor[b], draft[b][0..B-2]].
+// commit_rows[i] = (i, seq, start + i) for i < n, *n_commit = n (loop.hip).
+hipError_t launch_ingest_rows(int32_t* commit_rows, int32_t* n_commit, int seq, int start, int n, hipStream_t st);
 hipError_t launch_loop_tokens(const int32_t* anchor, const int32_t* draft, int32_t* tokens, int batch, int B,
                               hipStream_t st);
 

@@ -1,7 +1,8 @@
 // Bookkeeping kernels of the on-device speculative loop (gfx950), integer
-// only: the target's input row per sequence, and the end-of-step update that
+// only: the target's input row per sequence, the end-of-step update that
 // appends the emitted tokens to the output and moves the cursor, the running
-// flags, the anchors and the step counter. One wave per sequence.
+// flags, the anchors and the step counter (one wave per sequence), and the
+// commit rows of a context ingest.
 #include "common.h"
 #include "internal.h"
 
@@ -34,7 +35,24 @@ __global__ __launch_bounds__(256) void loop_advance_kernel(const LoopAdvancePara
   }
 }
 
+// commit_rows[i] = (i, seq, start + i) for i < n, *n_commit = n
+__global__ __launch_bounds__(256) void ingest_rows_kernel(int32_t* commit_rows, int32_t* n_commit, int seq, int start,
+                                                          int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) n_commit[0] = n;
+  if (i >= n) return;
+  commit_rows[3 * i] = i;
+  commit_rows[3 * i + 1] = seq;
+  commit_rows[3 * i + 2] = start + i;
+}
+
 }  // namespace
+
+hipError_t launch_ingest_rows(int32_t* commit_rows, int32_t* n_commit, int seq, int start, int n, hipStream_t st) {
+  hipLaunchKernelGGL(ingest_rows_kernel, dim3(n > 0 ? (n + 255) / 256 : 1), dim3(256), 0, st, commit_rows, n_commit, seq,
+                     start, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_loop_tokens(const int32_t* anchor, const int32_t* draft, int32_t* tokens, int batch, int B,
                               hipStream_t st) {

@@ -225,12 +225,11 @@ class Drafter:
         if n > self.max_rows:
             raise ValueError("ingest rows exceed max_rows of the workspace")
         self.fuse_ctx(taps, n, ctx)
-        # commit rows (src, seq, pos) built on the device: no host round trip
-        # between the two calls
-        i32 = dict(dtype=torch.int32, device=self.device)
-        ar = torch.arange(n, **i32)
-        rows = torch.stack([ar, torch.full((n,), b, **i32), ar + start], dim=1).contiguous()
-        cnt = torch.full((1,), n, **i32)
+        # commit rows (src, seq, pos) written by the library on the device: no
+        # host round trip between the calls
+        rows = torch.empty((max(n, 1), 3), dtype=torch.int32, device=self.device)
+        cnt = torch.empty((1,), dtype=torch.int32, device=self.device)
+        bd.dflash_ingest_rows(self.model, self.kv, int(b), int(start), n, bd.ptr(rows), bd.ptr(cnt), self.stream())
         self.inject_kv(ctx, n, rows, cnt, n)
 
 

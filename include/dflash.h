@@ -348,6 +348,17 @@ dflash_status dflash_target_forward(const dflash_model* m, dflash_kv* kv, const 
 dflash_status dflash_kv_commit(const dflash_model* m, dflash_kv* kv, const int32_t* commit_rows,
                                const int32_t* n_commit, int32_t max_commit, void* stream);
 
+/* Commit rows of a context ingest: commit_rows[i] = (i, seq, start + i) for
+ * i < n and *n_commit = n, the rows dflash_inject_kv takes to inject n fused
+ * context rows of sequence seq at positions start .. start + n - 1 (the
+ * context is injected as the target writes it, [P3 "L'idea chiave: Il
+ * target sa meglio"]).
+ *   commit_rows  device int32 [n, 3] out; n_commit device int32 [1] out
+ * 0 <= seq < batch, start >= 0, n >= 0 and start + n <= max_ctx, else
+ * DFLASH_ERR_SHAPE before any launch. */
+dflash_status dflash_ingest_rows(const dflash_model* m, const dflash_kv* kv, int32_t seq, int32_t start, int32_t n,
+                                 int32_t* commit_rows, int32_t* n_commit, void* stream);
+
 /* On-device speculative loop: the two steps of the greedy loop that are
  * neither drafting, verification nor commit, so that a whole step (draft
  * block, target pass, verify, commits, fuse, inject, advance) runs without

@@ -311,5 +311,13 @@ def test_loop_entry_points_check_arguments_without_a_gpu():
                                        None) == bd.DFLASH_ERR_SHAPE
         assert lib.dflash_loop_advance(h, C.byref(kv), p, p, p, p, p, 10, 10, None, p, p, None,
                                        None) == bd.DFLASH_ERR_NULL
+        # ingest rows: sequence out of range, negative start or count, past the cache, null outputs
+        assert lib.dflash_ingest_rows(h, C.byref(kv), 2, 0, 4, p, p, None) == bd.DFLASH_ERR_SHAPE
+        assert lib.dflash_ingest_rows(h, C.byref(kv), -1, 0, 4, p, p, None) == bd.DFLASH_ERR_SHAPE
+        assert lib.dflash_ingest_rows(h, C.byref(kv), 0, -1, 4, p, p, None) == bd.DFLASH_ERR_SHAPE
+        assert lib.dflash_ingest_rows(h, C.byref(kv), 0, 0, -4, p, p, None) == bd.DFLASH_ERR_SHAPE
+        assert lib.dflash_ingest_rows(h, C.byref(kv), 1, 2040, 9, p, p, None) == bd.DFLASH_ERR_SHAPE
+        assert lib.dflash_ingest_rows(h, C.byref(kv), 0, 0, 4, None, p, None) == bd.DFLASH_ERR_NULL
+        assert lib.dflash_ingest_rows(h, C.byref(kv), 0, 0, 4, p, None, None) == bd.DFLASH_ERR_NULL
     finally:
         bd.dflash_model_destroy(h)

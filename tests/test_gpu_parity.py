@@ -62,6 +62,45 @@ def test_pack_matrix_layout(gpu_lib):
         assert np.array_equal(got.reshape(rows, cols), want)
 
 
+def test_ingest_rows_and_offset_ingest(gpu_lib):
+    """The commit rows of a context ingest (bit exact, also for n = 0), and an
+    ingest of one sequence in two parts, the second at an offset: the cache
+    slots of both parts against the oracle's injection at those positions,
+    the other sequences untouched."""
+    torch = _torch()
+    from block_diffusion_drafter_target_amd import binding as bd
+    cfg = gh.SHAPES["b12"]
+    gh.log("[ingest rows] b12, sequence 1: 7 rows at 0, then 20 at 7")
+    W = synth.make_weights(cfg, gains="random")
+    WO = gh.oracle_weights(W)
+    ocfg = ref.OracleConfig.from_any(cfg)
+    dr = Drafter(cfg, W, batch=3, max_ctx=64, max_rows=32)
+    rows = torch.full((9, 3), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    bd.dflash_ingest_rows(dr.model, dr.kv, 2, 5, 9, bd.ptr(rows), bd.ptr(cnt), dr.stream())
+    torch.cuda.synchronize()
+    want = np.stack([np.arange(9), np.full(9, 2), 5 + np.arange(9)], axis=1)
+    assert np.array_equal(rows.cpu().numpy(), want) and int(cnt.item()) == 9
+    bd.dflash_ingest_rows(dr.model, dr.kv, 0, 64, 0, bd.ptr(rows), bd.ptr(cnt), dr.stream())
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 0 and np.array_equal(rows.cpu().numpy(), want)
+    t0, t1 = synth.make_taps(cfg, 7, tid=0), synth.make_taps(cfg, 20, tid=1)
+    dev = lambda t: torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).to("cuda")
+    dr.ingest(1, dev(t0), start=0)
+    dr.ingest(1, dev(t1), start=7)
+    torch.cuda.synchronize()
+    cache = ref.new_cache(ocfg, 3, 64)
+    ref.inject_kv(ocfg, WO, ref.fuse_ctx(ocfg, WO, synth.bf16_to_f64(t0)), [(r, 1, r) for r in range(7)], cache)
+    ref.inject_kv(ocfg, WO, ref.fuse_ctx(ocfg, WO, synth.bf16_to_f64(t1)), [(r, 1, 7 + r) for r in range(20)], cache)
+    assert dr.ctx_len.cpu().tolist() == [0, 27, 0]
+    for l in range(cfg.n_layers):
+        k, v = gpu_cache(dr, l, 1, 27)
+        gh.check_rel(k, cache["k"][l, 1, :27], what=f"K layer {l}", axis=1)
+        gh.check_rel(v, cache["v"][l, 1, :27], what=f"V layer {l}", axis=1)
+        for b in (0, 2):
+            assert not dr.k[l, b].abs().sum().item() and not dr.v[l, b].abs().sum().item()
+
+
 # every shape with unit gains, and the shapes below again with random gains
 # (each gain vector its own draw, so a swapped, unused or misindexed gain
 # changes the compared values)
