@@ -87,24 +87,28 @@ constexpr int kWsSlots = 256;        // deep-prefetch tiled workgroups per round
 constexpr int kWsSwigluMinWGs = 128; // single-pass SwiGLU workgroups from which that kernel takes it
 constexpr int kWsMinK = 8192;        // partial-mode K from which that kernel takes it
 
-// Kernel, tile shape and split-K for Y = A W^T.
-// From kBigMinRows rows: the large-tile kernel (256 x 256 tiles, both
-// operands staged through LDS; the product is bound by the matrix cores).
+// Kernel, tile shape and split-K for Y = A W^T (every choice measured on
+// MI355X against the alternatives).
+// From kBigMinRows rows: the large-tile kernel (both operands staged through
+// LDS; the product is bound by the matrix cores), 256 x 256 tiles, 128 x 256
+// where those halve the split-K partials, 256 x 192 for a SwiGLU grid short
+// of one round (see the branch below).
 // Up to kStreamMaxRows rows (or K < 128): the weight-streaming kernel with
-// NF = 2 weight fragments per workgroup (measured best on MI355X with cold
-// caches: more waves in flight beat wider tiles); split-K only in partial
-// mode, to bring the grid to about kTargetWGs workgroups (1024 when there are
-// at most 128 column tiles: longer splits per workgroup measured slower
-// there). Up to kBigMinRows rows: the
-// tiled kernel (activations shared through LDS) with 64 or 128 activation
-// rows per tile. Its split-K partials cost 2*splits*M/K bytes per weight
-// byte: with one row tile (HBM-bound) splits aim for 256 workgroups at 128
-// rows and 384 at 64 rows (64-row tiles also use 64-column tiles), with
-// several row tiles (MFMA-bound) for 512, two per CU (all measured on MI355X
-// against the alternatives). A SwiGLU pass whose single-split grid would have
-// fewer than 256 workgroups runs as a partial-mode GEMM over the concatenated
-// gate and up rows and a combine pass (c4: 2 splits of 128-column tiles,
-// 58 us against 71 us for the 192-workgroup single pass).
+// NF = 2 weight fragments per workgroup (more waves in flight beat wider
+// tiles with cold caches); split-K only in partial mode, to bring the grid to
+// about kTargetWGs workgroups (1024 when there are at most 128 column tiles:
+// longer splits per workgroup measured slower there).
+// In between: partial-mode products of one 65..128-row tile with K below
+// kWsMinK take the large-tile kernel's 128 x 128 tiles; the rest the tiled
+// kernels (activations shared through LDS) with 64 or 128 activation rows
+// per tile, the deep-prefetch one for the single-pass SwiGLU of at least
+// kWsSwigluMinWGs workgroups and for partial products with K >= kWsMinK.
+// Split-K partials cost 2*splits*M/K bytes per weight byte: with one row
+// tile (HBM-bound) splits aim for 256 workgroups at 128 rows and 384 at 64
+// rows (64-row tiles also use 64-column tiles), with several row tiles
+// (MFMA-bound) for 512, two per CU. A SwiGLU whose single-pass grid would be
+// smaller runs as a partial-mode GEMM over the concatenated gate and up rows
+// and a combine pass.
 GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
   GemmPlan g;
   g.swiglu_split = false;
@@ -188,9 +192,10 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
     const int slabs = (int)cdiv(K, 128);
     // the deep-prefetch tiled kernel (gemm_ws.hip) for the single-pass SwiGLU
     // with at least kWsSwigluMinWGs workgroups and for partial-mode products
-    // over long K: there it beats the other tiled kernel (c4: gate/up 67 ->
-    // 62 us, down 36 -> 34, fuse 51 -> 46 per launch); elsewhere (qkv, o, the
-    // LM head, the gpt-oss-shaped 64-row GEMMs) it measured equal or slower
+    // over long K: there it beats the other tiled kernel (Qwen3-8B-shaped
+    // drafter, batch 8 x block 16: gate/up 67 -> 62 us, down 36 -> 34, fuse
+    // 51 -> 46 per launch); elsewhere (qkv, o, the LM head, the gpt-oss-shaped
+    // 64-row GEMMs) it measured equal or slower
     g.ws = (mode == dfl::kGemmSwiglu && cdiv(N, 64) * m_tiles * nz >= kWsSwigluMinWGs) ||
            (mode == dfl::kGemmPartial && K >= kWsMinK);
     if (g.ws) {
@@ -421,9 +426,11 @@ AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx, int B) {
   a.n_ranges = a.n_chunks * batch;
   a.slots = a.n_ranges;
   // 64-key slices at every shape: measured on MI355X against 128-key slices,
-  // equal or faster everywhere (c4 303 -> 274 us, c3 466 -> 444, c5 538 ->
-  // 530 per step), mostly because a chunk rounds up to whole slices and the
-  // block's B keys push each chunk over a slice boundary
+  // equal or faster everywhere (batch 8 at context 8192: 303 -> 274 us per
+  // step, batch 32 at contexts 512..4096: 466 -> 444, the gpt-oss-shaped
+  // batch 4 at context 32768: 538 -> 530), mostly because a chunk rounds up
+  // to whole slices and the block's B keys push each chunk over a slice
+  // boundary
   a.slice = 64;
   return a;
 }
