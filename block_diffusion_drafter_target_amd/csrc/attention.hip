@@ -405,19 +405,23 @@ void attn_kernel(const AttnParams p) {
 
 // o[m][h] = sum_c exp2(m_c - M) O_c / sum_c exp2(m_c - M) l_c over the
 // chunks of the sequence. One wave per (row, head); lane c holds chunk c's
-// statistics, lane d output elements d and d + 64. The statistics and the
-// first NB chunks' partial outputs are loaded in one round trip (NB covers
-// the typical chunk count up to 32; more take further rounds); the weights
-// are applied once the wave's maximum is known.
-template <int NB>
+// statistics, lane i output elements E i .. E i + E - 1 (E = D / 64, one
+// load of E floats per chunk). The statistics and the first NB chunks'
+// partial outputs are loaded in one round trip (NB covers the typical chunk
+// count up to 32; more take further rounds); the weights are applied once
+// the wave's maximum is known.
+template <int NB, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   constexpr int kMergeBatch = NB;
+  constexpr int E = D / 64;
+  static_assert(E == 1 || E == 2, "head size 64 or 128");
+  typedef float fE __attribute__((ext_vector_type(E)));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = blockIdx.y;
   const int h = blockIdx.x * 4 + wave;
   if (h >= p.Hq) return;
   const int b = m / p.B, j = m % p.B;
-  bf16_t* out = p.out + ((long long)m * p.Hq + h) * p.D;
+  bf16_t* out = p.out + ((long long)m * p.Hq + h) * D;
   const int st = p.status[b];
   const int G = p.Hq / p.Hkv;
   const int g = h / G, rr = (h % G) * p.B + j;
@@ -428,22 +432,19 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   // (a sequence without chunks may have s0 == slots: its loads, never used,
   // stay in the buffer)
   const long long base = (long long)g * p.slots + min(s0, p.slots - 1);
-  const bool two = p.D > 64;
   // Loads are unconditional at clamped chunk indexes: a guarded load becomes a
   // branch, and the compiler waits for every outstanding load where branches
   // join. Chunks past nch carry weight 0.
   const int clast = max(nch - 1, 0);
-  const int d2 = two ? lane + 64 : lane;
   const long long sl = (base + min(lane, clast)) * p.gb_pad + rr;
   float mc = p.pm[sl];
   float lc = p.pl[sl];
-  float a[kMergeBatch], bb[kMergeBatch];
+  fE a[kMergeBatch];
   auto load = [&](int c0) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < kMergeBatch; ++t) {
-      const float* po = p.po + ((base + min(c0 + t, clast)) * p.gb_pad + rr) * p.D;
-      a[t] = po[lane];
-      bb[t] = po[d2];
+      const float* po = p.po + ((base + min(c0 + t, clast)) * p.gb_pad + rr) * D;
+      a[t] = *reinterpret_cast<const fE*>(po + E * lane);
     }
   };
   load(0);
@@ -456,26 +457,24 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const float M = wave_max(mc);
   const float w = lane < nch ? fast_exp2(mc - M) : 0.f;
   const float l = wave_sum(w * lc);
-  float o0 = 0.f, o1 = 0.f;
+  fE o = {};
   for (int c0 = 0; c0 < nch; c0 += kMergeBatch) {
     if (c0 > 0) load(c0);
 #pragma unroll
     for (int t = 0; t < kMergeBatch; ++t) {
       const float wc = __shfl(w, (c0 + t) & 63);
-      if (c0 + t < nch) {
-        o0 += wc * a[t];
-        o1 += wc * bb[t];
-      }
+      if (c0 + t < nch) o += wc * a[t];
     }
   }
-  if (st != 0) {
-    out[lane] = 0;
-    if (two) out[lane + 64] = 0;
-    return;
-  }
+  // a sequence with an error status gets zeros (selected, not multiplied:
+  // its partials are never written)
   const float inv = 1.0f / l;
-  out[lane] = f2bf(o0 * inv);
-  if (two) out[lane + 64] = f2bf(o1 * inv);
+  if constexpr (E == 1) {
+    out[lane] = f2bf(st != 0 ? 0.f : o[0] * inv);
+  } else {
+    *reinterpret_cast<uint32_t*>(out + 2 * lane) =
+        pack_bf2(st != 0 ? 0.f : o[0] * inv, st != 0 ? 0.f : o[1] * inv);
+  }
 }
 
 template <int D, int SL>
@@ -510,18 +509,25 @@ hipError_t launch_attention(const AttnParams& p, int D, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+template <int D>
+hipError_t launch_merge_d(const MergeParams& p, dim3 grid, hipStream_t st) {
+  if (p.seg_hint <= 4)
+    hipLaunchKernelGGL((merge_kernel<4, D>), grid, dim3(256), 0, st, p);
+  else if (p.seg_hint <= 8)
+    hipLaunchKernelGGL((merge_kernel<8, D>), grid, dim3(256), 0, st, p);
+  else if (p.seg_hint <= 16)
+    hipLaunchKernelGGL((merge_kernel<16, D>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((merge_kernel<32, D>), grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t st) {
   if (p.n_ranges < p.batch || p.batch < 1 || p.slots < p.n_ranges) return hipErrorInvalidValue;
   const dim3 grid((p.Hq + 3) / 4, p.batch * p.B);
-  if (p.seg_hint <= 4)
-    hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(256), 0, st, p);
-  else if (p.seg_hint <= 8)
-    hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(256), 0, st, p);
-  else if (p.seg_hint <= 16)
-    hipLaunchKernelGGL(merge_kernel<16>, grid, dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL(merge_kernel<32>, grid, dim3(256), 0, st, p);
-  return hipGetLastError();
+  if (p.D == 64) return launch_merge_d<64>(p, grid, st);
+  if (p.D == 128) return launch_merge_d<128>(p, grid, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dfl
