@@ -121,12 +121,20 @@ void gemm_tile_kernel(const GemmParams p) {
                          : __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[f] + (long long)(kk >> 5) * 512));
     }
     // k past the end (K % 128 == 64 on the last slab) re-reads the row's last
-    // chunk; those values are masked where they are used
+    // chunk; those values are zeroed before they reach LDS
     const int kx = min(k0 + xch, p.K - 8);
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) xs[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + kx);
   };
-  auto store = [&](int buf) __attribute__((always_inline)) {
+  // chunks at k >= kend (the last slab when K % 128 == 64) are stored as
+  // zeros, so the MFMAs need no mask
+  auto store = [&](int buf, int k0) __attribute__((always_inline)) {
+    if (k0 + kBK > kend) {  // uniform over the workgroup
+      const bool zero = k0 + xch >= kend;
+#pragma unroll
+      for (int i = 0; i < kXPer; ++i)
+        if (zero) xs[i] = u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
       const int e = threadIdx.x + 256 * i;
@@ -144,7 +152,7 @@ void gemm_tile_kernel(const GemmParams p) {
   int buf = 0;
   if (kbeg < kend) {
     load(kbeg);
-    store(0);
+    store(0, kbeg);
     __syncthreads();
   }
   for (int k0 = kbeg; k0 < kend; k0 += kBK) {
@@ -157,17 +165,16 @@ void gemm_tile_kernel(const GemmParams p) {
     if (more) load(k0 + kBK);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t keep = (k0 + 32 * u < kend) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const int row = t * 16 + r;
-        const u32x4 b = sx[buf][row * 16 + ((u * 4 + g) ^ (row & 15))] & keep;
+        const u32x4 b = sx[buf][row * 16 + ((u * 4 + g) ^ (row & 15))];
 #pragma unroll
         for (int f = 0; f < NG; ++f) acc[f][t] = mfma16x16x32(wc[f][u], b, acc[f][t]);
       }
     }
     if (more) {
-      store(buf ^ 1);
+      store(buf ^ 1, k0 + kBK);
       __syncthreads();
       buf ^= 1;
     }

@@ -16,7 +16,8 @@
 //     one step later (a ring of two LDS buffers, chunk ch of row r at word
 //     r*16 + (ch ^ (r & 15)): the 16 lanes of one LDS cycle hit 16 bank
 //     groups); the wait for it then leaves the weights of slabs j + 2 and
-//     j + 3 in flight;
+//     j + 3 in flight; chunks past the end of K are stored as zeros, so the
+//     MFMAs read LDS without a mask;
 //   * the fragments of the next 32-k step are read from LDS while the MFMAs of
 //     the current one run;
 //   * whole groups of three slabs run as straight-line code, so the compiler
@@ -109,8 +110,17 @@ void gemm_ws_kernel(const GemmParams p) {
 #pragma unroll
     for (int ii = 0; ii < kXW; ++ii) xr[ii] = *reinterpret_cast<const u32x4*>(xsrc[ii] + kx);
   };
+  // chunks at k >= kend (the last slab when K % 128 == 64) are stored as
+  // zeros, so the MFMAs need no mask; slabs past the end are never read
   auto store_x = [&](int j) __attribute__((always_inline)) {
     u32x4* dst = &sx[j % kRing][0];
+    const int k0 = kbeg + j * kBK;
+    if (k0 + kBK > kend) {  // uniform over the workgroup
+      const bool zero = k0 + xch >= kend;
+#pragma unroll
+      for (int ii = 0; ii < kXW; ++ii)
+        if (zero) xr[ii] = u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int ii = 0; ii < kXW; ++ii) dst[xdst[ii]] = xr[ii];
   };
@@ -168,7 +178,6 @@ void gemm_ws_kernel(const GemmParams p) {
   __syncthreads();
   // one step: slab j from ring slot d (j % D == d) and LDS buffer j % kRing
   auto step = [&](int d, int j) __attribute__((always_inline)) {
-    const int k0 = kbeg + j * kBK;
     const u32x4* xs = &sx[j % kRing][0];
     // the MT activation fragments of k step u + 1 are read from LDS while the
     // MFMAs of step u run
@@ -184,13 +193,10 @@ void gemm_ws_kernel(const GemmParams p) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (u < 3) read_b(u + 1, b[(u + 1) & 1]);
-      const uint32_t keep = (k0 + 32 * u < kend) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const u32x4 bt = b[u & 1][t] & keep;
+      for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int f = 0; f < NG; ++f) acc[f][t] = mfma16x16x32(w[d][f][u], bt, acc[f][t]);
-      }
+        for (int f = 0; f < NG; ++f) acc[f][t] = mfma16x16x32(w[d][f][u], b[u & 1][t], acc[f][t]);
     }
     // X(j+1) (only W(j+2) was issued after it) goes to the buffer of slab
     // j - 1, which every wave finished before the previous barrier

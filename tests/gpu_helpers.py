@@ -165,6 +165,14 @@ SHAPES = {
     "big-b8x40": synth.DraftConfig(name="big-b8x40", hidden=512, n_layers=2, n_q_heads=8, n_kv_heads=2,
                                    head_dim=64, intermediate=1536, vocab=1040, n_tap=2, block=8,
                                    batch=40, ctx_len=0),
+    # K % 128 == 64 on the tiled kernels: hidden 320 (QKV, o's input width
+    # 256 aside, and the LM head on the LDS-tiled kernel over 80 rows, the
+    # last 128-k slab half used) and I = 8256 (gate/up on the deep-prefetch
+    # kernel with 129 workgroups, down on it with K = 8256: both end in a half
+    # slab)
+    "ws-tail": synth.DraftConfig(name="ws-tail", hidden=320, n_layers=1, n_q_heads=4, n_kv_heads=2,
+                                 head_dim=64, intermediate=8256, vocab=1040, n_tap=2, block=16,
+                                 batch=5, ctx_len=0),
     # long contexts: chunks of many 64-key attention slices, G = 8, D = 64
     "long-d64": synth.DraftConfig(name="long-d64", hidden=512, n_layers=1, n_q_heads=64, n_kv_heads=8,
                                   head_dim=64, intermediate=512, vocab=1024, n_tap=2, block=16,
@@ -187,5 +195,5 @@ CTX = {"gqa-d128": [1, 300, 777, 0, 64], "g8-d64": [500, 33], "b12": [129, 0, 64
        "long-d64": [8900, 8500, 8193, 100], "long-d128": [16900, 16000, 9000, 3],
        "mlp-wide": [40, 0, 17, 300, 64, 1, 129, 90, 33, 7], "mlp-wide-b2": [70, 250],
        "big-b19": [0, 1, 17, 64, 129, 260, 300, 33, 90, 5, 200, 150, 75, 12, 280, 45, 100, 3, 64],
-       "big-b8x40": [(37 * i) % 211 for i in range(40)],
+       "big-b8x40": [(37 * i) % 211 for i in range(40)], "ws-tail": [0, 33, 100, 64, 7],
        "ragged-1long": [6000, 0, 1, 5, 17, 3, 64, 2, 0, 9, 33, 1, 7, 0, 12, 4, 65, 1, 2, 8, 0, 3, 1, 6]}
