@@ -316,68 +316,141 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
 // ---------------------------------------------------------------------------
 // KV injection epilogue: for commit row i and layer l, k = RoPE(RMSNorm_head(
 // W_k c)), v = W_v c, scattered to (seq, pos); ctx_len[seq] grows to pos + 1.
-// One wave per (block of kInjectRows commit rows, layer, head): the commit
-// rows, split partials and RoPE rows of the whole block are loaded before any
-// arithmetic (a wave per single row left the context ingest bound by workgroup
-// starts: 81,920 workgroups of under 1 KB each for a 4096-row chunk).
-constexpr int kInjectRows = 8;
+// One wave per (block of kInjectRows commit rows, layer, head), D/8 lanes per
+// row: lane q of a row holds dimensions 4q..4q+3 and their RoPE partners
+// 4q+D/2..4q+D/2+3, so the fp32 partials and the (cos, sin) row arrive in
+// 16-byte loads and K/V leave in 8-byte stores; a wave covers 512/D rows per
+// round, and the commit rows, partials and RoPE rows of every round are
+// loaded before any arithmetic (one float per lane and a wave per head of 8
+// rows ran the 4096-row ingest chunk's pass at 1.8 TB/s).
+constexpr int kInjectRows = 16;
 
+// x1/x2 += splits 1.. of the lane's two 4-dimension groups for every round
+// (split 0 is already in x1/x2); SB splits per batch of loads, all issued
+// before the adds (clamped split index: unconditional loads)
+template <int NR, int SB>
+__device__ __forceinline__ void inject_add_splits(f32x4_t (&x1)[NR], f32x4_t (&x2)[NR],
+                                                  const float* const (&src)[NR], long long s_stride, int splits,
+                                                  int half) {
+  for (int s0 = 1; s0 < splits; s0 += SB) {
+    f32x4_t a[SB][NR], b[SB][NR];
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float* q = src[r] + (long long)min(s0 + j, splits - 1) * s_stride;
+        a[j][r] = *reinterpret_cast<const f32x4_t*>(q);
+        b[j][r] = *reinterpret_cast<const f32x4_t*>(q + half);
+      }
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+      if (s0 + j < splits)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          x1[r] += a[j][r];
+          x2[r] += b[j][r];
+        }
+  }
+}
+
+template <int D>
 __global__ __launch_bounds__(256) void inject_post_kernel(const InjectPostParams p) {
+  constexpr int half = D / 2;
+  constexpr int LPR = D / 8;               // lanes per row
+  constexpr int RPR = 64 / LPR;            // rows per round
+  constexpr int NR = kInjectRows / RPR;    // rounds
+  static_assert(NR * RPR == kInjectRows, "rows per wave");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane % LPR, rs = lane / LPR;
+  const int d0 = 4 * q;
   const int i0 = p.c0 + blockIdx.x * kInjectRows, l = blockIdx.y;
   const int head = blockIdx.z * 4 + wave;
   if (head >= 2 * p.Hkv) return;
-  const int D = p.D, half = D >> 1;
   const int width = 2 * p.Hkv * D;
-  const bool active = lane < half;
-  const int li = active ? lane : 0;
   int nc = *p.n_commit;
   nc = nc < 0 ? 0 : (nc > p.max_commit ? p.max_commit : nc);
-  const int iend = min(min(nc, p.c1), i0 + kInjectRows);
-  int src[kInjectRows], seq[kInjectRows], pos[kInjectRows];
-  float x1[kInjectRows], x2[kInjectRows];
-  float2 cs[kInjectRows];
+  const int iend = min(nc, p.c1);
+  const bool is_k = head < p.Hkv;
+  // split 0 of the partials first (the bytes that matter), then the commit
+  // rows, then the RoPE rows of K heads (they need the positions)
+  const float* psrc[NR];
+  f32x4_t x1[NR], x2[NR];
 #pragma unroll
-  for (int r = 0; r < kInjectRows; ++r) {  // clamped rows: every load in bounds, results unused
-    const int i = min(i0 + r, p.c1 - 1);
+  for (int r = 0; r < NR; ++r) {  // clamped rows: every load in bounds, results unused
+    const int i = min(i0 + r * RPR + rs, p.c1 - 1);
+    psrc[r] = p.P + (long long)l * p.p_z_stride + (long long)(i - p.c0) * width + head * D + d0;
+    x1[r] = *reinterpret_cast<const f32x4_t*>(psrc[r]);
+    x2[r] = *reinterpret_cast<const f32x4_t*>(psrc[r] + half);
+  }
+  int src[NR], seq[NR], pos[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int i = min(i0 + r * RPR + rs, p.c1 - 1);
     src[r] = p.commit_rows[3 * i];
     seq[r] = p.commit_rows[3 * i + 1];
     pos[r] = p.commit_rows[3 * i + 2];
   }
+  // (cos, sin) of dimensions d0..d0+3 at the row's position: two 16-byte loads
+  f32x4_t cs0[NR], cs1[NR];
 #pragma unroll
-  for (int r = 0; r < kInjectRows; ++r) {
-    const int i = min(i0 + r, p.c1 - 1);
-    sum_pair(p.P + (long long)l * p.p_z_stride + (long long)(i - p.c0) * width + head * D + li, p.p_s_stride,
-             p.splits, half, active, x1[r], x2[r]);
-    const int rpos = pos[r] < 0 ? 0 : (pos[r] >= p.rope_max ? p.rope_max - 1 : pos[r]);
-    cs[r] = reinterpret_cast<const float2*>(p.rope)[(long long)rpos * half + li];
+  for (int r = 0; r < NR; ++r) cs0[r] = cs1[r] = f32x4_t{1.f, 0.f, 1.f, 0.f};
+  if (is_k) {  // uniform over the wave
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int rpos = pos[r] < 0 ? 0 : (pos[r] >= p.rope_max ? p.rope_max - 1 : pos[r]);
+      const f32x4_t* rp = reinterpret_cast<const f32x4_t*>(p.rope + ((long long)rpos * half + d0) * 2);
+      cs0[r] = rp[0];
+      cs1[r] = rp[1];
+    }
   }
-  const float g1 = bf2f(p.gk[l][li]), g2 = bf2f(p.gk[l][li + half]);
-  const bool first = l == 0 && blockIdx.z == 0 && threadIdx.x == 0;
+  // batches of at most two further splits hold the head size 128 kernel to
+  // three waves per SIMD (four-split batches took 186 registers)
+  if (p.splits > 1) inject_add_splits<NR, 2>(x1, x2, psrc, p.p_s_stride, p.splits, half);
+  const u32x2 gw1 = *reinterpret_cast<const u32x2*>(p.gk[l] + d0);
+  const u32x2 gw2 = *reinterpret_cast<const u32x2*>(p.gk[l] + d0 + half);
+  const f32x4_t g1 = bf4_to_f32(gw1), g2 = bf4_to_f32(gw2);
+  // one lane per row records the context length and capacity errors
+  const bool first = l == 0 && blockIdx.z == 0 && wave == 0 && q == 0;
   const int g = head < p.Hkv ? head : head - p.Hkv;
 #pragma unroll
-  for (int r = 0; r < kInjectRows; ++r) {
-    if (i0 + r >= iend) break;
+  for (int r = 0; r < NR; ++r) {
+    // the head's sum of squares over the row's LPR lanes (every lane takes
+    // part in the shuffles, valid row or not)
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += x1[r][e] * x1[r][e] + x2[r][e] * x2[r][e];
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) ss += __shfl_xor(ss, o);
+    const int i = i0 + r * RPR + rs;
+    if (i >= iend) continue;
     if (src[r] < 0 || src[r] >= p.n_ctx_rows || seq[r] < 0 || seq[r] >= p.batch) continue;
     if (pos[r] < 0 || pos[r] >= p.max_ctx || pos[r] >= p.rope_max) {
       if (first) p.status[seq[r]] = kErrCapacity;
       continue;
     }
-    const long long off = ((((long long)l * p.batch + seq[r]) * p.Hkv + g) * p.max_ctx + pos[r]) * D;
-    if (head >= p.Hkv) {
-      if (active) {
-        p.vc[off + lane] = f2bf(x1[r]);
-        p.vc[off + lane + half] = f2bf(x2[r]);
-      }
+    const long long off = ((((long long)l * p.batch + seq[r]) * p.Hkv + g) * p.max_ctx + pos[r]) * D + d0;
+    u32x2 lo, hi;
+    if (!is_k) {
+      lo = u32x2{pack_bf2(x1[r][0], x1[r][1]), pack_bf2(x1[r][2], x1[r][3])};
+      hi = u32x2{pack_bf2(x2[r][0], x2[r][1]), pack_bf2(x2[r][2], x2[r][3])};
+      *reinterpret_cast<u32x2*>(p.vc + off) = lo;
+      *reinterpret_cast<u32x2*>(p.vc + off + half) = hi;
     } else {
-      const float ss = wave_sum(x1[r] * x1[r] + x2[r] * x2[r]);
       const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
-      if (active) {
-        const float y1 = x1[r] * inv * g1;
-        const float y2 = x2[r] * inv * g2;
-        p.kc[off + lane] = f2bf(y1 * cs[r].x - y2 * cs[r].y);
-        p.kc[off + lane + half] = f2bf(y1 * cs[r].y + y2 * cs[r].x);
+      const float c[4] = {cs0[r][0], cs0[r][2], cs1[r][0], cs1[r][2]};
+      const float sn[4] = {cs0[r][1], cs0[r][3], cs1[r][1], cs1[r][3]};
+      float k1[4], k2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float y1 = x1[r][e] * inv * g1[e];
+        const float y2 = x2[r][e] * inv * g2[e];
+        k1[e] = y1 * c[e] - y2 * sn[e];
+        k2[e] = y1 * sn[e] + y2 * c[e];
       }
+      lo = u32x2{pack_bf2(k1[0], k1[1]), pack_bf2(k1[2], k1[3])};
+      hi = u32x2{pack_bf2(k2[0], k2[1]), pack_bf2(k2[2], k2[3])};
+      *reinterpret_cast<u32x2*>(p.kc + off) = lo;
+      *reinterpret_cast<u32x2*>(p.kc + off + half) = hi;
     }
     if (first) atomicMax(p.ctx_len + seq[r], pos[r] + 1);
   }
@@ -503,8 +576,13 @@ hipError_t launch_qkv_post(const QkvPostParams& p, hipStream_t st) {
 
 hipError_t launch_inject_post(const InjectPostParams& p, hipStream_t st) {
   if (p.c1 <= p.c0) return hipSuccess;
-  hipLaunchKernelGGL(inject_post_kernel, dim3((p.c1 - p.c0 + kInjectRows - 1) / kInjectRows, p.n_layers, (2 * p.Hkv + 3) / 4),
-                     dim3(256), 0, st, p);
+  const dim3 grid((p.c1 - p.c0 + kInjectRows - 1) / kInjectRows, p.n_layers, (2 * p.Hkv + 3) / 4);
+  if (p.D == 128)
+    hipLaunchKernelGGL(inject_post_kernel<128>, grid, dim3(256), 0, st, p);
+  else if (p.D == 64)
+    hipLaunchKernelGGL(inject_post_kernel<64>, grid, dim3(256), 0, st, p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
