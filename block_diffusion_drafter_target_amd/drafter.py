@@ -91,6 +91,9 @@ class Drafter:
                                 rope=self.rope.data_ptr(), rope_max_pos=self.rope_max)
         self._c_cfg, self._c_layers, self._c_w = c, layers, wst
         self.model = bd.dflash_model_create(c, wst)
+        # the library's own destroy call, kept here so that __del__ needs no
+        # module globals (they may already be gone at interpreter exit)
+        self._destroy = bd.load().dflash_model_destroy
         # draft KV cache
         NL, Hkv, D = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
         dev = self.device
@@ -116,9 +119,9 @@ class Drafter:
         self.ctx = torch.zeros((self.max_rows, cfg.hidden), dtype=torch.bfloat16, device=dev)
 
     def __del__(self):
-        m = getattr(self, "model", None)
-        if m:
-            bd.dflash_model_destroy(m)
+        m, destroy = getattr(self, "model", None), getattr(self, "_destroy", None)
+        if m and destroy is not None:
+            destroy(m)
             self.model = None
 
     @staticmethod
@@ -276,6 +279,7 @@ class DeviceTarget:
                                 rope=self.rope.data_ptr(), rope_max_pos=self.rope_max)
         self._c_cfg, self._c_layers, self._c_w = c, layers, wst
         self.model = bd.dflash_target_create(c, wst, self.tap_layers)
+        self._destroy = bd.load().dflash_model_destroy
         Hkv, D = cfg.n_kv_heads, cfg.head_dim
         self.k = torch.zeros((n_layers, batch, Hkv, max_ctx, D), dtype=torch.bfloat16, device=self.device)
         self.v = torch.zeros((n_layers, batch, Hkv, max_ctx, D), dtype=torch.bfloat16, device=self.device)
@@ -290,9 +294,9 @@ class DeviceTarget:
                                 device=self.device)
 
     def __del__(self):
-        m = getattr(self, "model", None)
-        if m:
-            bd.dflash_model_destroy(m)
+        m, destroy = getattr(self, "model", None), getattr(self, "_destroy", None)
+        if m and destroy is not None:
+            destroy(m)
             self.model = None
 
     # -- entry points --------------------------------------------------------
