@@ -210,117 +210,6 @@ __global__ __launch_bounds__(kRowThreads) void row_norm_kernel(const RowNormPara
   }
 }
 
-// Sum over splits of two values per lane (pair i, i + D/2 of one head); src
-// is already clamped to a valid lane. Loads are unconditional (see
-// add_splits); lanes that hold no pair (active false) return zeros, so that
-// wave sums over the head see only its D values.
-template <int SB>
-__device__ __forceinline__ void sum_pair_sb(const float* src, long long s_stride, int splits, int half,
-                                            bool active, float& x1, float& x2) {
-  constexpr int kSplitBatch = SB;
-  x1 = 0.f;
-  x2 = 0.f;
-  for (int s0 = 0; s0 < splits; s0 += kSplitBatch) {
-    float a[kSplitBatch], c[kSplitBatch];
-#pragma unroll
-    for (int j = 0; j < kSplitBatch; ++j) {
-      const long long off = (long long)min(s0 + j, splits - 1) * s_stride;
-      a[j] = src[off];
-      c[j] = src[off + half];
-    }
-#pragma unroll
-    for (int j = 0; j < kSplitBatch; ++j) {
-      if (s0 + j < splits) {
-        x1 += a[j];
-        x2 += c[j];
-      }
-    }
-  }
-  if (!active) {
-    x1 = 0.f;
-    x2 = 0.f;
-  }
-}
-
-// Sum of the split partials of a lane's pair (i, i + half), in batches that
-// match the split count (see add_splits).
-__device__ __forceinline__ void sum_pair(const float* src, long long s_stride, int splits, int half,
-                                         bool active, float& x1, float& x2) {
-  if (splits == 1)
-    sum_pair_sb<1>(src, s_stride, splits, half, active, x1, x2);
-  else if (splits <= 2)
-    sum_pair_sb<2>(src, s_stride, splits, half, active, x1, x2);
-  else if (splits <= 4)
-    sum_pair_sb<4>(src, s_stride, splits, half, active, x1, x2);
-  else
-    sum_pair_sb<kSplitBatch>(src, s_stride, splits, half, active, x1, x2);
-}
-
-// ---------------------------------------------------------------------------
-// q/k/v of block rows: sum split partials per head; q and k get a per-head
-// RMSNorm and rotate-half RoPE at position L_b + j; q goes to the query buffer,
-// k and v to cache slot L_b + j (speculative append). One wave per head;
-// lane i < D/2 holds the pair (i, i + D/2).
-__global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m = blockIdx.y;
-  // the extra row of workgroups: the first one's first wave writes the
-  // attention chunk split (the embedding pass has set every status)
-  if (m == p.batch * p.B) {
-    if (blockIdx.x == 0 && wave == 0)
-      attn_plan_wave(p.ctx_len, p.status, p.batch, p.B, p.n_ranges, p.slice, p.plan);
-    return;
-  }
-  const int head = blockIdx.x * 4 + wave;
-  const int nh = p.Hq + 2 * p.Hkv;
-  if (head >= nh) return;
-  const int b = m / p.B, j = m % p.B;
-  const int D = p.D, half = D >> 1;
-  const int width = nh * D;
-  const bool active = lane < half;
-  const int li = active ? lane : 0;
-  // Every load is issued before the sequence's status is known (the status
-  // only decides whether anything is stored); the RoPE row index is clamped
-  // to the table, and a sequence whose position is out of range has a
-  // capacity status from the embedding kernel.
-  const int st = p.status[b];
-  const int pos = p.ctx_len[b] + j;
-  float x1, x2;
-  sum_pair(p.P + (long long)m * width + head * D + li, p.p_s_stride, p.splits, half, active, x1, x2);
-  const bf16_t* gain = head < p.Hq ? p.gq : p.gk;
-  const float g1 = bf2f(gain[li]), g2 = bf2f(gain[li + half]);
-  const int rpos = pos < 0 ? 0 : (pos >= p.rope_max ? p.rope_max - 1 : pos);
-  const float2 cs = reinterpret_cast<const float2*>(p.rope)[(long long)rpos * half + li];
-  if (st != 0) return;
-  if (head >= p.Hq + p.Hkv) {  // v
-    if (active) {
-      const int g = head - p.Hq - p.Hkv;
-      bf16_t* dst = p.vc + (((long long)b * p.Hkv + g) * p.max_ctx + pos) * D;
-      dst[lane] = f2bf(x1);
-      dst[lane + half] = f2bf(x2);
-    }
-    return;
-  }
-  const float ss = wave_sum(x1 * x1 + x2 * x2);
-  const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
-  if (!active) return;
-  const float y1 = x1 * inv * g1;
-  const float y2 = x2 * inv * g2;
-  const float o1 = y1 * cs.x - y2 * cs.y;
-  const float o2 = y1 * cs.y + y2 * cs.x;
-  bf16_t* dst;
-  float sc = 1.f;
-  if (head < p.Hq) {
-    dst = p.q + ((long long)m * p.Hq + head) * D;
-    sc = p.q_scale;  // queries carry the softmax scale (one rounding to bf16)
-  } else {
-    const int g = head - p.Hq;
-    dst = p.kc + (((long long)b * p.Hkv + g) * p.max_ctx + pos) * D;
-  }
-  dst[lane] = f2bf(o1 * sc);
-  dst[lane + half] = f2bf(o2 * sc);
-}
-
 // ---------------------------------------------------------------------------
 // KV injection epilogue: for commit row i and layer l, k = RoPE(RMSNorm_head(
 // W_k c)), v = W_v c, scattered to (seq, pos); ctx_len[seq] grows to pos + 1.
@@ -465,6 +354,121 @@ __global__ __launch_bounds__(256) void inject_post_kernel(const InjectPostParams
 }
 
 // ---------------------------------------------------------------------------
+// q/k/v of block rows: sum split partials per head; q and k get a per-head
+// RMSNorm and rotate-half RoPE at position L_b + j; q goes to the query buffer
+// (times q_scale), k and v to cache slot L_b + j (speculative append).
+// Nothing is stored for a sequence with a nonzero status (the embedding pass
+// has set it, capacity included). One wave per (block of 512/D rows, head),
+// D/8 lanes per row as in inject_post_kernel (lane q: dimensions 4q..4q+3 and
+// their RoPE partners 4q+D/2..): 16-byte loads of the partials and RoPE
+// rows, 8-byte stores, every load of the wave issued before the arithmetic
+// (one wave per (row, head) with a float per lane took 11-15 us per launch at
+// 512 rows); one round of rows per wave keeps a 16-row block spread over
+// many CUs. One more row of workgroups writes the attention chunk split.
+template <int D>
+constexpr int qkv_rows() { return 512 / D; }
+
+template <int D>
+__global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
+  constexpr int half = D / 2;
+  constexpr int LPR = D / 8;              // lanes per row
+  constexpr int RPR = 64 / LPR;           // rows per round
+  constexpr int kQkvRows = qkv_rows<D>();
+  constexpr int NR = kQkvRows / RPR;      // rounds (one)
+  static_assert(NR * RPR == kQkvRows, "rows per wave");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rows = p.batch * p.B;
+  // the extra row of workgroups: the first one's first wave writes the
+  // attention chunk split (the embedding pass has set every status)
+  if ((int)blockIdx.y == (rows + kQkvRows - 1) / kQkvRows) {
+    if (blockIdx.x == 0 && wave == 0)
+      attn_plan_wave(p.ctx_len, p.status, p.batch, p.B, p.n_ranges, p.slice, p.plan);
+    return;
+  }
+  const int head = blockIdx.x * 4 + wave;
+  const int nh = p.Hq + 2 * p.Hkv;
+  if (head >= nh) return;
+  const int qd = lane % LPR, rs = lane / LPR;
+  const int d0 = 4 * qd;
+  const int width = nh * D;
+  const int m0 = blockIdx.y * kQkvRows;
+  const bool is_v = head >= p.Hq + p.Hkv;
+  // split 0 of the partials first, then the rows' sequence state, then the
+  // RoPE rows of q and k heads (they need the positions); clamped rows: every
+  // load in bounds, results unused
+  const float* psrc[NR];
+  f32x4_t x1[NR], x2[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int m = min(m0 + r * RPR + rs, rows - 1);
+    psrc[r] = p.P + (long long)m * width + head * D + d0;
+    x1[r] = *reinterpret_cast<const f32x4_t*>(psrc[r]);
+    x2[r] = *reinterpret_cast<const f32x4_t*>(psrc[r] + half);
+  }
+  int st[NR], pos[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int m = min(m0 + r * RPR + rs, rows - 1);
+    const int b = m / p.B;
+    st[r] = p.status[b];
+    pos[r] = p.ctx_len[b] + m % p.B;
+  }
+  f32x4_t cs0[NR], cs1[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) cs0[r] = cs1[r] = f32x4_t{1.f, 0.f, 1.f, 0.f};
+  if (!is_v) {  // uniform over the wave
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int rpos = pos[r] < 0 ? 0 : (pos[r] >= p.rope_max ? p.rope_max - 1 : pos[r]);
+      const f32x4_t* rp = reinterpret_cast<const f32x4_t*>(p.rope + ((long long)rpos * half + d0) * 2);
+      cs0[r] = rp[0];
+      cs1[r] = rp[1];
+    }
+  }
+  if (p.splits > 1) inject_add_splits<NR, 2>(x1, x2, psrc, p.p_s_stride, p.splits, half);
+  const uint16_t* gain = head < p.Hq ? p.gq : p.gk;
+  const f32x4_t g1 = bf4_to_f32(*reinterpret_cast<const u32x2*>(gain + d0));
+  const f32x4_t g2 = bf4_to_f32(*reinterpret_cast<const u32x2*>(gain + d0 + half));
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    // the head's sum of squares over the row's LPR lanes (every lane takes
+    // part in the shuffles, stored row or not)
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += x1[r][e] * x1[r][e] + x2[r][e] * x2[r][e];
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) ss += __shfl_xor(ss, o);
+    const int m = m0 + r * RPR + rs;
+    if (m >= rows || st[r] != 0) continue;
+    const int b = m / p.B;
+    if (is_v) {
+      const int g = head - p.Hq - p.Hkv;
+      uint16_t* dst = p.vc + (((long long)b * p.Hkv + g) * p.max_ctx + pos[r]) * D + d0;
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf2(x1[r][0], x1[r][1]), pack_bf2(x1[r][2], x1[r][3])};
+      *reinterpret_cast<u32x2*>(dst + half) = u32x2{pack_bf2(x2[r][0], x2[r][1]), pack_bf2(x2[r][2], x2[r][3])};
+      continue;
+    }
+    const float inv = 1.0f / sqrtf(ss / (float)D + p.eps);
+    // queries carry the softmax scale (one rounding to bf16)
+    const float sc = head < p.Hq ? p.q_scale : 1.f;
+    const float c[4] = {cs0[r][0], cs0[r][2], cs1[r][0], cs1[r][2]};
+    const float sn[4] = {cs0[r][1], cs0[r][3], cs1[r][1], cs1[r][3]};
+    float o1[4], o2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float y1 = x1[r][e] * inv * g1[e];
+      const float y2 = x2[r][e] * inv * g2[e];
+      o1[e] = (y1 * c[e] - y2 * sn[e]) * sc;
+      o2[e] = (y1 * sn[e] + y2 * c[e]) * sc;
+    }
+    uint16_t* dst = head < p.Hq ? p.q + ((long long)m * p.Hq + head) * D + d0
+                                : p.kc + (((long long)b * p.Hkv + (head - p.Hq)) * p.max_ctx + pos[r]) * D + d0;
+    *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3])};
+    *reinterpret_cast<u32x2*>(dst + half) = u32x2{pack_bf2(o2[0], o2[1]), pack_bf2(o2[2], o2[3])};
+  }
+}
+
+// ---------------------------------------------------------------------------
 // draft token of one LM row: the maximum key over the LM-head tiles (largest
 // logit, lowest index on ties), unpacked to the index. keys[tile][row] (each
 // GEMM workgroup writes its rows contiguously); 1024 threads with
@@ -590,7 +594,15 @@ hipError_t launch_row_norm(const RowNormParams& p, hipStream_t st) {
 hipError_t launch_qkv_post(const QkvPostParams& p, hipStream_t st) {
   const int nh = p.Hq + 2 * p.Hkv;
   if (p.plan && (p.n_ranges < p.batch || p.slice < 1)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(qkv_post_kernel, dim3((nh + 3) / 4, p.batch * p.B + (p.plan ? 1 : 0)), dim3(256), 0, st, p);
+  const int rows = p.batch * p.B;
+  if (p.D == 128)
+    hipLaunchKernelGGL(qkv_post_kernel<128>, dim3((nh + 3) / 4, (rows + qkv_rows<128>() - 1) / qkv_rows<128>() + (p.plan ? 1 : 0)),
+                       dim3(256), 0, st, p);
+  else if (p.D == 64)
+    hipLaunchKernelGGL(qkv_post_kernel<64>, dim3((nh + 3) / 4, (rows + qkv_rows<64>() - 1) / qkv_rows<64>() + (p.plan ? 1 : 0)),
+                       dim3(256), 0, st, p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
