@@ -160,6 +160,24 @@ GemmPlan plan_gemm(int M, int N, int K, int nz, int mode) {
         per = per128;
       }
     }
+    // 128-row partial tiles whose 256-column grid leaves CUs idle take 192
+    // columns where that fills more of the round (512 rows of the Qwen3-8B-
+    // shaped drafter, QKV: 192 -> 256 workgroups at the same 2 splits)
+    if (mode == dfl::kGemmPartial && g.bm == 128) {
+      const long long grid256 = cdiv(M, 128) * cols * g.splits;
+      const long long base = cdiv(M, 128) * cdiv(N, 192) * nz;
+      if (grid256 < kBigSlots && base < kBigSlots) {
+        int s = (int)(kBigSlots / base);
+        s = std::min(s, std::max(1, chunks / 8));  // at least 256 k per split
+        const int per192 = (int)cdiv(chunks, s);
+        const int s192 = (int)cdiv(chunks, per192);
+        if (base * s192 > grid256) {
+          g.bn = 192;
+          g.splits = s192;
+          per = per192;
+        }
+      }
+    }
     g.k_per_split = per * 32;
     return g;
   }
