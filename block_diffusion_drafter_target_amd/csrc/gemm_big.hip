@@ -19,7 +19,7 @@
 //     direct loads keep 40 KB of weights in flight per workgroup; 128 x 192
 //     (three 16-row weight groups per wave) fills the round where 128 x 256
 //     partial tiles leave CUs idle (512 rows, QKV: 192 -> 256 workgroups,
-//     42.5 -> 38.7 us per launch, measured on MI355X). The
+//     the QKV phase 228 -> 209 us per step, measured on MI355X). The
 //     256 x 192 SwiGLU tile (four waves of 64 rows
 //     along A, two of 96 weight rows = 48 gate and 48 up rows) fills one
 //     round of 256 CUs where 256 x 256 tiles leave a quarter of them idle;
