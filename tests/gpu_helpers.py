@@ -178,6 +178,11 @@ SHAPES = {
     "ws-tail": synth.DraftConfig(name="ws-tail", hidden=320, n_layers=1, n_q_heads=4, n_kv_heads=2,
                                  head_dim=64, intermediate=8256, vocab=1040, n_tap=2, block=16,
                                  batch=5, ctx_len=0),
+    # rows wider than 4096 (hidden 5120): the embedding and row-norm kernels
+    # with four float4 columns per thread (three used, the fourth clamped)
+    "wide-h5120": synth.DraftConfig(name="wide-h5120", hidden=5120, n_layers=1, n_q_heads=8, n_kv_heads=2,
+                                    head_dim=64, intermediate=512, vocab=1040, n_tap=2, block=16,
+                                    batch=2, ctx_len=0),
     # long contexts: chunks of many 64-key attention slices, G = 8, D = 64
     "long-d64": synth.DraftConfig(name="long-d64", hidden=512, n_layers=1, n_q_heads=64, n_kv_heads=8,
                                   head_dim=64, intermediate=512, vocab=1024, n_tap=2, block=16,
@@ -198,7 +203,7 @@ SHAPES = {
 CTX = {"gqa-d128": [1, 300, 777, 0, 64], "g8-d64": [500, 33], "b12": [129, 0, 64],
        "tiled-b9": [17, 260, 0, 64, 1, 333, 90, 128, 2],
        "long-d64": [8900, 8500, 8193, 100], "long-d128": [16900, 16000, 9000, 3],
-       "mlp-wide": [40, 0, 17, 300, 64, 1, 129, 90, 33, 7], "mlp-wide-b2": [70, 250], "mlp-wide-b1": [130],
+       "mlp-wide": [40, 0, 17, 300, 64, 1, 129, 90, 33, 7], "mlp-wide-b2": [70, 250], "mlp-wide-b1": [130], "wide-h5120": [77, 0],
        "big-b19": [0, 1, 17, 64, 129, 260, 300, 33, 90, 5, 200, 150, 75, 12, 280, 45, 100, 3, 64],
        "big-b8x40": [(37 * i) % 211 for i in range(40)], "ws-tail": [0, 33, 100, 64, 7],
        "ragged-1long": [6000, 0, 1, 5, 17, 3, 64, 2, 0, 9, 33, 1, 7, 0, 12, 4, 65, 1, 2, 8, 0, 3, 1, 6]}

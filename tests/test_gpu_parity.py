@@ -104,7 +104,7 @@ def test_ingest_rows_and_offset_ingest(gpu_lib):
 # every shape with unit gains, and the shapes below again with random gains
 # (each gain vector its own draw, so a swapped, unused or misindexed gain
 # changes the compared values)
-GAIN_SHAPES = ["gqa-d128", "g8-d64", "tiled-b9", "big-b19", "big-b8x40", "mlp-wide-b2", "b12", "ws-tail", "mlp-wide-b1"]
+GAIN_SHAPES = ["gqa-d128", "g8-d64", "tiled-b9", "big-b19", "big-b8x40", "mlp-wide-b2", "b12", "ws-tail", "mlp-wide-b1", "wide-h5120"]
 CASES = [(s, "ones") for s in sorted(gh.SHAPES)] + [(s, "random") for s in GAIN_SHAPES]
 CASE_IDS = [f"{s}-{g}" for s, g in CASES]
 
