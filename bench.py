@@ -414,27 +414,46 @@ def main():
     torch.cuda.synchronize()
     assert int(dr.status.abs().max()) == 0, "a sequence ran out of cache"
     after_warmup = {k: getattr(dr, k).clone() for k in ("ctx_len", "anchor_out", "commit_rows", "n_commit")}
+    # The timed region: K steps between two events. The LM head is timed live
+    # inside it by the library's phase events on every LM_STRIDE-th step (an
+    # event pair costs the stream a few microseconds per step; the per-step
+    # spread comes from a replay of the same steps below).
+    LM_STRIDE = 8
     bd.dflash_profile_enable(["lm_head"])
-    # one event at every step boundary: the mean over the K steps and the
-    # spread of single steps (median, p10, p90)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    start, stop = evs[0], evs[-1]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
+        bd.dflash_profile_pause(i % LM_STRIDE != 0)
         step(targets[1 + args.warmup + i])
-        evs[i + 1].record()
+    stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
-    per_step = np.array([1e3 * evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
-    spread = {"p10": round(float(np.percentile(per_step, 10)), 1), "median": round(float(np.median(per_step)), 1),
-              "p90": round(float(np.percentile(per_step, 90)), 1)}
     lm_ms, lm_n = bd.dflash_profile_read("lm_head")
     bd.dflash_profile_enable([])
     ctx_after = dr.ctx_len.cpu().numpy()
     assert int(dr.status.abs().max()) == 0
     # the replay accepted exactly the recorded prefix lengths
     assert dr.accept_len.cpu().numpy().tolist() == m_all[args.warmup + args.steps].cpu().numpy().tolist()
+
+    # spread of single steps (p10, median, p90): the same K steps replayed from
+    # the same state with an event at every step boundary; the replay must
+    # reach the timed run's end state
+    end_state = {k: getattr(dr, k).clone() for k in ("ctx_len", "anchor_out", "commit_rows", "n_commit")}
+    for k, v in after_warmup.items():
+        getattr(dr, k).copy_(v)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(args.steps):
+        step(targets[1 + args.warmup + i])
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    for k, v in end_state.items():
+        assert torch.equal(getattr(dr, k), v), f"the spread replay diverged from the timed steps ({k})"
+    per_step = np.array([1e3 * evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    spread = {"p10": round(float(np.percentile(per_step, 10)), 1), "median": round(float(np.median(per_step)), 1),
+              "p90": round(float(np.percentile(per_step, 90)), 1)}
 
     cold = None
     if args.evict_mb:

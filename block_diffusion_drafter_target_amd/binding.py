@@ -29,7 +29,7 @@ EXPORTED = ("dflash_model_create", "dflash_model_destroy", "dflash_rope_table",
             "dflash_target_create", "dflash_target_forward", "dflash_kv_commit",
             "dflash_draft_block_sample", "dflash_verify_sample", "dflash_sample_logits",
             "dflash_draft_block_noalloc", "dflash_loop_tokens", "dflash_loop_advance",
-            "dflash_ingest_rows")
+            "dflash_ingest_rows", "dflash_profile_pause")
 
 # bytes of the static device workspace behind dflash_draft_block_noalloc
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -109,6 +109,8 @@ def load() -> C.CDLL:
     lib.dflash_profile_enable.restype = i32
     lib.dflash_profile_read.argtypes = [i32, C.POINTER(C.c_double), C.POINTER(C.c_int32)]
     lib.dflash_profile_read.restype = i32
+    lib.dflash_profile_pause.argtypes = [i32]
+    lib.dflash_profile_pause.restype = i32
     lib.dflash_status_string.argtypes = [i32]
     lib.dflash_status_string.restype = C.c_char_p
     for fn in ("dflash_model_create", "dflash_rope_table", "dflash_fuse_ctx", "dflash_inject_kv",
@@ -251,6 +253,11 @@ def dflash_profile_enable(phases=()) -> None:
     for p in phases:
         mask |= 1 << (PHASES[p] if isinstance(p, str) else int(p))
     _check("dflash_profile_enable", load().dflash_profile_enable(mask))
+
+
+def dflash_profile_pause(paused: bool) -> None:
+    """Stop (True) or resume (False) recording phase events; records and mask are kept."""
+    _check("dflash_profile_pause", load().dflash_profile_pause(1 if paused else 0))
 
 
 def dflash_profile_read(phase) -> tuple[float, int]:

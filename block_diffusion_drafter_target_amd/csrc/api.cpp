@@ -36,13 +36,14 @@ struct Rec {
 uint32_t mask = 0;
 std::vector<Rec> recs;  // events are created once and reused
 size_t used = 0;
+bool paused = false;                  // dflash_profile_pause: skip launches, keep the records
 thread_local bool suspended = false;  // set while a call that must not allocate runs
 
 struct Scope {
   Rec* r = nullptr;
   hipStream_t st;
   Scope(int phase, hipStream_t s) : st(s) {
-    if (suspended || !(mask >> phase & 1u)) return;
+    if (suspended || paused || !(mask >> phase & 1u)) return;
     if (used == recs.size()) {
       Rec n{phase, nullptr, nullptr};
       if (hipEventCreate(&n.a) != hipSuccess || hipEventCreate(&n.b) != hipSuccess) return;
@@ -1431,7 +1432,13 @@ dflash_status dflash_pack_matrix(const void* src, void* dst, int32_t rows, int32
 
 dflash_status dflash_profile_enable(uint32_t phase_mask) {
   prof::mask = phase_mask;
+  prof::paused = false;
   if (phase_mask) prof::used = 0;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_profile_pause(int32_t paused) {
+  prof::paused = paused != 0;
   return DFLASH_OK;
 }
 

@@ -412,6 +412,11 @@ typedef enum dflash_phase {
 
 dflash_status dflash_profile_enable(uint32_t phase_mask);
 dflash_status dflash_profile_read(int32_t phase, double* total_ms, int32_t* launches);
+/* dflash_profile_pause(1) stops recording events without clearing the records
+ * or the mask, dflash_profile_pause(0) resumes: a benchmark times a sample of
+ * the launches (every event pair recorded on the stream costs the stream a few
+ * microseconds). Process-wide, not thread-safe; always DFLASH_OK. */
+dflash_status dflash_profile_pause(int32_t paused);
 
 const char* dflash_status_string(dflash_status s);
 
