@@ -212,6 +212,16 @@ def test_rope_table_values():
     assert bd.load().dflash_rope_table(out.ctypes.data_as(C.c_void_p), 4, 63, 1e6) == bd.DFLASH_ERR_SHAPE
 
 
+def test_profile_controls_without_a_gpu():
+    # enabling, pausing, resuming and reading record nothing without a launch
+    bd.dflash_profile_enable(["lm_head"])
+    bd.dflash_profile_pause(True)
+    bd.dflash_profile_pause(False)
+    assert bd.dflash_profile_read("lm_head") == (0.0, 0)
+    bd.dflash_profile_enable([])
+    assert bd.load().dflash_profile_read(99, bd.C.byref(bd.C.c_double()), bd.C.byref(bd.C.c_int32())) == bd.DFLASH_ERR_SHAPE
+
+
 def test_status_strings():
     assert bd.status_string(0) == "ok"
     assert "workspace" in bd.status_string(bd.DFLASH_ERR_WORKSPACE)
