@@ -308,6 +308,54 @@ def phase_roofline(cfg, phases, ctx0, ctx1):
     return out
 
 
+def library_gemms(torch, cfg, rows_list):
+    """The step's weight GEMMs in torch's bf16 linear (hipBLASLt on ROCm), for
+    comparison with the library's kernels on the same shapes: Y = X W^T with W
+    [N, K] bf16, X [M, K] bf16, weights cycled over copies that together exceed
+    the 256 MB Infinity Cache (cold, as in the step), launches captured in one
+    graph and replayed. Returns one record per (rows, product)."""
+    import math
+    F = torch.nn.functional
+    H, qw = cfg.hidden, cfg.n_q_heads * cfg.head_dim
+    shapes = {"qkv": (qw + 2 * cfg.n_kv_heads * cfg.head_dim, H), "o": (H, qw),
+              "gate_up": (2 * cfg.intermediate, H), "down": (H, cfg.intermediate),
+              "lm_head": (cfg.vocab, H), "fuse": (H, cfg.n_tap * H)}
+    out = []
+    dev = torch.device("cuda")
+    side = torch.cuda.Stream()
+    for M in rows_list:
+        for name, (N, K) in shapes.items():
+            nc = max(2, math.ceil(1.2e9 / (N * K * 2)))
+            Ws = [torch.randn(N, K, device=dev, dtype=torch.bfloat16) * 0.02 for _ in range(nc)]
+            X = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+            Y = [None] * nc
+            with torch.cuda.stream(side):
+                for i in range(nc):
+                    Y[i] = F.linear(X, Ws[i])
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for i in range(nc):
+                    Y[i] = F.linear(X, Ws[i])
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, 40 // nc)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / (reps * nc)
+            flop = 2.0 * M * N * K
+            out.append({"rows": M, "gemm": name, "N": N, "K": K, "us": round(us, 1),
+                        "weight_TBps": round(N * K * 2 / us / 1e6, 2), "mfma_frac": round(flop / us / 1e6 / MFMA_PEAK_TFLOPS, 3)})
+            log(f"library GEMM {name} M={M}: {us:.1f} us")
+            del g, Ws, X, Y
+            torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,6 +380,9 @@ def main():
                     help="also time steps one by one with this many MiB written between them (outside "
                          "each step's events), so that no step finds the previous one's data in the "
                          "256 MB Infinity Cache")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="instead of the step: time torch's bf16 linear (hipBLASLt) on the step's weight "
+                         "GEMM shapes at the block rows of the workload and of 16, 128 and 512 rows")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py measures one GPU; runs on several GPUs are not implemented",
@@ -349,6 +400,11 @@ def main():
     if args.batch:
         cfg = cfg.with_(batch=args.batch)
     B, V, H, batch = cfg.block, cfg.vocab, cfg.hidden, cfg.batch
+    if args.library_gemms:
+        rows = sorted({batch * B, 16, 128, 512})
+        print(json.dumps({"library_gemms": "torch bf16 linear (hipBLASLt), cold weights, graph-replayed",
+                          "config": {"workload": cfg.name}, "results": library_gemms(torch, cfg, rows)}))
+        return
     lens = synth.make_ctx_lens(cfg)
     n_break = min(args.steps, 20)  # steps of the per-phase breakdown pass
     n_steps = 1 + args.warmup + args.steps + n_break + (args.warmup if args.temperature > 0 else 0)
