@@ -97,7 +97,10 @@ def build(verbose: bool = True) -> str:
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    # --no-undefined: a kernel whose host-side stub the compiler dropped
+    # (a host-pass failure inside a template it reports nowhere) is a link
+    # error here, not a load error on the GPU
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
