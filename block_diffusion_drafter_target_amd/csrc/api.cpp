@@ -316,6 +316,12 @@ struct GemmCall {
   long long ld_dbg = 0;
   uint16_t* out = nullptr;            // swiglu mode
   long long ld_out = 0;
+  // row scale from the split RMSNorm (a single-pass SwiGLU on the weight-
+  // streaming kernel only; see GemmParams::rs): sums of squares
+  // [M][kMaxRowChunks], rs_n chunks of a row of rs_len columns
+  const float* rs = nullptr;
+  int rs_n = 0, rs_len = 0;
+  float rs_eps = 0.f;
 };
 
 // Runs the weight-streaming GEMM over all M rows (kGemmRows per launch).
@@ -344,6 +350,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     return dfl::launch_swiglu_combine(sc, st);
   }
   if (g.tiled || g.big) {
+    if (c.rs) return hipErrorInvalidValue;  // only the weight-streaming SwiGLU applies a row scale
     GemmParams p;
     std::memset(&p, 0, sizeof(p));
     p.A = c.A;
@@ -376,6 +383,7 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     return g.ws ? dfl::launch_gemm_ws(p, g.ng, g.mt, c.mode, c.nz, st)
                 : dfl::launch_gemm_tile(p, g.ng, g.mt, c.mode, c.nz, st);
   }
+  if (c.rs && c.mode != dfl::kGemmSwiglu) return hipErrorInvalidValue;
   for (int m0 = 0; m0 < c.M; m0 += kGemmRows) {
     GemmParams p;
     std::memset(&p, 0, sizeof(p));
@@ -399,6 +407,10 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     p.splits = g.splits;
     p.n_mats = c.nz;
     p.k_per_split = g.k_per_split;
+    p.rs = c.rs ? c.rs + (long long)m0 * dfl::kMaxRowChunks : nullptr;
+    p.rs_n = c.rs_n;
+    p.rs_len = c.rs_len;
+    p.rs_eps = c.rs_eps;
     if (c.mode == dfl::kGemmArgmax) {
       p.keys = c.keys + m0;
       p.ld_keys = c.ld_keys;
@@ -416,6 +428,21 @@ hipError_t run_gemm(const GemmCall& c, hipStream_t st, int* splits) {
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Whether run_gemm takes the weight-streaming kernel for this product in one
+// pass (no split SwiGLU): the products that can consume the split RMSNorm.
+bool gemm_streams(int M, int N, int K, int nz, int mode) {
+  const GemmPlan g = plan_gemm(M, N, K, nz, mode);
+  return !g.tiled && !g.big && !g.swiglu_split;
+}
+
+// Column chunks of the split RMSNorm over n columns, or 0 where the row
+// passes keep the one-workgroup-per-row form (a consumer off the weight-
+// streaming kernel, or rows too long for the chunk sums).
+int split_norm_chunks(int n, bool consumer_streams) {
+  const int ch = (n + dfl::kRowChunkCols - 1) / dfl::kRowChunkCols;
+  return consumer_streams && n % 4 == 0 && ch <= dfl::kMaxRowChunks ? ch : 0;
 }
 
 struct AttnPlan {
@@ -466,7 +493,7 @@ AttnPlan plan_attn(const dflash_config& c, int batch, int max_ctx, int B) {
 // of which reach the LM head (bytes, 256-aligned pieces): a draft block
 // (B = block, lm_rows = B - 1) or a target pass (B = n, lm_rows = n).
 struct StackWs {
-  size_t x, u, q, ao, s, ulm, keys, pm, pl, po, plan, P, total;
+  size_t x, u, q, ao, s, ulm, keys, pm, pl, po, plan, P, ss, total;
 };
 
 StackWs stack_ws(const dflash_config& c, int batch, int max_ctx, int B, int lm_rows) {
@@ -499,6 +526,7 @@ StackWs stack_ws(const dflash_config& c, int batch, int max_ctx, int B, int lm_r
   pf = std::max(pf, gemm_partial_floats((int)Mb, H, c.intermediate, 1));
   pf = std::max(pf, gemm_partial_floats((int)Mb, c.intermediate, H, 1, dfl::kGemmSwiglu));
   w.P = take(pf * 4);
+  w.ss = take(Mb * dfl::kMaxRowChunks * 4);  // split RMSNorm sums of squares
   w.total = off;
   return w;
 }
@@ -857,7 +885,16 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
   float* po = reinterpret_cast<float*>(base + w.po);
   int32_t* plan = reinterpret_cast<int32_t*>(base + w.plan);
   float* P = reinterpret_cast<float*>(base + w.P);
+  float* ss = reinterpret_cast<float*>(base + w.ss);
   const long long layer_kv = (long long)batch * Hkv * kv->max_ctx * D;
+  // Few rows (the weight-streaming GEMMs): the RMSNorms inside the stack take
+  // the split form, u = x * gain with the row sums of squares in ss, and 1/rms
+  // is applied after the next product, by the QKV post-pass or by the SwiGLU
+  // epilogue. The final norm keeps the one-pass form, so that the LM head's
+  // logits and argmax are the same numbers with or without logits requested.
+  // u_chunks: chunks of the norm that wrote u, 0 when u is normalised already
+  // (the embedding pass normalises its rows itself).
+  int u_chunks = 0;
   const long long hid = (long long)Mb * H;
   hipError_t e;
 
@@ -927,6 +964,12 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
     qp.plan = l == 0 ? plan : nullptr;
     qp.n_ranges = ap.n_ranges;
     qp.slice = ap.slice;
+    if (u_chunks) {
+      qp.rs = ss;
+      qp.rs_n = u_chunks;
+      qp.rs_len = H;
+      qp.rs_eps = c.rms_eps;
+    }
     if ((e = dfl::launch_qkv_post(qp, st)) != hipSuccess) return DFLASH_ERR_HIP;
     // attention over [context ; block]
     dfl::AttnParams at;
@@ -1004,6 +1047,11 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
     rn.rows = Mb;
     rn.n = H;
     rn.out = u;
+    const int gu_chunks = split_norm_chunks(H, gemm_streams(Mb, I, H, 1, dfl::kGemmSwiglu));
+    if (gu_chunks) {
+      rn.ssp = ss;
+      rn.ss_chunks = gu_chunks;
+    }
     if ((e = dfl::launch_row_norm(rn, st)) != hipSuccess) return DFLASH_ERR_HIP;
     // gate and up in one pass with SwiGLU in the epilogue
     GemmCall gg;
@@ -1019,6 +1067,12 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
     gg.out = sb;
     gg.ld_out = I;
     gg.P = P;
+    if (gu_chunks) {
+      gg.rs = ss;
+      gg.rs_n = gu_chunks;
+      gg.rs_len = H;
+      gg.rs_eps = c.rms_eps;
+    }
     {
       prof::Scope ps(DFLASH_PHASE_GATE_UP, st);
       e = run_gemm(gg, st, nullptr);
@@ -1058,11 +1112,17 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
     if (l + 1 < NL) {
       rn.gain = static_cast<const uint16_t*>(m->layers[l + 1].g_in);
       rn.out = u;
+      u_chunks = split_norm_chunks(H, gemm_streams(Mb, qkvw, H, 1, dfl::kGemmPartial));
     } else {
       rn.gain = static_cast<const uint16_t*>(m->w.g_final);
       rn.out = ulm;
       rn.final_mode = io.lm_skip;
       rn.B = B;
+      u_chunks = 0;
+    }
+    if (u_chunks) {
+      rn.ssp = ss;
+      rn.ss_chunks = u_chunks;
     }
     if ((e = dfl::launch_row_norm(rn, st)) != hipSuccess) return DFLASH_ERR_HIP;
   }

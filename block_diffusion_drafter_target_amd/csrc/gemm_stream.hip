@@ -23,7 +23,13 @@
 //     thousands of atomics);
 //     logits are never written unless a debug buffer is given;
 //   * swiglu mode (one split) pairs gate rows (W0) and up rows (W1) of the same
-//     output columns inside the workgroup and writes bf16 silu(g) * u.
+//     output columns inside the workgroup and writes bf16 silu(g) * u;
+//   * in swiglu mode an optional row scale applies the RMSNorm of A after the
+//     product: A then holds x * gain, and each row's gate and up products are
+//     multiplied by its 1/rms, formed from the per-chunk sums of squares of
+//     the split row pass (loaded with the first weights, reduced after the k
+//     loop). Partial products leave the scale to their consumer and an argmax
+//     does not depend on it.
 // MFMA: W rows are the A operand, activations the B operand, so a lane's four
 // results are four consecutive n of one row m.
 #include "common.h"
@@ -88,6 +94,25 @@ void gemm_stream_kernel(const GemmParams p) {
     arow[t] = p.A + (long long)row * p.lda + g * 8;
   }
 
+  // row-scale sums: lane group g holds chunks 4g .. 4g + 3 and 16 + 4g ..
+  // 16 + 4g + 3 of its row (from A when there is no scale: valid memory,
+  // values dropped, so no branch separates these loads from the weight
+  // stream)
+  static_assert(kMaxRowChunks == 32, "two float4 of chunk sums per lane");
+  constexpr bool kRowScale = MODE == kGemmSwiglu;
+  const bool has_rs = kRowScale && p.rs != nullptr;
+  f32x4_t rsv[MT][2];
+  if constexpr (kRowScale) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int m = min(16 * t + r, p.M - 1);
+      const float* rsrow =
+          has_rs ? p.rs + (long long)m * kMaxRowChunks + 4 * g : reinterpret_cast<const float*>(p.A);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) rsv[t][i] = *reinterpret_cast<const f32x4_t*>(rsrow + (has_rs ? 16 * i : 0));
+    }
+  }
+
   f32x4_t acc[NF][MT];
 #pragma unroll
   for (int f = 0; f < NF; ++f)
@@ -127,6 +152,22 @@ void gemm_stream_kernel(const GemmParams p) {
   for (int f = 0; f < NF; ++f)
 #pragma unroll
     for (int t = 0; t < MT; ++t) red[wave][f * MT + t][lane] = acc[f][t];
+  // row scales of the lane's rows 16t + r (1 without one)
+  float rsc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    rsc[t] = 1.f;
+    if constexpr (!kRowScale) continue;
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (16 * i + 4 * g + e < p.rs_n) a += rsv[t][i][e];
+    a += __shfl_xor(a, 16);
+    a += __shfl_xor(a, 32);
+    rsc[t] = has_rs ? 1.0f / sqrtf(a / (float)p.rs_len + p.rs_eps) : 1.f;
+  }
   __syncthreads();
 
   // each wave finishes the output fragments idx = wave, wave + 4, ...
@@ -137,6 +178,11 @@ void gemm_stream_kernel(const GemmParams p) {
     for (int w = 1; w < 4; ++w) v += red[w][idx][lane];
     const int m = 16 * t + r;
     const int nb = n0 + 16 * f + 4 * g;  // four consecutive n
+    float sc = rsc[0];
+#pragma unroll
+    for (int tt = 1; tt < MT; ++tt)
+      if (t == tt) sc = rsc[tt];
+    if (MODE == kGemmSwiglu) v *= sc;
     if (MODE == kGemmPartial) {
       if (m < p.M && nb < p.N) {
         float* dst = p.P + (long long)z * p.p_z_stride + (long long)s * p.p_s_stride +
@@ -148,6 +194,7 @@ void gemm_stream_kernel(const GemmParams p) {
       f32x4_t up = red[0][iu][lane];
 #pragma unroll
       for (int w = 1; w < 4; ++w) up += red[w][iu][lane];
+      up *= sc;
       if (m < p.M && nb < p.N) {
         float sv[4];
 #pragma unroll

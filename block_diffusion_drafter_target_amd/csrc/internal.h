@@ -54,7 +54,19 @@ struct GemmParams {
   // swiglu output (splits == 1): out[m][n] = bf16(silu(gate) * up)
   uint16_t* out;
   long long ld_out;
+  // optional row scale (the RMSNorm of A applied after the product; the
+  // weight-streaming kernel in SwiGLU mode only): gate and up products of row
+  // m are multiplied by 1 / sqrt(sum_{c < rs_n} rs[m * kMaxRowChunks + c] /
+  // rs_len + rs_eps) before the SwiGLU; rs_n <= kMaxRowChunks
+  const float* rs;
+  int rs_n, rs_len;
+  float rs_eps;
 };
+
+// Column chunks of the split RMSNorm (row_norm with ssp set): kRowChunkCols
+// columns each, rows of up to kMaxRowChunks chunks.
+constexpr int kRowChunkCols = 256;
+constexpr int kMaxRowChunks = 32;
 
 enum GemmMode { kGemmPartial = 0, kGemmArgmax = 1, kGemmSwiglu = 2 };
 
@@ -149,6 +161,14 @@ struct RowNormParams {
   uint16_t* tap;       // optional bf16 copy of x after the add, row stride tap_ld
   long long tap_ld;
   int final_mode, B;   // final_mode 1: out holds rows j >= 1 of every B-row sequence only
+  // Split form (few rows whose consumer is the weight-streaming GEMM): when
+  // set, out[row] = bf16(x * gain) without the 1/rms factor, and
+  // ssp[row * ss_chunks + c] = the sum of squares of x over column chunk c
+  // (kRowChunkCols columns; ss_chunks = ceil(n / kRowChunkCols)); the GEMM
+  // applies the factor through its row scale. Row stride kMaxRowChunks
+  // floats; row = the output row.
+  float* ssp;
+  int ss_chunks;
 };
 
 hipError_t launch_row_norm(const RowNormParams& p, hipStream_t st);
@@ -187,6 +207,12 @@ struct QkvPostParams {
   uint16_t* vc;
   int32_t* plan;      // if not NULL, one more workgroup writes the attention chunk split
   int n_ranges, slice;  // of the batch (attn_split.h) with n_ranges chunks per kv head
+  // optional row scale of the split RMSNorm that wrote the GEMM's input: the
+  // split sums of row m are multiplied by 1 / sqrt(sum_{c < rs_n}
+  // rs[m * kMaxRowChunks + c] / rs_len + rs_eps) (as in GemmParams)
+  const float* rs;
+  int rs_n, rs_len;
+  float rs_eps;
 };
 
 hipError_t launch_qkv_post(const QkvPostParams& p, hipStream_t st);

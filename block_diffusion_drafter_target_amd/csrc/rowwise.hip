@@ -210,6 +210,61 @@ __global__ __launch_bounds__(kRowThreads) void row_norm_kernel(const RowNormPara
   }
 }
 
+// Split RMSNorm for few rows whose consumer is the weight-streaming GEMM: one
+// wave per (kRowChunkCols-column chunk, row) sums the chunk's split partials
+// into the residual (or takes them alone), writes x back (and the debug and
+// tap copies), out = bf16(x * gain) and the chunk's sum of squares to ssp; the
+// GEMM multiplies its products by the row's 1/rms. One workgroup per row put a
+// 16-row pass on 16 CUs, each reading a whole row's partials (up to 144 KB);
+// this grid spreads them over rows * n / 256 waves (measured on MI355X with
+// the row scale left out: Qwen3-8B-shaped drafter step at batch 1, eleven
+// row passes, 794 -> 777 us).
+__global__ __launch_bounds__(64) void row_split_kernel(const RowNormParams p) {
+  const int m = blockIdx.y, c = blockIdx.x;
+  const int n4 = p.n / 4;
+  const int i4 = c * (kRowChunkCols / 4) + threadIdx.x;
+  const int ci = min(i4, n4 - 1);
+  const long long row_off = (long long)m * p.n;
+  // independent loads at clamped columns first (see add_splits); without a
+  // residual the row load reads the first split (valid memory, dropped)
+  const u32x2 gw = *reinterpret_cast<const u32x2*>(p.gain + 4 * ci);
+  const float* xs = p.x ? p.x : p.P;
+  const float keep_x = p.x ? 1.f : 0.f;
+  f32x4_t v = *reinterpret_cast<const f32x4_t*>(xs + row_off + 4 * ci) * keep_x;
+  for (int s0 = 0; s0 < p.splits; s0 += kSplitBatch) {
+    f32x4_t a[kSplitBatch];
+#pragma unroll
+    for (int k = 0; k < kSplitBatch; ++k)
+      a[k] = *reinterpret_cast<const f32x4_t*>(p.P + (long long)min(s0 + k, p.splits - 1) * p.p_s_stride + row_off +
+                                               4 * ci);
+#pragma unroll
+    for (int k = 0; k < kSplitBatch; ++k)
+      if (s0 + k < p.splits) v += a[k];
+  }
+  if (i4 >= n4) {
+    v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  } else {
+    if (p.x) *reinterpret_cast<f32x4_t*>(p.x + row_off + 4 * i4) = v;
+    if (p.dbg) *reinterpret_cast<f32x4_t*>(p.dbg + row_off + 4 * i4) = v;
+    if (p.tap)
+      *reinterpret_cast<u32x2*>(p.tap + (long long)m * p.tap_ld + 4 * i4) =
+          u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+  }
+  const float ss = wave_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
+  int orow = m;
+  if (p.final_mode) {
+    const int b = m / p.B, j = m % p.B;
+    if (j == 0) return;
+    orow = b * (p.B - 1) + j - 1;
+  }
+  if (i4 < n4) {
+    const f32x4_t g = bf4_to_f32(gw);
+    *reinterpret_cast<u32x2*>(p.out + (long long)orow * p.n + 4 * i4) =
+        u32x2{pack_bf2(v[0] * g[0], v[1] * g[1]), pack_bf2(v[2] * g[2], v[3] * g[3])};
+  }
+  if (threadIdx.x == 0) p.ssp[(long long)orow * kMaxRowChunks + c] = ss;
+}
+
 // ---------------------------------------------------------------------------
 // KV injection epilogue: for commit row i and layer l, k = RoPE(RMSNorm_head(
 // W_k c)), v = W_v c, scattered to (seq, pos); ctx_len[seq] grows to pos + 1.
@@ -405,6 +460,19 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
     x1[r] = *reinterpret_cast<const f32x4_t*>(psrc[r]);
     x2[r] = *reinterpret_cast<const f32x4_t*>(psrc[r] + half);
   }
+  // row scale of the split RMSNorm: the row's LPR lanes hold its chunk sums
+  // (kMaxRowChunks / LPR each; from P when there is none: valid memory,
+  // values dropped)
+  constexpr int kRsLane = kMaxRowChunks / LPR;
+  static_assert(kRsLane == 2 || kRsLane == 4, "chunk sums per lane");
+  typedef float rsv_t __attribute__((ext_vector_type(kRsLane)));
+  const bool has_rs = p.rs != nullptr;
+  rsv_t rsv[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int m = min(m0 + r * RPR + rs, rows - 1);
+    rsv[r] = *reinterpret_cast<const rsv_t*>(has_rs ? p.rs + (long long)m * kMaxRowChunks + kRsLane * qd : p.P);
+  }
   int st[NR], pos[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -426,6 +494,18 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(const QkvPostParams p) {
     }
   }
   if (p.splits > 1) inject_add_splits<NR, 2>(x1, x2, psrc, p.p_s_stride, p.splits, half);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < kRsLane; ++e)
+      if (kRsLane * qd + e < p.rs_n) a += rsv[r][e];
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) a += __shfl_xor(a, o);
+    const float sc = has_rs ? 1.0f / sqrtf(a / (float)p.rs_len + p.rs_eps) : 1.f;
+    x1[r] *= sc;
+    x2[r] *= sc;
+  }
   const uint16_t* gain = head < p.Hq ? p.gq : p.gk;
   const f32x4_t g1 = bf4_to_f32(*reinterpret_cast<const u32x2*>(gain + d0));
   const f32x4_t g2 = bf4_to_f32(*reinterpret_cast<const u32x2*>(gain + d0 + half));
@@ -580,6 +660,13 @@ hipError_t launch_embed(const EmbedParams& p, hipStream_t st) {
 }
 
 hipError_t launch_row_norm(const RowNormParams& p, hipStream_t st) {
+  if (p.ssp) {
+    if (p.n % 4 != 0 || p.ss_chunks != (p.n + kRowChunkCols - 1) / kRowChunkCols || p.ss_chunks > kMaxRowChunks ||
+        !p.P || p.splits < 1 || p.rows < 1)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(row_split_kernel, dim3(p.ss_chunks, p.rows), dim3(64), 0, st, p);
+    return hipGetLastError();
+  }
   if (p.n > kRowThreads * 4 * kMaxC4 || p.n % 4 || !p.P || p.splits < 1) return hipErrorInvalidValue;
   const int c4 = (p.n / 4 + kRowThreads - 1) / kRowThreads;  // float4 columns per thread
   if (c4 <= 1)
