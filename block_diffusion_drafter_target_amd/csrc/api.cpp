@@ -458,7 +458,11 @@ struct AttnPlan {
 // and batch-1 splits being the same at both)
 constexpr int kAttnTargetWGsD64 = 512;
 constexpr int kAttnTargetWGsD128 = 384;
-constexpr int kAttnMaxChunks = 32;   // per (sequence, kv head): 64 measured slower at batch 1
+// chunks per (sequence, kv head) at most: at batch 1 (context ~1050, so two
+// 64-key slices per chunk) 16 measured 2-3 us per step faster than 32 (one
+// slice per chunk: 17 chunks of partials to write and merge) and than 8 or 4
+// (longer chunks in fewer workgroups), 64 slower still (measured on MI355X)
+constexpr int kAttnMaxChunks = 16;
 
 // Attention chunks: about the target number of workgroups over the batch,
 // n_chunks per sequence and kv head at full length, without chunks shorter
@@ -892,8 +896,8 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
   // is applied after the next product, by the QKV post-pass or by the SwiGLU
   // epilogue. The final norm keeps the one-pass form, so that the LM head's
   // logits and argmax are the same numbers with or without logits requested.
-  // u_chunks: chunks of the norm that wrote u, 0 when u is normalised already
-  // (the embedding pass normalises its rows itself).
+  // u_chunks: chunks of the norm that wrote u (the embedding pass included),
+  // 0 when u is normalised already.
   int u_chunks = 0;
   const long long hid = (long long)Mb * H;
   hipError_t e;
@@ -917,6 +921,11 @@ dflash_status run_stack(const dflash_model* m, dflash_kv* kv, const StackIO& io,
   ep.x = x;
   ep.u = u;
   ep.dbg = dbg_hidden;
+  u_chunks = split_norm_chunks(H, gemm_streams(Mb, qkvw, H, 1, dfl::kGemmPartial));
+  if (u_chunks) {
+    ep.ssp = ss;
+    ep.ss_chunks = u_chunks;
+  }
   if ((e = dfl::launch_embed(ep, st)) != hipSuccess) return DFLASH_ERR_HIP;
 
   for (int l = 0; l < NL; ++l) {

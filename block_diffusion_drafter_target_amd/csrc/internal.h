@@ -185,6 +185,10 @@ struct EmbedParams {
   float* x;        // [batch*B, H]
   uint16_t* u;     // [batch*B, H]
   float* dbg;      // optional [batch*B, H]
+  // split form (as RowNormParams::ssp): u = bf16(x * gain), the chunk sums of
+  // squares in ssp [batch*B][kMaxRowChunks]
+  float* ssp;
+  int ss_chunks;
 };
 
 hipError_t launch_embed(const EmbedParams& p, hipStream_t st);

@@ -145,6 +145,36 @@ __global__ __launch_bounds__(kRowThreads) void embed_kernel(const EmbedParams p)
   }
 }
 
+// The embedding pass in the split form of the RMSNorm (see row_split_kernel):
+// one wave per (kRowChunkCols-column chunk, row); chunk 0 of a sequence's first
+// row writes its status.
+__global__ __launch_bounds__(64) void embed_split_kernel(const EmbedParams p) {
+  const int m = blockIdx.y, c = blockIdx.x;
+  const int b = m / p.B, j = m % p.B;
+  const int L = p.ctx_len[b];
+  const bool cap_bad = L < 0 || L + p.B > p.max_ctx || L + p.B > p.rope_max;
+  int tok = p.tokens ? p.tokens[(long long)b * p.B + j] : (j == 0 ? p.anchor[b] : p.mask_id);
+  const bool tok_bad = tok < 0 || tok >= p.V;
+  if (j == 0 && c == 0 && threadIdx.x == 0) p.status[b] = cap_bad ? kErrCapacity : (tok_bad ? kErrShape : 0);
+  if (tok_bad) tok = 0;
+  const int n4 = p.H / 4;
+  const int i4 = c * (kRowChunkCols / 4) + threadIdx.x;
+  const int ci = min(i4, n4 - 1);
+  const u32x2 gw = *reinterpret_cast<const u32x2*>(p.gain + 4 * ci);
+  const u32x2 ew = *reinterpret_cast<const u32x2*>(p.embed + (long long)tok * p.H + 4 * ci);
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (i4 < n4) {
+    v = bf4_to_f32(ew);
+    *reinterpret_cast<f32x4_t*>(p.x + (long long)m * p.H + 4 * i4) = v;
+    if (p.dbg) *reinterpret_cast<f32x4_t*>(p.dbg + (long long)m * p.H + 4 * i4) = v;
+    const f32x4_t g = bf4_to_f32(gw);
+    *reinterpret_cast<u32x2*>(p.u + (long long)m * p.H + 4 * i4) =
+        u32x2{pack_bf2(v[0] * g[0], v[1] * g[1]), pack_bf2(v[2] * g[2], v[3] * g[3])};
+  }
+  const float ss = wave_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
+  if (threadIdx.x == 0) p.ssp[(long long)m * kMaxRowChunks + c] = ss;
+}
+
 // ---------------------------------------------------------------------------
 // y = (x +=) sum of split partials (at least one split); out =
 // bf16(RMSNorm(y) * gain)
@@ -648,6 +678,13 @@ hipError_t launch_swiglu_combine(const SwigluCombineParams& p, hipStream_t st) {
 }
 
 hipError_t launch_embed(const EmbedParams& p, hipStream_t st) {
+  if (p.ssp) {
+    if (p.H % 4 != 0 || p.ss_chunks != (p.H + kRowChunkCols - 1) / kRowChunkCols || p.ss_chunks > kMaxRowChunks ||
+        p.batch * p.B < 1)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(embed_split_kernel, dim3(p.ss_chunks, p.batch * p.B), dim3(64), 0, st, p);
+    return hipGetLastError();
+  }
   if (p.H > kRowThreads * 4 * kMaxC4 || p.H % 4) return hipErrorInvalidValue;
   const int c4 = (p.H / 4 + kRowThreads - 1) / kRowThreads;  // float4 columns per thread
   if (c4 <= 1)
