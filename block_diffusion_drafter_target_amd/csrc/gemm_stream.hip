@@ -42,14 +42,18 @@ namespace {
 constexpr int kKB = 128;  // k per block = four 32-wide MFMA steps
 
 // Waves per SIMD the register budget is tuned for (fewer activation tiles,
-// more waves in flight).
-template <int MT>
+// more waves in flight). With one activation tile the argmax product (the LM
+// head) runs five: Qwen3-8B-shaped LM head at batch 1 202 -> 196 us per launch
+// against four, 199-200 at six or eight; five made the four-group SwiGLU
+// slower (197 -> 252 us per step) and left the partial products unchanged,
+// three slowed every mode (measured on MI355X).
+template <int MT, int MODE>
 struct Occ {
-  static constexpr int kWaves = MT == 1 ? 4 : (MT == 2 ? 3 : 2);
+  static constexpr int kWaves = MT == 1 ? (MODE == kGemmArgmax ? 5 : 4) : (MT == 2 ? 3 : 2);
 };
 
 template <int MT, int NF, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Occ<MT>::kWaves, Occ<MT>::kWaves)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Occ<MT, MODE>::kWaves, Occ<MT, MODE>::kWaves)))
 void gemm_stream_kernel(const GemmParams p) {
   __shared__ f32x4_t red[4][NF * MT][kWave];
   __shared__ unsigned long long kbest[MODE == kGemmArgmax ? NF : 1][16 * MT];
