@@ -699,7 +699,7 @@ SampleWs sample_ws(const dflash_config& c, int batch) {
   w.a = take((size_t)batch * B * 4);
   w.m = take((size_t)batch * 4);
   w.rej = take((size_t)batch * 4);
-  w.keys = take((size_t)dfl::sample_chunks(c.vocab) * items * 8);
+  w.keys = take((size_t)dfl::gumbel_chunks(c.vocab) * items * 8);
   w.total = off;
   return w;
 }
@@ -1231,7 +1231,7 @@ dflash_status dflash_draft_block_sample(const dflash_model* m, dflash_kv* kv, co
   g.B = c.block;
   g.V = c.vocab;
   g.items = kv->batch * (c.block - 1);
-  g.chunks = dfl::sample_chunks(c.vocab);
+  g.chunks = dfl::gumbel_chunks(c.vocab);
   g.inv_t = 1.0f / temperature;
   g.seed_lo = (uint32_t)seed;
   g.seed_hi = (uint32_t)(seed >> 32);
@@ -1365,7 +1365,7 @@ dflash_status dflash_sample_logits(const dflash_model* m, const float* logits, i
   if (!logits || !tokens || !ws) return DFLASH_ERR_NULL;
   if (!sample_temperature_ok(temperature)) return DFLASH_ERR_SHAPE;
   const dflash_config& c = m->cfg;
-  const size_t need = align256((size_t)dfl::sample_chunks(c.vocab) * rows * 8);
+  const size_t need = align256((size_t)dfl::gumbel_chunks(c.vocab) * rows * 8);
   if (ws_bytes < need) return DFLASH_ERR_WORKSPACE;
   dfl::GumbelParams g{};
   std::memset(&g, 0, sizeof(g));
@@ -1374,7 +1374,7 @@ dflash_status dflash_sample_logits(const dflash_model* m, const float* logits, i
   g.B = 2;
   g.V = c.vocab;
   g.items = rows;
-  g.chunks = dfl::sample_chunks(c.vocab);
+  g.chunks = dfl::gumbel_chunks(c.vocab);
   g.inv_t = 1.0f / temperature;
   g.seed_lo = (uint32_t)seed;
   g.seed_hi = (uint32_t)(seed >> 32);
@@ -1459,7 +1459,7 @@ dflash_status dflash_verify_sample(const dflash_model* m, const dflash_kv* kv, c
   g.B = B;
   g.V = c.vocab;
   g.items = batch;
-  g.chunks = dfl::sample_chunks(c.vocab);
+  g.chunks = dfl::gumbel_chunks(c.vocab);
   g.inv_t = lp.inv_t;
   g.seed_lo = ap.seed_lo;
   g.seed_hi = ap.seed_hi;

@@ -349,12 +349,13 @@ struct GumbelParams {
   float inv_t;
   uint32_t seed_lo, seed_hi, step;
   const int32_t* step_dev;  // or NULL: the draws' step is step + *step_dev
-  unsigned long long* keys;  // [chunks, items]
+  unsigned long long* keys;  // [chunks, items], chunks = gumbel_chunks(V)
   int32_t* out;
   const int32_t* status;
   int32_t* a;
 };
-int sample_chunks(int V);
+int sample_chunks(int V);  // log-sum-exp chunks per row
+int gumbel_chunks(int V);  // Gumbel-argmax chunks per item (keys)
 hipError_t launch_gumbel(const GumbelParams& p, int mode, hipStream_t st);
 
 }  // namespace dfl

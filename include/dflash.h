@@ -245,7 +245,7 @@ dflash_status dflash_draft_block_sample(const dflash_model* m, dflash_kv* kv, co
  * which comes from the target's last prompt row. [P4 "Ejecutando DFlash":
  * the call's temperature]
  *   logits  device fp32 [rows, V]; tokens device int32 [rows] out
- *   ws      at least 8 * ceil(V / 8192) * rows bytes (dflash_workspace_bytes
+ *   ws      at least 8 * ceil(V / 2048) * rows bytes (dflash_workspace_bytes
  *           covers rows <= batch * (block - 1)) */
 dflash_status dflash_sample_logits(const dflash_model* m, const float* logits, int32_t rows, float temperature,
                                    uint64_t seed, int32_t step, int32_t row0, int32_t* tokens, void* ws,
