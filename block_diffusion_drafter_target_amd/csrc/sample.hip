@@ -118,14 +118,33 @@ __global__ __launch_bounds__(256) void lse_partial_kernel(const LseParams p) {
   }
 }
 
-// log-sum-exp of one row from its per-chunk pairs
+// log-sum-exp of one row from its per-chunk pairs: up to kLseBatch pairs are
+// loaded together (clamped indexes, no branch between the loads) and folded
+// into a running (max, sum), so a row of up to kLseBatch chunks costs one
+// round trip instead of one per unrolled step of two serial loops
+constexpr int kLseBatch = 32;
 __device__ __forceinline__ float lse_of(const float* pmax, const float* psum, int row, int chunks) {
   const float* pm = pmax + (long long)row * chunks;
   const float* ps = psum + (long long)row * chunks;
-  float m = pm[0];
-  for (int c = 1; c < chunks; ++c) m = fmaxf(m, pm[c]);
-  float t = 0.f;
-  for (int c = 0; c < chunks; ++c) t += ps[c] * __expf(pm[c] - m);
+  float m = -__builtin_inff(), t = 0.f;
+  for (int c0 = 0; c0 < chunks; c0 += kLseBatch) {
+    float a[kLseBatch], b[kLseBatch];
+#pragma unroll
+    for (int j = 0; j < kLseBatch; ++j) {
+      const int c = min(c0 + j, chunks - 1);
+      a[j] = pm[c];
+      b[j] = ps[c];
+    }
+    float bm = m;
+#pragma unroll
+    for (int j = 0; j < kLseBatch; ++j)
+      if (c0 + j < chunks) bm = fmaxf(bm, a[j]);
+    t = m == -__builtin_inff() ? 0.f : t * __expf(m - bm);
+#pragma unroll
+    for (int j = 0; j < kLseBatch; ++j)
+      if (c0 + j < chunks) t += b[j] * __expf(a[j] - bm);
+    m = bm;
+  }
   return m + logf(t);
 }
 
